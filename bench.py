@@ -1,0 +1,237 @@
+"""Benchmark of the joint video-audio attention hot path on one MI355X.
+
+One step = the whole hot path of one dual-stream block on the 480p-latent
+layer (21 x 30 x 52 video tokens + one conditioning frame at t = -1, 218
+audio tokens, 512 text tokens, 24 heads x 128): video->text cross-attention
+(unrotated video queries), time-shifted 3D RoPE of Q and K, joint
+self-attention over all 35050 tokens, and both directions of the
+audio<->video cross-attention.  Inputs are seeded synthetic bf16 tensors
+already resident in HBM.
+
+The JSON line reports the step's attention throughput (4 * Nq * Nk * d per
+head summed over the step's attention calls, over the step time), the
+joint-attention call against the bf16 matrix-core peak, the block-sparse vs
+dense comparison on the 172032-token video grid, and the fp64 oracle timed on
+the host over a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def attn_flops(nq, nk, heads, d):
+    return 4.0 * nq * nk * heads * d
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse leg")
+    ap.add_argument("--sparse-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows of the oracle sample (all heads, all keys)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import joint_video_audio_rope_amd as J
+    from synth import WORKLOADS, joint_inputs, n_tokens, sparse_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS["480p"]
+    n = n_tokens(w)
+    h, d = w["heads"], w["head_dim"]
+    frame = w["H"] * w["W"]
+    n_vs = (w["n_cond_frames"] + w["T"]) * frame           # video stream incl. cond frame
+    n_a, n_t = w["n_audio"], w["n_text"]
+    a0, t0 = n_vs, n_vs + n_a
+
+    x = joint_inputs(w, dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    qv, kv, vv = q[:n_vs], k[:n_vs], v[:n_vs]              # contiguous views (leading rows)
+    qa, ka, va = (t[a0:a0 + n_a] for t in (q, k, v))
+    kt, vt = k[t0:t0 + n_t], v[t0:t0 + n_t]
+    spec = J.rope_spec_for(w)
+    spec.device_table(dev)
+
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_joint = torch.empty((n, h, d), **f32)
+    o_vt = torch.empty((n_vs, h, d), **f32)
+    o_va = torch.empty((n_vs, h, d), **f32)
+    o_av = torch.empty((n_a, h, d), **f32)
+    ws_joint = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, h, d, J.MMDIT_BF16),
+                           dtype=torch.uint8, device=dev)
+    ws_vt = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n_vs, n_t, h, d, J.MMDIT_BF16),
+                        dtype=torch.uint8, device=dev)
+    ws_av = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_AV_CROSS_ATTN, n_vs, n_a, h, d, J.MMDIT_BF16),
+                        dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev_joint = []
+
+    def step(record=False):
+        J.mmdit_joint_attn(qv, kt, vt, o=o_vt, ws=ws_vt, stream=stream)
+        J.mmdit_rope3d(spec, q, k, stream=stream)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        J.mmdit_joint_attn(q, k, v, o=o_joint, ws=ws_joint, stream=stream)
+        if record:
+            e1.record(stream)
+            ev_joint.append((e0, e1))
+        J.mmdit_av_cross_attn(qv, kv, vv, qa, ka, va, o_video=o_va, o_audio=o_av, ws=ws_av,
+                              stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step(record=True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    joint_ms = sum(a.elapsed_time(b) for a, b in ev_joint) / len(ev_joint)
+
+    fl_joint = attn_flops(n, n, h, d)
+    fl_step = fl_joint + attn_flops(n_vs, n_t, h, d) + 2 * attn_flops(n_vs, n_a, h, d)
+    value = fl_step / (ms_step * 1e-3) / 1e12
+    joint_tflops = fl_joint / (joint_ms * 1e-3) / 1e12
+    print("[bench] step %.3f ms, joint call %.3f ms (%.1f TFLOP/s)" % (ms_step, joint_ms, joint_tflops),
+          file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "MMDiT joint-attn fwd TFLOP/s (480p-latent, 21f+218 audio) + % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, bf16, resident in HBM)",
+        "config": {"workload": "480p-latent layer: video 21x30x52 + 1 cond frame (t=-1), 218 audio, "
+                               "512 text; 35050 tokens, 24 heads x 128; step = video->text + RoPE + "
+                               "joint self-attn + audio<->video cross-attn",
+                   "tokens": n, "heads": h, "head_dim": d, "step_flop": fl_step},
+        "joint_attn": {"ms": round(joint_ms, 4), "tflops": round(joint_tflops, 2),
+                       "pct_bf16_peak": round(100.0 * joint_tflops / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(joint_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(joint_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "joint attention call (V^T staging + attn_bf16_kernel<128>), "
+                               "4*N^2*d*h = %.4g FLOP per call" % fl_joint},
+    }
+
+    del o_vt, o_va, o_av, ws_vt, ws_av
+    if not args.no_sparse:
+        out["block_sparse"] = sparse_leg(args, torch, J, WORKLOADS["sparse2k"], sparse_inputs, dev)
+        print("[bench] block sparse: %s" % out["block_sparse"], file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, torch, q, k, v)
+        print("[bench] cpu baseline: %s" % out["cpu_baseline"], file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+def sparse_leg(args, torch, J, w, sparse_inputs, dev):
+    """Dense vs block-sparse self-attention on the 24 x 64 x 112 video grid."""
+    T, H, W = w["T"], w["H"], w["W"]
+    h, d = w["heads"], w["head_dim"]
+    n = T * H * W
+    x = sparse_inputs(w, dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    sd = J.sparse_desc(w["zone"], w["block"], w["top_k"], w["top_p"])
+    ws_s = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, J.MMDIT_BF16, sd),
+                       dtype=torch.uint8, device=dev)
+    nb = n // 64
+    mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=dev)
+    cnt = torch.empty((h, nb), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def dense():
+        J.mmdit_joint_attn(q, k, v, o=o, ws=ws_d, stream=stream)
+
+    def sparse():
+        J.mmdit_block_sparse_attn(q, k, v, T, H, W, w["zone"], w["block"], w["top_k"], w["top_p"],
+                                  o=o, sel_mask=mask, sel_count=cnt, ws=ws_s, stream=stream)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.sparse_reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.sparse_reps
+
+    t_dense = timed(dense)
+    t_sparse = timed(sparse)
+    counts = cnt.to(torch.float64)
+    density = float(counts.mean().item() / nb)
+    fl_dense = attn_flops(n, n, h, d)
+    fl_sparse = 4.0 * 64 * 64 * d * float(counts.sum().item())
+    return {"workload": "video 24x64x112 (172032 tokens), 24 heads x 128, zones 8x8x8, blocks 4x4x4, "
+                        "top-k 32 + top-p 0.9, smooth-field Q/K/V",
+            "dense_ms": round(t_dense, 3), "sparse_ms": round(t_sparse, 3),
+            "speedup": round(t_dense / t_sparse, 3), "density": round(density, 4),
+            "dense_tflops": round(fl_dense / t_dense * 1e-9, 1),
+            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_sparse * 1e-9, 1)}
+
+
+def cpu_baseline(args, torch, q, k, v):
+    """The fp64 oracle on host cores over a bounded sample of the joint attention."""
+    import numpy as np
+
+    from oracle import attention as A
+
+    rows = np.linspace(0, q.shape[0] - 1, args.cpu_rows).astype(np.int64)
+    qh = q[torch.from_numpy(rows).to(q.device)].to("cpu", torch.float64).numpy()
+    kh = k.to("cpu", torch.float64).numpy()
+    vh = v.to("cpu", torch.float64).numpy()
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    A.attention(qh, kh, vh, chunk=256)
+    dt = time.perf_counter() - t0
+    fl = attn_flops(len(rows), k.shape[0], q.shape[1], q.shape[2])
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "joint attention of %d evenly spaced query rows x all 24 heads against all %d "
+                      "keys (numpy fp64, BLAS threads for the products, exp single-threaded), "
+                      "%.1f s" % (len(rows), k.shape[0], dt)}
+
+
+if __name__ == "__main__":
+    main()

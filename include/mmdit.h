@@ -1,0 +1,199 @@
+/*
+ * mmdit.h - C ABI of the joint video-audio attention hot path for MI355X (gfx950).
+ *
+ * What the calls compute comes from the pages on SkyReels-V4 (a dual-stream
+ * MMDiT that generates video and audio together) and on Prism (dynamic
+ * block-sparse attention for joint video-audio DiTs at 2K):
+ *   - mmdit_rope3d            time-shifted 3D rotary embedding of Q and K;
+ *   - mmdit_joint_attn        softmax attention, joint over [video|audio|text] or
+ *                             any query set against any key set (video->text);
+ *   - mmdit_av_cross_attn     bidirectional audio<->video cross-attention;
+ *   - mmdit_block_sparse_attn mean-pooled block scores, hybrid top-k/top-p block
+ *                             selection, attention over the selected blocks.
+ *
+ * Conventions shared by every call
+ *   Layout     Q, K, V and O are contiguous [tokens][heads][head_dim] (head_dim
+ *              fastest).  Device pointers must be 16-byte aligned.  Inputs are
+ *              bf16 (MMDIT_BF16) or fp32 (MMDIT_FP32); attention outputs are
+ *              always fp32.
+ *   Ownership  The caller owns every buffer, the workspace included (its size
+ *              comes from mmdit_workspace_bytes).  The library allocates and
+ *              frees nothing and keeps no state besides a thread-local error
+ *              string.
+ *   Streams    `stream` is a hipStream_t passed as void* (NULL = the default
+ *              stream).  Device calls enqueue kernels and return at once;
+ *              results are ready when the stream is.
+ *   Errors     Every argument is checked on the host before anything is
+ *              enqueued: a non-OK status means nothing was enqueued.  A failed
+ *              launch returns MMDIT_ERR_HIP.  Faults inside a kernel surface at
+ *              the caller's next synchronisation.  Nothing throws across the
+ *              ABI.  mmdit_last_error() describes the last non-OK status of the
+ *              calling thread.
+ *   Outputs    Outputs are overwritten, never accumulated into, and must not
+ *              alias inputs.  mmdit_rope3d works in place on Q and K.
+ *   Threads    Calls are reentrant; concurrent calls must not share a workspace.
+ */
+#ifndef MMDIT_H
+#define MMDIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMDIT_ABI_VERSION 1
+#define MMDIT_MAX_SEGMENTS 16
+
+typedef enum {
+    MMDIT_OK = 0,
+    MMDIT_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size or parameter */
+    MMDIT_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement     */
+    MMDIT_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required      */
+    MMDIT_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed      */
+} mmdit_status;
+
+typedef enum { MMDIT_FP32 = 0, MMDIT_BF16 = 1 } mmdit_dtype;
+
+typedef enum { MMDIT_SEG_VIDEO = 0, MMDIT_SEG_AUDIO = 1, MMDIT_SEG_TEXT = 2 } mmdit_seg_kind;
+
+typedef enum {
+    MMDIT_OP_JOINT_ATTN = 0,
+    MMDIT_OP_AV_CROSS_ATTN = 1,
+    MMDIT_OP_BLOCK_SPARSE_ATTN = 2
+} mmdit_op;
+
+/* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
+ * VIDEO: `count` = T*H*W tokens of frames t0 .. t0+T-1 in raster (t, h, w)
+ *        order; conditioning latents are a VIDEO segment with negative t0
+ *        (SkyReels-V4 analysis, workflow step 1 and novelty 4: negative
+ *        temporal indices mark conditioning latents).
+ * AUDIO: token j sits at temporal position j * t_scale and h = w = 0, so it is
+ *        turned by the video's temporal bands only; t_scale = 21/218 lines 218
+ *        audio tokens up with 21 frames (novelty 5; trdm.cn article, 2.2).
+ * TEXT:  not rotated (the pages give text no positions). */
+typedef struct {
+    int32_t kind;          /* mmdit_seg_kind */
+    int64_t offset;        /* first token of the segment */
+    int64_t count;         /* number of tokens */
+    int32_t t0, T, H, W;   /* VIDEO only */
+    double t_scale;        /* AUDIO only */
+} mmdit_segment;
+
+/* RoPE geometry.  head_dim = d_t + d_h + d_w, each slice even; slices sit in
+ * t, h, w order and rotate adjacent pairs (2i, 2i+1) of the slice by angle
+ * p_axis * theta^(-2i/d_axis).  With the vectorised kernel every slice width
+ * must be a multiple of 8. */
+typedef struct {
+    int32_t heads, head_dim;
+    int32_t d_t, d_h, d_w;
+    double theta;
+    const mmdit_segment* segs;
+    int32_t n_segs;        /* 1 .. MMDIT_MAX_SEGMENTS, non-overlapping */
+    int64_t n_tokens;      /* tokens in the Q / K buffers */
+} mmdit_rope_desc;
+
+/* Block-sparse geometry (Prism page, "Ideas clave" and "Metodo" section 3):
+ * macro-zones zone[3] = {Z_T, Z_H, Z_W} cut into uniform blocks block[3];
+ * blocks are numbered zone by zone in raster order, raster inside a zone.
+ * Each query block keeps the longer of its top_k most probable key blocks and
+ * the smallest probability-ordered prefix whose mass reaches top_p (ties go
+ * to the lower block id). */
+typedef struct {
+    int32_t zone[3];
+    int32_t block[3];
+    int32_t top_k;         /* >= 0 */
+    double top_p;          /* in [0, 1]; >= 1 keeps every block */
+} mmdit_sparse_desc;
+
+/* ---- host-only calls (no GPU needed) ------------------------------------- */
+
+int32_t mmdit_abi_version(void);
+
+/* Text of the calling thread's last non-OK status ("" if none).  The pointer
+ * stays valid until the thread's next failing library call. */
+const char* mmdit_last_error(void);
+
+/* Number of floats the RoPE table for `desc` needs, or 0 if desc is invalid. */
+size_t mmdit_rope3d_table_floats(const mmdit_rope_desc* desc);
+
+/* Fill `host_table` (mmdit_rope3d_table_floats(desc) floats, caller-owned host
+ * memory) with (cos, sin) pairs: angles in fp64, rounded to fp32.  Per segment
+ * in order: VIDEO -> [T][d_t/2] then [H][d_h/2] then [W][d_w/2] pairs for
+ * positions t0.., 0.., 0..; AUDIO -> [count][d_t/2] pairs for j * t_scale;
+ * TEXT -> nothing.  The caller copies the table to device memory. */
+mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* desc, float* host_table);
+
+/* Workspace bytes `op` needs for these sizes (0 if none).  JOINT_ATTN: n_q, n_kv
+ * as in mmdit_joint_attn.  AV_CROSS_ATTN: n_q = n_video, n_kv = n_audio.
+ * BLOCK_SPARSE_ATTN: n_q = n_kv = T*H*W and `sp` gives the block geometry. */
+size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
+                             int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp);
+
+/* ---- device calls (async on `stream`) ------------------------------------- */
+
+/* Time-shifted 3D RoPE, in place on q and k ([n_tokens][heads][head_dim]).
+ * Sources: SkyReels-V4 analysis (paper.rainbus.top 2602.21818), workflow step 1,
+ * novelties 4 and 5; trdm.cn SkyReels-V4 article, section 2.2.
+ * dev_table: device copy of mmdit_rope3d_build_table's output for `desc`.
+ * Math is fp32 on the stored values; bf16 results are rounded to nearest even.
+ * Tokens outside every VIDEO/AUDIO segment are neither read nor written. */
+mmdit_status mmdit_rope3d(const mmdit_rope_desc* desc, const float* dev_table,
+                          void* q, void* k, int32_t dtype, void* stream);
+
+/* O[i] = sum_j softmax_j(softmax_scale * <q_i, k_j>) v_j per head, no mask.
+ * Sources: SkyReels-V4 analysis, workflow step 3 (joint self-attention over
+ * video/audio and text tokens; video queries text embeddings); trdm.cn
+ * article, section 2.1.  Joint self-attention passes the same concatenated
+ * [cond|video|audio|text] buffer as q, k and v with n_q = n_kv; video->text
+ * passes video queries and text keys.
+ * q [n_q][heads][head_dim], k and v [n_kv][heads][head_dim] in `dtype`,
+ * o [n_q][heads][head_dim] fp32.  head_dim 64 or 128.  bf16: products on
+ * bf16 matrix cores with fp32 accumulation and fp32 online softmax; fp32: fp32
+ * throughout.  n_q >= 0 (0 is a no-op), n_kv >= 1. */
+mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const void* v,
+                              int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                              float softmax_scale, float* o, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Both directions of the audio<->video cross-attention of one block.
+ * Sources: SkyReels-V4 analysis, workflow step 3 and novelty 2 (bidirectional
+ * audio-video cross-attention in every layer); trdm.cn article, section 2.2.
+ * o_video[n_video] = attention(q_v, k_a, v_a)   (video queries, audio keys)
+ * o_audio[n_audio] = attention(q_a, k_v, v_v)   (audio queries, video keys)
+ * The video side includes conditioning-frame tokens.  Shapes as in
+ * mmdit_joint_attn; the two outputs are fp32 and must not alias. */
+mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v_v,
+                                 int64_t n_video, const void* q_a, const void* k_a,
+                                 const void* v_a, int64_t n_audio, int32_t heads,
+                                 int32_t head_dim, int32_t dtype, float softmax_scale,
+                                 float* o_video, float* o_audio, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Block-sparse video self-attention over a T x H x W raster grid.
+ * Source: Prism page (xyznot.com 2610.05416), "Ideas clave" (macro-zones,
+ * hybrid top-k/top-p) and "Metodo" section 3 (mean-pooled block
+ * representatives, block probabilities, S_i = TopK(P_i,k) u TopP(P_i,p),
+ * online-softmax attention over S_i only).
+ * Steps: fp64 block means of Q and K; fp64 logits <Qbar_i, Kbar_j> *
+ * softmax_scale (taken as double: the selection is decided in fp64) and their
+ * row softmax P_i; selection as described for
+ * mmdit_sparse_desc; attention of every query over the tokens of its block's
+ * selected key blocks.
+ * q, k, v [T*H*W][heads][head_dim] bf16; o same shape fp32.
+ * sel_mask [heads][nb][ceil(nb/32)] uint32: bit j%32 of word j/32 set iff key
+ * block j is selected; sel_count [heads][nb] int32 = number of selected blocks.
+ * Either may be NULL if not wanted.  T, H, W must be multiples of the zone,
+ * the zone of the block; block volume 64; head_dim 128. */
+mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v, int32_t T,
+                                     int32_t H, int32_t W, int32_t heads, int32_t head_dim,
+                                     const mmdit_sparse_desc* sp, double softmax_scale, float* o,
+                                     uint32_t* sel_mask, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMDIT_H */

@@ -1,0 +1,279 @@
+"""ctypes binding of libmmdit.so (include/mmdit.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  Tensors are torch tensors used as device memory; the current
+torch stream is passed as the hipStream_t.  There is no fallback: if the
+library is missing, every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmdit.so")
+
+MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMDIT_ERR_HIP = range(5)
+MMDIT_FP32, MMDIT_BF16 = 0, 1
+MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
+MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN = 0, 1, 2
+MMDIT_MAX_SEGMENTS = 16
+
+_STATUS = {1: "MMDIT_ERR_INVALID_ARG", 2: "MMDIT_ERR_UNSUPPORTED", 3: "MMDIT_ERR_WORKSPACE",
+           4: "MMDIT_ERR_HIP"}
+
+
+class MmditError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), msg))
+        self.status = status
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("offset", ctypes.c_int64), ("count", ctypes.c_int64),
+                ("t0", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("W", ctypes.c_int32), ("t_scale", ctypes.c_double)]
+
+
+class RopeDesc(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_t", ctypes.c_int32),
+                ("d_h", ctypes.c_int32), ("d_w", ctypes.c_int32), ("theta", ctypes.c_double),
+                ("segs", ctypes.POINTER(Segment)), ("n_segs", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int64)]
+
+
+class SparseDesc(ctypes.Structure):
+    _fields_ = [("zone", ctypes.c_int32 * 3), ("block", ctypes.c_int32 * 3),
+                ("top_k", ctypes.c_int32), ("top_p", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmmdit.so is not built (%s); run "
+                               "`python -m joint_video_audio_rope_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz, f32, f64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_size_t, ctypes.c_float, ctypes.c_double)
+        L.mmdit_abi_version.restype = i32
+        L.mmdit_abi_version.argtypes = []
+        L.mmdit_last_error.restype = ctypes.c_char_p
+        L.mmdit_last_error.argtypes = []
+        L.mmdit_rope3d_table_floats.restype = sz
+        L.mmdit_rope3d_table_floats.argtypes = [ctypes.POINTER(RopeDesc)]
+        L.mmdit_rope3d_build_table.restype = i32
+        L.mmdit_rope3d_build_table.argtypes = [ctypes.POINTER(RopeDesc), vp]
+        L.mmdit_workspace_bytes.restype = sz
+        L.mmdit_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, ctypes.POINTER(SparseDesc)]
+        L.mmdit_rope3d.restype = i32
+        L.mmdit_rope3d.argtypes = [ctypes.POINTER(RopeDesc), vp, vp, vp, i32, vp]
+        L.mmdit_joint_attn.restype = i32
+        L.mmdit_joint_attn.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, sz, vp]
+        L.mmdit_av_cross_attn.restype = i32
+        L.mmdit_av_cross_attn.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i32, i32, i32, f32,
+                                          vp, vp, vp, sz, vp]
+        L.mmdit_block_sparse_attn.restype = i32
+        L.mmdit_block_sparse_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(SparseDesc), f64, vp, vp, vp, vp, sz, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != MMDIT_OK:
+        raise MmditError(status, lib().mmdit_last_error().decode())
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return MMDIT_BF16
+    if t.dtype == torch.float32:
+        return MMDIT_FP32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ws(nbytes, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace of %d bytes needed" % nbytes)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ---- host-only calls ---------------------------------------------------------
+def mmdit_abi_version():
+    return lib().mmdit_abi_version()
+
+
+def mmdit_last_error():
+    return lib().mmdit_last_error().decode()
+
+
+def layout_segments(T, H, W, n_cond_frames=0, n_audio=0, n_text=0, audio_scale=None):
+    """Segments of one joint sequence [cond | video | audio | text].
+
+    Conditioning frames form a VIDEO segment at t0 = -n_cond_frames (so one
+    frame sits at t = -1); generated frames start at t = 0; audio token j sits
+    at j * audio_scale, audio_scale given as (num, den) (default T / n_audio).
+    """
+    segs = []
+    off = 0
+    if n_cond_frames:
+        n = n_cond_frames * H * W
+        segs.append(dict(kind=MMDIT_SEG_VIDEO, offset=off, count=n, t0=-n_cond_frames,
+                         T=n_cond_frames, H=H, W=W))
+        off += n
+    n = T * H * W
+    segs.append(dict(kind=MMDIT_SEG_VIDEO, offset=off, count=n, t0=0, T=T, H=H, W=W))
+    off += n
+    if n_audio:
+        num, den = audio_scale if audio_scale is not None else (T, n_audio)
+        segs.append(dict(kind=MMDIT_SEG_AUDIO, offset=off, count=n_audio, t_scale=num / den))
+        off += n_audio
+    if n_text:
+        segs.append(dict(kind=MMDIT_SEG_TEXT, offset=off, count=n_text))
+        off += n_text
+    return segs, off
+
+
+class RopeSpec:
+    """A RoPE descriptor kept alive together with its segment array."""
+
+    def __init__(self, segments, n_tokens, heads, head_dim, split, theta=10000.0):
+        arr = (Segment * max(1, len(segments)))()
+        for i, s in enumerate(segments):
+            arr[i] = Segment(s["kind"], s["offset"], s["count"], s.get("t0", 0), s.get("T", 0),
+                             s.get("H", 0), s.get("W", 0), float(s.get("t_scale", 0.0)))
+        self._segs = arr
+        self.desc = RopeDesc(heads, head_dim, split[0], split[1], split[2], float(theta),
+                             ctypes.cast(arr, ctypes.POINTER(Segment)), len(segments), n_tokens)
+        self._dev_table = {}
+
+    def table_floats(self):
+        return lib().mmdit_rope3d_table_floats(ctypes.byref(self.desc))
+
+    def host_table(self):
+        n = self.table_floats()
+        buf = torch.empty(max(n, 1), dtype=torch.float32)
+        _check(lib().mmdit_rope3d_build_table(ctypes.byref(self.desc), ctypes.c_void_p(buf.data_ptr())))
+        return buf[:n]
+
+    def device_table(self, device):
+        dev = torch.device(device)
+        if dev not in self._dev_table:
+            self._dev_table[dev] = self.host_table().to(dev)
+        return self._dev_table[dev]
+
+
+def mmdit_rope3d_table_floats(spec):
+    return spec.table_floats()
+
+
+def mmdit_rope3d_build_table(spec):
+    """Host (cos, sin) table as a CPU float32 tensor."""
+    return spec.host_table()
+
+
+def mmdit_workspace_bytes(op, n_q, n_kv, heads, head_dim, dtype, sparse=None):
+    sp = None if sparse is None else ctypes.byref(sparse)
+    return lib().mmdit_workspace_bytes(op, n_q, n_kv, heads, head_dim, dtype, sp)
+
+
+# ---- device calls ------------------------------------------------------------
+def mmdit_rope3d(spec, q, k, stream=None):
+    """Rotate q and k in place ([n_tokens, heads, head_dim], same dtype)."""
+    assert q.is_contiguous() and k.is_contiguous() and q.dtype == k.dtype and q.shape == k.shape
+    tab = spec.device_table(q.device)
+    _check(lib().mmdit_rope3d(ctypes.byref(spec.desc), _ptr(tab), _ptr(q), _ptr(k), _dtype(q),
+                              _stream(stream)))
+    return q, k
+
+
+def mmdit_joint_attn(q, k, v, softmax_scale=None, o=None, ws=None, stream=None):
+    """Softmax attention of q [n_q, h, d] against k, v [n_kv, h, d]; fp32 output."""
+    n_q, h, d = q.shape
+    n_kv = k.shape[0]
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if o is None:
+        o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_joint_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
+                                  _ptr(o), _ptr(ws), wsb, _stream(stream)))
+    return o
+
+
+def mmdit_av_cross_attn(q_v, k_v, v_v, q_a, k_a, v_a, softmax_scale=None, o_video=None,
+                        o_audio=None, ws=None, stream=None):
+    """Video queries -> audio keys and audio queries -> video keys; fp32 outputs."""
+    n_v, h, d = q_v.shape
+    n_a = q_a.shape[0]
+    for t in (q_v, k_v, v_v, q_a, k_a, v_a):
+        assert t.is_contiguous() and t.dtype == q_v.dtype
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if o_video is None:
+        o_video = torch.empty((n_v, h, d), dtype=torch.float32, device=q_v.device)
+    if o_audio is None:
+        o_audio = torch.empty((n_a, h, d), dtype=torch.float32, device=q_v.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_AV_CROSS_ATTN, n_v, n_a, h, d, _dtype(q_v))
+    ws, wsb = _ws(need, q_v.device, ws)
+    _check(lib().mmdit_av_cross_attn(_ptr(q_v), _ptr(k_v), _ptr(v_v), n_v, _ptr(q_a), _ptr(k_a),
+                                     _ptr(v_a), n_a, h, d, _dtype(q_v), scale, _ptr(o_video),
+                                     _ptr(o_audio), _ptr(ws), wsb, _stream(stream)))
+    return o_video, o_audio
+
+
+def sparse_desc(zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9):
+    sd = SparseDesc()
+    for i in range(3):
+        sd.zone[i] = zone[i]
+        sd.block[i] = block[i]
+    sd.top_k = top_k
+    sd.top_p = top_p
+    return sd
+
+
+def mmdit_block_sparse_attn(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4), top_k=32,
+                            top_p=0.9, softmax_scale=None, o=None, sel_mask=None, sel_count=None,
+                            ws=None, stream=None, want_selection=True):
+    """Block-sparse self-attention over a T x H x W raster grid.
+
+    Returns (o fp32, sel_mask uint32-as-int32 [h, nb, ceil(nb/32)], sel_count int32 [h, nb]).
+    """
+    n, h, d = q.shape
+    assert n == T * H * W and q.dtype == torch.bfloat16
+    sd = sparse_desc(zone, block, top_k, top_p)
+    nb = n // (block[0] * block[1] * block[2])
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+    if want_selection and sel_mask is None:
+        sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+    if want_selection and sel_count is None:
+        sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_block_sparse_attn(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d,
+                                         ctypes.byref(sd), scale, _ptr(o), _ptr(sel_mask),
+                                         _ptr(sel_count), _ptr(ws), wsb, _stream(stream)))
+    return o, sel_mask, sel_count

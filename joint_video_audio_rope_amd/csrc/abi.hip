@@ -1,0 +1,482 @@
+// C ABI: argument checks, workspace plans, the host RoPE table builder and
+// kernel dispatch.  Every check runs before the first HIP call so a failed
+// call enqueues nothing.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+
+using namespace mmdit;
+
+namespace {
+
+thread_local std::string g_err;
+
+mmdit_status fail(mmdit_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+mmdit_status hip_fail(hipError_t e, const char* what) {
+    return fail(MMDIT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t elem_size(int dtype) { return dtype == MMDIT_BF16 ? 2 : 4; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- dense attention plan ----------------------------------------------------
+struct AttnPlan {
+    int64_t n_pad, n_q_pad;
+    int32_t q_tiles, kv_tiles, splits, tiles_per_split;
+    size_t vt_bytes, part_o_bytes, part_ml_bytes;
+    size_t total() const { return vt_bytes + part_o_bytes + part_ml_bytes; }
+};
+
+AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
+    AttnPlan p{};
+    if (dtype != MMDIT_BF16) return p;   // the fp32 kernel needs no workspace
+    p.n_pad = round_up(n_kv, kTileN);
+    p.q_tiles = (int32_t)((n_q + 127) / 128);
+    p.n_q_pad = (int64_t)p.q_tiles * 128;
+    p.kv_tiles = (int32_t)(p.n_pad / kTileN);
+    const int64_t base = (int64_t)p.q_tiles * heads;
+    int splits = 1;
+    if (base > 0 && base < 512) {
+        const int64_t want = (1024 + base - 1) / base;
+        const int64_t cap = std::max<int64_t>(1, p.kv_tiles / 4);
+        splits = (int)std::min(want, cap);
+    }
+    p.tiles_per_split = (p.kv_tiles + splits - 1) / splits;
+    p.splits = (p.kv_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
+    p.vt_bytes = align256((size_t)heads * hd * p.n_pad * 2);
+    if (p.splits > 1) {
+        p.part_o_bytes = align256((size_t)p.splits * heads * p.n_q_pad * hd * 4);
+        p.part_ml_bytes = align256((size_t)p.splits * heads * p.n_q_pad * 2 * 4);
+    }
+    return p;
+}
+
+mmdit_status check_attn_args(const void* q, int64_t n_q, const void* k, const void* v,
+                             int64_t n_kv, int heads, int hd, int dtype, float scale,
+                             const float* o, const char* who) {
+    if (dtype != MMDIT_FP32 && dtype != MMDIT_BF16)
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: dtype %d is neither MMDIT_FP32 nor MMDIT_BF16", who,
+                    dtype);
+    if (hd != 64 && hd != 128)
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", who, hd);
+    if (heads < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: heads %d < 1", who, heads);
+    if (n_q < 0) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_q %lld < 0", who, (long long)n_q);
+    if (n_kv < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_kv %lld < 1", who, (long long)n_kv);
+    if (!std::isfinite(scale)) return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale not finite", who);
+    const int64_t lim = (int64_t)1 << 31;
+    if (n_q * heads >= lim || n_kv * heads >= lim)
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: tokens * heads must stay below 2^31", who);
+    if (!k || !v) return fail(MMDIT_ERR_INVALID_ARG, "%s: null k or v", who);
+    if (!aligned16(k) || !aligned16(v))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", who);
+    if (n_q > 0) {
+        if (!q || !o) return fail(MMDIT_ERR_INVALID_ARG, "%s: null q or o", who);
+        if (!aligned16(q) || !aligned16(o))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: q and o must be 16-byte aligned", who);
+        const size_t es = elem_size(dtype);
+        const size_t ob = (size_t)n_q * heads * hd * 4;
+        if (overlaps(o, ob, q, (size_t)n_q * heads * hd * es) ||
+            overlaps(o, ob, k, (size_t)n_kv * heads * hd * es) ||
+            overlaps(o, ob, v, (size_t)n_kv * heads * hd * es))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: output aliases an input", who);
+    }
+    return MMDIT_OK;
+}
+
+// Enqueue one attention after its arguments and workspace were checked.
+mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, int64_t n_kv,
+                      int heads, int hd, int dtype, float scale, float* o, char* ws,
+                      const AttnPlan& p, hipStream_t s, const char* who) {
+    if (n_q == 0) return MMDIT_OK;
+    hipError_t e;
+    if (dtype == MMDIT_FP32) {
+        e = launch_attn_fp32((const float*)q, n_q, (const float*)k, (const float*)v, n_kv, heads,
+                             hd, scale, o, s);
+        return e == hipSuccess ? MMDIT_OK : hip_fail(e, who);
+    }
+    AttnArgs a{};
+    a.q = (const __bf16*)q;
+    a.k = (const __bf16*)k;
+    a.vt = (const _Float16*)ws;
+    a.o = o;
+    a.part_o = p.splits > 1 ? (float*)(ws + p.vt_bytes) : nullptr;
+    a.part_ml = p.splits > 1 ? (float*)(ws + p.vt_bytes + p.part_o_bytes) : nullptr;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.n_pad = p.n_pad;
+    a.n_q_pad = p.n_q_pad;
+    a.heads = heads;
+    a.q_tiles = p.q_tiles;
+    a.splits = p.splits;
+    a.tiles_per_split = p.tiles_per_split;
+    a.kv_tiles = p.kv_tiles;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    e = launch_vt_dense((const __bf16*)v, n_kv, p.n_pad, heads, hd, (_Float16*)ws, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    e = launch_attn_bf16(a, hd, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if (p.splits > 1) {
+        e = launch_attn_combine(a, hd, s);
+        if (e != hipSuccess) return hip_fail(e, who);
+    }
+    return MMDIT_OK;
+}
+
+// ---- RoPE ----------------------------------------------------------------------
+struct RopePlan {
+    size_t floats = 0;
+    RopeArgs args{};
+};
+
+mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
+    if (!d) return fail(MMDIT_ERR_INVALID_ARG, "rope: null descriptor");
+    if (d->heads < 1) return fail(MMDIT_ERR_INVALID_ARG, "rope: heads %d < 1", d->heads);
+    if (d->head_dim < 8 || d->head_dim % 8)
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: head_dim %d must be a positive multiple of 8",
+                    d->head_dim);
+    if (d->d_t < 0 || d->d_h < 0 || d->d_w < 0 || d->d_t % 8 || d->d_h % 8 || d->d_w % 8)
+        return fail(MMDIT_ERR_UNSUPPORTED, "rope: slice widths (%d, %d, %d) must be multiples of 8",
+                    d->d_t, d->d_h, d->d_w);
+    if (d->d_t + d->d_h + d->d_w != d->head_dim)
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: d_t + d_h + d_w != head_dim");
+    if (!(d->theta > 0.0) || !std::isfinite(d->theta))
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: theta must be positive and finite");
+    if (d->n_segs < 1 || d->n_segs > MMDIT_MAX_SEGMENTS)
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: n_segs %d outside 1..%d", d->n_segs,
+                    MMDIT_MAX_SEGMENTS);
+    if (!d->segs) return fail(MMDIT_ERR_INVALID_ARG, "rope: null segment array");
+    if (d->n_tokens < 0) return fail(MMDIT_ERR_INVALID_ARG, "rope: n_tokens < 0");
+    if (dtype != MMDIT_FP32 && dtype != MMDIT_BF16)
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: bad dtype %d", dtype);
+
+    std::vector<std::pair<int64_t, int64_t>> ranges;
+    RopeArgs& a = out->args;
+    a.heads = d->heads;
+    a.head_dim = d->head_dim;
+    a.d_t = d->d_t;
+    a.d_h = d->d_h;
+    a.d_w = d->d_w;
+    const int epc = dtype == MMDIT_BF16 ? 8 : 4;
+    a.chunks_per_token = d->heads * d->head_dim / epc;
+    int64_t pairs = 0;   // float2 entries
+    int64_t chunks = 0;
+    int ns = 0;
+    for (int i = 0; i < d->n_segs; ++i) {
+        const mmdit_segment& s = d->segs[i];
+        if (s.offset < 0 || s.count < 0 || s.offset + s.count > d->n_tokens)
+            return fail(MMDIT_ERR_INVALID_ARG, "rope: segment %d outside the token range", i);
+        if (s.count > 0) ranges.push_back({s.offset, s.offset + s.count});
+        if (s.kind == MMDIT_SEG_TEXT) continue;
+        if (s.kind != MMDIT_SEG_VIDEO && s.kind != MMDIT_SEG_AUDIO)
+            return fail(MMDIT_ERR_INVALID_ARG, "rope: segment %d has unknown kind %d", i, s.kind);
+        RopeSeg rs{};
+        rs.kind = s.kind;
+        rs.offset = s.offset;
+        if (s.kind == MMDIT_SEG_VIDEO) {
+            if (s.T < 1 || s.H < 1 || s.W < 1 || (int64_t)s.T * s.H * s.W != s.count)
+                return fail(MMDIT_ERR_INVALID_ARG, "rope: video segment %d needs count == T*H*W >= 1",
+                            i);
+            rs.T = s.T, rs.H = s.H, rs.W = s.W;
+            rs.tab_t = (int32_t)pairs;
+            pairs += (int64_t)s.T * (d->d_t / 2);
+            rs.tab_h = (int32_t)pairs;
+            pairs += (int64_t)s.H * (d->d_h / 2);
+            rs.tab_w = (int32_t)pairs;
+            pairs += (int64_t)s.W * (d->d_w / 2);
+        } else {
+            if (!std::isfinite(s.t_scale))
+                return fail(MMDIT_ERR_INVALID_ARG, "rope: audio segment %d t_scale not finite", i);
+            rs.T = rs.H = rs.W = 1;
+            rs.tab_t = (int32_t)pairs;
+            pairs += s.count * (d->d_t / 2);
+        }
+        const int64_t c = s.count * a.chunks_per_token;
+        if (c >= ((int64_t)1 << 31))
+            return fail(MMDIT_ERR_UNSUPPORTED, "rope: segment %d has 2^31 or more chunks", i);
+        rs.chunk_begin = chunks;
+        chunks += c;
+        rs.chunk_end = chunks;
+        if (c > 0) a.seg[ns++] = rs;
+    }
+    if (pairs >= ((int64_t)1 << 30)) return fail(MMDIT_ERR_UNSUPPORTED, "rope: table too large");
+    std::sort(ranges.begin(), ranges.end());
+    for (size_t i = 1; i < ranges.size(); ++i)
+        if (ranges[i].first < ranges[i - 1].second)
+            return fail(MMDIT_ERR_INVALID_ARG, "rope: segments overlap");
+    a.n_segs = ns;
+    a.total_chunks = chunks;
+    out->floats = (size_t)pairs * 2;
+    return MMDIT_OK;
+}
+
+// ---- block sparse plan ------------------------------------------------------------
+struct SparsePlan {
+    SparseGeom g{};
+    size_t off_qbar, off_kbar, off_scores, off_list, off_count, off_base, off_vt, total;
+};
+
+mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_sparse_desc* sp,
+                         SparsePlan* p) {
+    if (!sp) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: null sparse descriptor");
+    if (T < 1 || H < 1 || W < 1 || heads < 1)
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: T, H, W and heads must be >= 1");
+    if (hd != 128) return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: head_dim %d (supported: 128)", hd);
+    for (int a = 0; a < 3; ++a)
+        if (sp->zone[a] < 1 || sp->block[a] < 1 || sp->zone[a] % sp->block[a])
+            return fail(MMDIT_ERR_INVALID_ARG,
+                        "block_sparse: zone sizes must be positive multiples of block sizes");
+    if (T % sp->zone[0] || H % sp->zone[1] || W % sp->zone[2])
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: T, H, W must be multiples of the zone");
+    if (sp->block[0] * sp->block[1] * sp->block[2] != kTileN)
+        return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: block volume must be %d", kTileN);
+    if (sp->top_k < 0) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: top_k < 0");
+    if (!(sp->top_p >= 0.0 && sp->top_p <= 1.0))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: top_p must lie in [0, 1]");
+    const int64_t n = (int64_t)T * H * W;
+    if (n * heads >= ((int64_t)1 << 31))
+        return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: tokens * heads must stay below 2^31");
+    const int64_t nb = n / kTileN;
+    if (nb > 4096) return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: %lld blocks (max 4096)", (long long)nb);
+    SparseGeom& g = p->g;
+    g.T = T, g.H = H, g.W = W;
+    g.ZT = sp->zone[0], g.ZH = sp->zone[1], g.ZW = sp->zone[2];
+    g.BT = sp->block[0], g.BH = sp->block[1], g.BW = sp->block[2];
+    g.nzh = H / g.ZH, g.nzw = W / g.ZW;
+    g.bz_t = g.ZT / g.BT, g.bz_h = g.ZH / g.BH, g.bz_w = g.ZW / g.BW;
+    g.nb = (int32_t)nb;
+    g.heads = heads;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    p->off_qbar = take((size_t)heads * nb * hd * 8);
+    p->off_kbar = take((size_t)heads * nb * hd * 8);
+    p->off_scores = take((size_t)heads * nb * nb * 8);
+    p->off_list = take((size_t)heads * nb * nb * 2);
+    p->off_count = take((size_t)heads * nb * 4);
+    p->off_base = take((size_t)nb * 4);
+    p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
+    p->total = off;
+    return MMDIT_OK;
+}
+
+mmdit_status check_ws(const void* ws, size_t ws_bytes, size_t need, const char* who) {
+    if (need == 0) return MMDIT_OK;
+    if (!ws) return fail(MMDIT_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got null", who, need);
+    if (ws_bytes < need)
+        return fail(MMDIT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", who, ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
+    return MMDIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mmdit_abi_version(void) { return MMDIT_ABI_VERSION; }
+
+const char* mmdit_last_error(void) { return g_err.c_str(); }
+
+size_t mmdit_rope3d_table_floats(const mmdit_rope_desc* desc) {
+    RopePlan p;
+    if (plan_rope(desc, MMDIT_BF16, &p) != MMDIT_OK) return 0;
+    return p.floats;
+}
+
+mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* d, float* host_table) {
+    RopePlan p;
+    mmdit_status st = plan_rope(d, MMDIT_BF16, &p);
+    if (st != MMDIT_OK) return st;
+    if (p.floats > 0 && !host_table) return fail(MMDIT_ERR_INVALID_ARG, "rope table: null output");
+    size_t at = 0;
+    // pair i of an axis of width w turns at position * theta^(-2i/w)
+    auto axis = [&](double pos, int width) {
+        for (int i = 0; i < width / 2; ++i) {
+            const double om = std::pow(d->theta, -2.0 * i / (double)width);
+            const double ang = pos * om;
+            host_table[at++] = (float)std::cos(ang);
+            host_table[at++] = (float)std::sin(ang);
+        }
+    };
+    for (int i = 0; i < d->n_segs; ++i) {
+        const mmdit_segment& s = d->segs[i];
+        if (s.kind == MMDIT_SEG_VIDEO) {
+            for (int t = 0; t < s.T; ++t) axis((double)(s.t0 + t), d->d_t);
+            for (int h = 0; h < s.H; ++h) axis((double)h, d->d_h);
+            for (int w = 0; w < s.W; ++w) axis((double)w, d->d_w);
+        } else if (s.kind == MMDIT_SEG_AUDIO) {
+            for (int64_t j = 0; j < s.count; ++j) axis((double)j * s.t_scale, d->d_t);
+        }
+    }
+    return MMDIT_OK;
+}
+
+size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
+                             int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp) {
+    if (heads < 1 || head_dim < 1 || n_q < 0 || n_kv < 0) return 0;
+    if (op == MMDIT_OP_JOINT_ATTN) {
+        if (n_kv < 1) return 0;
+        return plan_attn(n_q, n_kv, heads, head_dim, dtype).total();
+    }
+    if (op == MMDIT_OP_AV_CROSS_ATTN) {
+        if (n_q < 1 || n_kv < 1) return 0;
+        return plan_attn(n_q, n_kv, heads, head_dim, dtype).total() +
+               plan_attn(n_kv, n_q, heads, head_dim, dtype).total();
+    }
+    if (op == MMDIT_OP_BLOCK_SPARSE_ATTN) {
+        if (!sp) return 0;
+        // T, H, W are not known here; the plan depends on them only through nb.
+        const int64_t nb = n_q / kTileN;
+        size_t t = 0;
+        t += align256((size_t)heads * nb * head_dim * 8) * 2;
+        t += align256((size_t)heads * nb * nb * 8);
+        t += align256((size_t)heads * nb * nb * 2);
+        t += align256((size_t)heads * nb * 4);
+        t += align256((size_t)nb * 4);
+        t += align256((size_t)heads * nb * head_dim * kTileN * 2);
+        return t;
+    }
+    return 0;
+}
+
+mmdit_status mmdit_rope3d(const mmdit_rope_desc* desc, const float* dev_table, void* q, void* k,
+                          int32_t dtype, void* stream) {
+    RopePlan p;
+    mmdit_status st = plan_rope(desc, dtype, &p);
+    if (st != MMDIT_OK) return st;
+    if (p.args.total_chunks == 0) return MMDIT_OK;
+    if (!q || !k || !dev_table) return fail(MMDIT_ERR_INVALID_ARG, "rope: null q, k or table");
+    if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(dev_table) & 7u))
+        return fail(MMDIT_ERR_INVALID_ARG, "rope: q, k must be 16-byte and the table 8-byte aligned");
+    const size_t bytes = (size_t)desc->n_tokens * desc->heads * desc->head_dim * elem_size(dtype);
+    if (overlaps(q, bytes, k, bytes)) return fail(MMDIT_ERR_INVALID_ARG, "rope: q and k overlap");
+    hipError_t e = launch_rope(p.args, dev_table, q, k, dtype, (hipStream_t)stream);
+    return e == hipSuccess ? MMDIT_OK : hip_fail(e, "rope");
+}
+
+mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const void* v,
+                              int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                              float softmax_scale, float* o, void* ws, size_t ws_bytes,
+                              void* stream) {
+    mmdit_status st = check_attn_args(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale,
+                                      o, "joint_attn");
+    if (st != MMDIT_OK) return st;
+    const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
+    if (n_q > 0 && (st = check_ws(ws, ws_bytes, p.total(), "joint_attn")) != MMDIT_OK) return st;
+    return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, (char*)ws, p,
+                    (hipStream_t)stream, "joint_attn");
+}
+
+mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v_v,
+                                 int64_t n_video, const void* q_a, const void* k_a,
+                                 const void* v_a, int64_t n_audio, int32_t heads,
+                                 int32_t head_dim, int32_t dtype, float softmax_scale,
+                                 float* o_video, float* o_audio, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (n_video < 1 || n_audio < 1)
+        return fail(MMDIT_ERR_INVALID_ARG, "av_cross_attn: n_video and n_audio must be >= 1");
+    mmdit_status st = check_attn_args(q_v, n_video, k_a, v_a, n_audio, heads, head_dim, dtype,
+                                      softmax_scale, o_video, "av_cross_attn (video->audio)");
+    if (st != MMDIT_OK) return st;
+    st = check_attn_args(q_a, n_audio, k_v, v_v, n_video, heads, head_dim, dtype, softmax_scale,
+                         o_audio, "av_cross_attn (audio->video)");
+    if (st != MMDIT_OK) return st;
+    const size_t ob_v = (size_t)n_video * heads * head_dim * 4;
+    const size_t ob_a = (size_t)n_audio * heads * head_dim * 4;
+    const size_t es = elem_size(dtype);
+    if (overlaps(o_video, ob_v, o_audio, ob_a) ||
+        overlaps(o_video, ob_v, q_a, (size_t)n_audio * heads * head_dim * es) ||
+        overlaps(o_video, ob_v, k_v, (size_t)n_video * heads * head_dim * es) ||
+        overlaps(o_video, ob_v, v_v, (size_t)n_video * heads * head_dim * es) ||
+        overlaps(o_audio, ob_a, q_v, (size_t)n_video * heads * head_dim * es) ||
+        overlaps(o_audio, ob_a, k_a, (size_t)n_audio * heads * head_dim * es) ||
+        overlaps(o_audio, ob_a, v_a, (size_t)n_audio * heads * head_dim * es))
+        return fail(MMDIT_ERR_INVALID_ARG, "av_cross_attn: an output aliases an input or the other output");
+    const AttnPlan pva = plan_attn(n_video, n_audio, heads, head_dim, dtype);
+    const AttnPlan pav = plan_attn(n_audio, n_video, heads, head_dim, dtype);
+    if ((st = check_ws(ws, ws_bytes, pva.total() + pav.total(), "av_cross_attn")) != MMDIT_OK)
+        return st;
+    char* w = (char*)ws;
+    st = run_attn(q_v, n_video, k_a, v_a, n_audio, heads, head_dim, dtype, softmax_scale, o_video,
+                  w, pva, (hipStream_t)stream, "av_cross_attn (video->audio)");
+    if (st != MMDIT_OK) return st;
+    return run_attn(q_a, n_audio, k_v, v_v, n_video, heads, head_dim, dtype, softmax_scale,
+                    o_audio, w ? w + pva.total() : nullptr, pav, (hipStream_t)stream,
+                    "av_cross_attn (audio->video)");
+}
+
+mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v, int32_t T,
+                                     int32_t H, int32_t W, int32_t heads, int32_t head_dim,
+                                     const mmdit_sparse_desc* sp, double softmax_scale, float* o,
+                                     uint32_t* sel_mask, int32_t* sel_count, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    SparsePlan p{};
+    mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
+    if (st != MMDIT_OK) return st;
+    if (!std::isfinite(softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: softmax_scale not finite");
+    if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: null q, k, v or o");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: q, k, v, o must be 16-byte aligned");
+    if ((sel_mask && !aligned16(sel_mask)) || (sel_count && (reinterpret_cast<uintptr_t>(sel_count) & 3u)))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: misaligned sel_mask or sel_count");
+    const size_t n = (size_t)T * H * W;
+    const size_t ib = n * heads * head_dim * 2, ob = n * heads * head_dim * 4;
+    if (overlaps(o, ob, q, ib) || overlaps(o, ob, k, ib) || overlaps(o, ob, v, ib))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: output aliases an input");
+    if ((st = check_ws(ws, ws_bytes, p.total, "block_sparse")) != MMDIT_OK) return st;
+    char* w = (char*)ws;
+    SparseWs sw{};
+    sw.qbar = (double*)(w + p.off_qbar);
+    sw.kbar = (double*)(w + p.off_kbar);
+    sw.scores = (double*)(w + p.off_scores);
+    sw.list = (uint16_t*)(w + p.off_list);
+    sw.count = (int32_t*)(w + p.off_count);
+    sw.base = (int32_t*)(w + p.off_base);
+    sw.vt = (_Float16*)(w + p.off_vt);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse pool");
+    if ((e = launch_vt_blocks(p.g, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse vt");
+    if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse scores");
+    if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, sel_mask, sel_count, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse select");
+    if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
+                                (float)(softmax_scale * 1.4426950408889634), sw, o, s)) !=
+        hipSuccess)
+        return hip_fail(e, "block_sparse attention");
+    return MMDIT_OK;
+}
+
+}  // extern "C"

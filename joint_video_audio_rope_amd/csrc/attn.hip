@@ -1,0 +1,280 @@
+// Dense softmax attention kernels.
+//
+//   O_i = sum_j softmax_j(s <q_i, k_j>) v_j   per head, no mask
+//
+// which the SkyReels-V4 pages use for the joint self-attention over
+// [video | audio | text] tokens, for video queries against text embeddings
+// and for both directions of the audio<->video cross-attention
+// (paper.rainbus.top analysis, workflow step 3 and novelty 2; trdm.cn
+// article, sections 2.1-2.2).
+//
+// bf16 path: 256-thread workgroups (4 waves x 32 queries = 128 queries) walk
+// the key range in 64-key tiles staged through LDS; the next tile's global
+// loads are in flight in registers while the current tile is computed.  When
+// there are too few query tiles to fill 256 CUs (audio queries against video
+// keys) the key range is split and a combine kernel merges the partial
+// results by their log-sum-exp.  Workgroup ids are remapped so that the
+// workgroups running on one XCD (ids congruent mod 8) take consecutive query
+// tiles of the same head and share that head's K/V through their L2.
+#include "attn_core.hpp"
+
+namespace mmdit {
+
+namespace {
+
+// ---- V^T staging: [n_kv][heads][hd] bf16 -> [heads][hd][n_pad] fp16 -------
+template <int HD>
+__global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict__ v, int64_t n_kv,
+                                                       int64_t n_pad, int heads,
+                                                       _Float16* __restrict__ vt) {
+    __shared__ _Float16 tile[kTileN][HD + 2];
+    const int head = blockIdx.y;
+    const int64_t k0 = (int64_t)blockIdx.x * kTileN;
+    constexpr int CPR = HD / 8;                 // 16-byte chunks per row
+    for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
+        const int r = u / CPR, c = u % CPR;
+        const int64_t key = k0 + r;
+        const bf16x8 x = load_bf16x8(v + (key * heads + head) * HD + c * 8, key < n_kv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)(float)x[i];
+    }
+    __syncthreads();
+    // each thread writes 8 consecutive keys of one d row
+    for (int u = threadIdx.x; u < HD * (kTileN / 8); u += 256) {
+        const int d = u / (kTileN / 8), c = u % (kTileN / 8);
+        f16x8 y;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = tile[c * 8 + i][d];
+        *reinterpret_cast<f16x8*>(vt + ((int64_t)head * HD + d) * n_pad + k0 + c * 8) = y;
+    }
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+    using L = TileLayout<HD>;
+    constexpr int NT = 256;
+    constexpr int KS = HD / 16;
+    constexpr int DB = HD / 32;
+    constexpr int KCH = kTileN * L::kKChunks / NT;   // K chunks per thread
+    constexpr int VCH = HD * 8 / NT;                 // V^T chunks per thread
+    __shared__ __attribute__((aligned(16))) char lk[L::kKBytes];
+    __shared__ __attribute__((aligned(16))) char lv[L::kVBytes];
+
+    const int total = a.q_tiles * a.heads * a.splits;
+    const int per_xcd = (total + 7) >> 3;
+    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (logical >= total) return;
+    const int qt = logical % a.q_tiles;
+    const int hs = logical / a.q_tiles;
+    const int split = hs % a.splits;
+    const int head = hs / a.splits;
+    const int tile0 = split * a.tiles_per_split;
+    const int tile1 = min(a.kv_tiles, tile0 + a.tiles_per_split);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int hh = lane >> 5;
+    const int m = lane & 31;
+    const int64_t rstride = (int64_t)a.heads * HD;
+
+    const int64_t qrow = (int64_t)qt * 128 + wave * 32 + m;
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
+
+    SoftmaxState<HD> st;
+    st.init();
+
+    uint4 kreg[KCH], vreg[VCH];
+    auto gload = [&](int t) {
+        const int64_t kv0 = (int64_t)t * kTileN;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int u = tid + i * NT;
+            const int row = u / L::kKChunks, c = u % L::kKChunks;
+            const int64_t key = kv0 + ((row & ~31) | perm_row(row & 31));
+            kreg[i] = make_uint4(0, 0, 0, 0);
+            if (key < a.n_kv)
+                kreg[i] = *reinterpret_cast<const uint4*>(a.k + key * rstride + head * HD + c * 8);
+        }
+        const _Float16* vb = a.vt + (int64_t)head * HD * a.n_pad + kv0;
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int u = tid + i * NT;
+            const int d = u >> 3, c = u & 7;
+            vreg[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)d * a.n_pad + c * 8);
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int u = tid + i * NT;
+            const int row = u / L::kKChunks, c = u % L::kKChunks;
+            *reinterpret_cast<uint4*>(lk + L::k_off(row, c)) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int u = tid + i * NT;
+            const int d = u >> 3, c = u & 7;
+            *reinterpret_cast<uint4*>(lv + L::v_off(d, c)) = vreg[i];
+        }
+    };
+
+    gload(tile0);
+    for (int t = tile0; t < tile1; ++t) {
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (t + 1 < tile1) gload(t + 1);
+        const int64_t valid = a.n_kv - (int64_t)t * kTileN;
+        if (valid < kTileN)
+            attn_tile<HD, true>(lk, lv, qf, st, a.scale_log2, (int)valid);
+        else
+            attn_tile<HD, false>(lk, lv, qf, st, a.scale_log2, kTileN);
+    }
+
+    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    if (qrow >= a.n_q) return;
+    if (a.splits == 1) {
+        const float inv = 1.f / l_tot;
+        float* orow = a.o + qrow * rstride + head * HD;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * db + 8 * g + 4 * hh;
+                *reinterpret_cast<float4*>(orow + d0) =
+                    make_float4(st.o[db][4 * g] * inv, st.o[db][4 * g + 1] * inv,
+                                st.o[db][4 * g + 2] * inv, st.o[db][4 * g + 3] * inv);
+            }
+    } else {
+        const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
+        float* orow = a.part_o + prow * HD;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * db + 8 * g + 4 * hh;
+                *reinterpret_cast<float4*>(orow + d0) =
+                    make_float4(st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                                st.o[db][4 * g + 3]);
+            }
+        if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m_run, l_tot);
+    }
+}
+
+// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int C4 = HD / 4;
+    const int64_t total = a.n_q * a.heads * C4;
+    if (g >= total) return;
+    const int c4 = (int)(g % C4);
+    const int64_t qh = g / C4;
+    const int head = (int)(qh % a.heads);
+    const int64_t q = qh / a.heads;
+    float M = -__builtin_inff();
+    for (int s = 0; s < a.splits; ++s)
+        M = fmaxf(M, a.part_ml[(((int64_t)s * a.heads + head) * a.n_q_pad + q) * 2]);
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    float den = 0.f;
+    for (int s = 0; s < a.splits; ++s) {
+        const int64_t prow = ((int64_t)s * a.heads + head) * a.n_q_pad + q;
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+        const float w = __builtin_amdgcn_exp2f(ml.x - M);
+        const float4 x = *reinterpret_cast<const float4*>(a.part_o + prow * HD + c4 * 4);
+        num.x += w * x.x, num.y += w * x.y, num.z += w * x.z, num.w += w * x.w;
+        den += w * ml.y;
+    }
+    const float inv = 1.f / den;
+    *reinterpret_cast<float4*>(a.o + (q * a.heads + head) * HD + c4 * 4) =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+}
+
+// fp32 path: one lane per (query, head), keys walked in order with an online
+// softmax in fp32.  Meant for small problems (the fp32 parity workload).
+template <int HD>
+__global__ __launch_bounds__(64) void attn_fp32_kernel(const float* __restrict__ q, int64_t n_q,
+                                                       const float* __restrict__ k,
+                                                       const float* __restrict__ v, int64_t n_kv,
+                                                       int heads, float scale, float* __restrict__ o) {
+    const int head = blockIdx.y;
+    const int64_t qi = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (qi >= n_q) return;
+    const int64_t rs = (int64_t)heads * HD;
+    float qv[HD], acc[HD];
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+        qv[d] = q[qi * rs + head * HD + d];
+        acc[d] = 0.f;
+    }
+    float mr = -__builtin_inff(), l = 0.f;
+    for (int64_t j = 0; j < n_kv; ++j) {
+        const float* kr = k + j * rs + head * HD;
+        const float* vr = v + j * rs + head * HD;
+        float sdot = 0.f;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) sdot = fmaf(qv[d], kr[d], sdot);
+        const float x = sdot * scale;
+        const float mn = fmaxf(mr, x);
+        const float al = expf(mr - mn);
+        const float p = expf(x - mn);
+        l = l * al + p;
+#pragma unroll
+        for (int d = 0; d < HD; ++d) acc[d] = fmaf(p, vr[d], acc[d] * al);
+        mr = mn;
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) o[qi * rs + head * HD + d] = acc[d] * inv;
+}
+
+}  // namespace
+
+hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
+                           _Float16* vt, hipStream_t s) {
+    dim3 grid((unsigned)(n_pad / kTileN), (unsigned)heads);
+    if (hd == 128)
+        hipLaunchKernelGGL(vt_dense_kernel<128>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vt);
+    else
+        hipLaunchKernelGGL(vt_dense_kernel<64>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vt);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s) {
+    const int total = a.q_tiles * a.heads * a.splits;
+    const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    if (hd == 128)
+        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, int hd, hipStream_t s) {
+    const int64_t total = a.n_q * a.heads * (hd / 4);
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (hd == 128)
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const float* v,
+                            int64_t n_kv, int heads, int hd, float scale, float* o,
+                            hipStream_t s) {
+    dim3 grid((unsigned)((n_q + 63) / 64), (unsigned)heads);
+    if (hd == 128)
+        hipLaunchKernelGGL(attn_fp32_kernel<128>, grid, dim3(64), 0, s, q, n_q, k, v, n_kv, heads,
+                           scale, o);
+    else
+        hipLaunchKernelGGL(attn_fp32_kernel<64>, grid, dim3(64), 0, s, q, n_q, k, v, n_kv, heads,
+                           scale, o);
+    return hipGetLastError();
+}
+
+}  // namespace mmdit

@@ -1,0 +1,127 @@
+// Internal declarations shared by the library's translation units (not part
+// of the ABI).  Everything here is gfx950 HIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mmdit.h"
+
+namespace mmdit {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Threads per 64-lane wavefront on CDNA.
+constexpr int kWave = 64;
+// Keys per K/V tile of the attention kernels.
+constexpr int kTileN = 64;
+
+// ---- RoPE ------------------------------------------------------------------
+struct RopeSeg {
+    int32_t kind;
+    int32_t T, H, W;
+    int64_t offset;        // first token
+    int64_t chunk_begin;   // first 16-byte chunk id of this segment (global numbering)
+    int64_t chunk_end;
+    int32_t tab_t, tab_h, tab_w;   // float2 index of each axis sub-table in the table
+};
+
+struct RopeArgs {
+    RopeSeg seg[MMDIT_MAX_SEGMENTS];
+    int32_t n_segs;
+    int32_t heads, head_dim, d_t, d_h, d_w;
+    int32_t chunks_per_token;      // heads * head_dim / elems per chunk
+    int64_t total_chunks;
+};
+
+hipError_t launch_rope(const RopeArgs& a, const float* table, void* q, void* k, int dtype,
+                       hipStream_t s);
+
+// ---- dense attention ---------------------------------------------------------
+// V of one key range transposed to fp16 [heads][head_dim][n_pad] (pad keys zero).
+hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
+                           _Float16* vt, hipStream_t s);
+
+struct AttnArgs {
+    const __bf16* q;
+    const __bf16* k;
+    const _Float16* vt;    // [heads][hd][n_pad]
+    float* o;              // [n_q][heads][hd], used when splits == 1
+    float* part_o;         // [splits][heads][n_q_pad][hd], splits > 1
+    float* part_ml;        // [splits][heads][n_q_pad][2]
+    int64_t n_q, n_kv, n_pad, n_q_pad;
+    int32_t heads;
+    int32_t q_tiles;       // ceil(n_q / 128)
+    int32_t splits;
+    int32_t tiles_per_split;
+    int32_t kv_tiles;
+    float scale_log2;      // softmax scale * log2(e)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, int hd, hipStream_t s);
+
+hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const float* v,
+                            int64_t n_kv, int heads, int hd, float scale, float* o,
+                            hipStream_t s);
+
+// ---- block sparse -------------------------------------------------------------
+struct SparseGeom {
+    int32_t T, H, W;
+    int32_t ZT, ZH, ZW;        // zone
+    int32_t BT, BH, BW;        // block
+    int32_t nzh, nzw;          // zones along h and w
+    int32_t bz_t, bz_h, bz_w;  // blocks per zone along each axis
+    int32_t nb;                // blocks in the grid
+    int32_t heads;
+};
+
+struct SparseWs {
+    double* qbar;       // [heads][nb][hd]
+    double* kbar;       // [heads][nb][hd]
+    double* scores;     // [heads][nb][nb] (logits, scaled)
+    uint16_t* list;     // [heads][nb][nb] selected key blocks, ascending
+    int32_t* count;     // [heads][nb]
+    int32_t* base;      // [nb] raster token index of each block's first token
+    _Float16* vt;       // [heads][nb][hd][64]
+};
+
+hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
+                             const SparseWs& w, hipStream_t s);
+hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* v, int hd, const SparseWs& w,
+                            hipStream_t s);
+hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w,
+                               hipStream_t s);
+hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
+                               uint32_t* sel_mask, int32_t* sel_count, hipStream_t s);
+hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
+                              float scale_log2, const SparseWs& w, float* o, hipStream_t s);
+
+// Token index (raster t, h, w) of local token r (0..63, raster inside the
+// 4x4x4 block) of block j.
+__device__ __forceinline__ int64_t block_token(const SparseGeom& g, int j, int r) {
+    const int bpz = g.bz_t * g.bz_h * g.bz_w;
+    const int zone = j / bpz;
+    const int loc = j - zone * bpz;
+    const int zt = zone / (g.nzh * g.nzw);
+    const int zrem = zone - zt * (g.nzh * g.nzw);
+    const int zh = zrem / g.nzw;
+    const int zw = zrem - zh * g.nzw;
+    const int bt = loc / (g.bz_h * g.bz_w);
+    const int brem = loc - bt * (g.bz_h * g.bz_w);
+    const int bh = brem / g.bz_w;
+    const int bw = brem - bh * g.bz_w;
+    const int a = r / (g.BH * g.BW);
+    const int rr = r - a * (g.BH * g.BW);
+    const int b = rr / g.BW;
+    const int c = rr - b * g.BW;
+    const int t = zt * g.ZT + bt * g.BT + a;
+    const int h = zh * g.ZH + bh * g.BH + b;
+    const int w = zw * g.ZW + bw * g.BW + c;
+    return ((int64_t)t * g.H + h) * g.W + w;
+}
+
+}  // namespace mmdit

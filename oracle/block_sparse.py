@@ -97,29 +97,38 @@ def select_blocks(P, top_k, top_p):
     kk = min(max(int(top_k), 0), nk)
     min_cs = np.inf
     min_gap = np.inf
-    ids = np.arange(nk)
+    rows = np.arange(nq)[:, None]
     for hd in range(h):
-        for i in range(nq):
-            p_row = P[hd, i]
-            order = np.lexsort((ids, -p_row))          # P descending, then lower id
-            ps = p_row[order]
-            cs = np.cumsum(ps)
-            if top_p >= 1.0:
-                n_p = nk
-            else:
-                hit = np.nonzero(cs >= top_p)[0]
-                n_p = int(hit[0]) + 1 if hit.size else nk
-                n_p = max(n_p, 1)
-                if hit.size:
-                    min_cs = min(min_cs, abs(cs[n_p - 1] - top_p))
-                    if n_p >= 2:
-                        min_cs = min(min_cs, abs(cs[n_p - 2] - top_p))
-            K = max(kk, n_p)
-            counts[hd, i] = K
-            mask[hd, i, order[:K]] = True
-            if K < nk:
-                a, b = ps[K - 1], ps[K]
-                min_gap = min(min_gap, (a - b) / a if a > 0 else np.inf)
+        # stable sort of -P: descending probability, equal values keep the lower id first
+        order = np.argsort(-P[hd], axis=1, kind="stable")
+        ps = np.take_along_axis(P[hd], order, axis=1)
+        cs = np.cumsum(ps, axis=1)
+        if top_p >= 1.0:
+            n_p = np.full(nq, nk)
+        else:
+            reached = cs >= top_p
+            hit = reached.any(axis=1)
+            first = np.argmax(reached, axis=1)
+            n_p = np.where(hit, first + 1, nk)
+            r = np.flatnonzero(hit)
+            if r.size:
+                at = cs[r, n_p[r] - 1]
+                min_cs = min(min_cs, float(np.min(np.abs(at - top_p))))
+                r2 = r[n_p[r] >= 2]
+                if r2.size:
+                    before = cs[r2, n_p[r2] - 2]
+                    min_cs = min(min_cs, float(np.min(np.abs(before - top_p))))
+        K = np.maximum(kk, n_p)
+        counts[hd] = K
+        sel = np.arange(nk)[None, :] < K[:, None]          # prefix of the order
+        mask[hd][np.broadcast_to(rows, order.shape)[sel], order[sel]] = True
+        cut = np.flatnonzero(K < nk)
+        if cut.size:
+            a = ps[cut, K[cut] - 1]
+            b = ps[cut, K[cut]]
+            with np.errstate(divide="ignore", invalid="ignore"):
+                g = np.where(a > 0, (a - b) / a, np.inf)
+            min_gap = min(min_gap, float(np.min(g)))
     return mask, counts, dict(cumsum=float(min_cs), rel_gap=float(min_gap))
 
 

@@ -1,0 +1,168 @@
+"""The C ABI on the host: the library loads, exports what include/mmdit.h
+declares, builds the RoPE table the oracle's angles define, plans workspaces,
+and rejects bad arguments before touching the GPU (CPU only)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import joint_video_audio_rope_amd as J
+from joint_video_audio_rope_amd import _lib as L
+from oracle import rope as R
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mmdit.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mmdit_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
+              "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
+              "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = J.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, flags=re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_abi_version_and_empty_error():
+    assert J.mmdit_abi_version() == 1
+    assert isinstance(J.mmdit_last_error(), str)
+
+
+def test_struct_layout_matches_header():
+    # the binding's ctypes structs follow the C layout on x86-64
+    assert ctypes.sizeof(L.Segment) == 48
+    assert L.Segment.t_scale.offset == 40
+    assert ctypes.sizeof(L.SparseDesc) == 40
+    assert L.RopeDesc.segs.offset == 32 and L.RopeDesc.n_tokens.offset == 48
+
+
+@pytest.mark.parametrize("name", ["tiny", "block", "480p", "720p"])
+def test_rope_table_matches_oracle_angles(name):
+    w = WORKLOADS[name]
+    spec = J.rope_spec_for(w)
+    tab = spec.host_table().numpy().reshape(-1, 2)
+    ref = R.rope_table(w)
+    parts = []
+    if w["n_cond_frames"]:
+        parts += [ref["cond_t"], ref["h"], ref["w"]]
+    parts += [ref["video_t"], ref["h"], ref["w"], ref["audio_t"]]
+    want = np.concatenate([p.reshape(-1, 2) for p in parts]).astype(np.float32)
+    assert tab.shape == want.shape
+    assert np.array_equal(tab.view(np.uint32), want.view(np.uint32))
+
+
+def test_layout_segments_follow_the_sequence_order():
+    segs, n = J.layout_segments(3, 4, 4, 1, 16, 8, (3, 16))
+    assert n == 88
+    assert [s["kind"] for s in segs] == [0, 0, 1, 2]
+    assert segs[0]["t0"] == -1 and segs[0]["count"] == 16
+    assert segs[1]["offset"] == 16 and segs[1]["t0"] == 0
+    assert segs[2]["offset"] == 64 and segs[2]["t_scale"] == 3 / 16
+    assert segs[3]["offset"] == 80
+
+
+def test_workspace_plans():
+    ws = J.mmdit_workspace_bytes
+    # bf16 joint attention: V^T in fp16, key count padded to 64
+    n = 35050
+    assert ws(J.MMDIT_OP_JOINT_ATTN, n, n, 24, 128, J.MMDIT_BF16) == 24 * 128 * 35072 * 2
+    assert ws(J.MMDIT_OP_JOINT_ATTN, 88, 88, 2, 64, J.MMDIT_FP32) == 0
+    # audio queries against video keys split the keys and add partials
+    big = ws(J.MMDIT_OP_AV_CROSS_ATTN, 34320, 218, 24, 128, J.MMDIT_BF16)
+    assert big > 24 * 128 * 34368 * 2
+    sd = J.sparse_desc()
+    b = ws(J.MMDIT_OP_BLOCK_SPARSE_ATTN, 172032, 172032, 24, 128, J.MMDIT_BF16, sd)
+    assert b >= 24 * 2688 * 2688 * (8 + 2) + 24 * 2688 * 128 * 64 * 2
+
+
+def _call_joint(**over):
+    a = dict(q=16, n_q=10, k=32, v=48, n_kv=10, heads=2, hd=64, dtype=J.MMDIT_BF16, scale=0.125,
+             o=1 << 20, ws=1 << 24, ws_bytes=1 << 20)
+    a.update(over)
+    lib = J.lib()
+    return lib.mmdit_joint_attn(a["q"], a["n_q"], a["k"], a["v"], a["n_kv"], a["heads"], a["hd"],
+                                a["dtype"], a["scale"], a["o"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hd=96), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(dtype=7), L.MMDIT_ERR_INVALID_ARG),
+    (dict(n_kv=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(n_q=-1), L.MMDIT_ERR_INVALID_ARG),
+    (dict(heads=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(k=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(q=8), L.MMDIT_ERR_INVALID_ARG),                     # misaligned
+    (dict(o=16), L.MMDIT_ERR_INVALID_ARG),                    # output aliases q
+    (dict(scale=math.inf), L.MMDIT_ERR_INVALID_ARG),
+    (dict(ws=0), L.MMDIT_ERR_WORKSPACE),
+    (dict(ws_bytes=100), L.MMDIT_ERR_WORKSPACE),
+])
+def test_joint_attn_rejects_bad_arguments(over, status):
+    # fake, never-dereferenced addresses: validation fails before any HIP call
+    assert _call_joint(**over) == status
+    assert J.mmdit_last_error() != ""
+
+
+def test_rope_rejects_bad_descriptors():
+    w = dict(WORKLOADS["480p"])
+    lib = J.lib()
+    good = J.rope_spec_for(w)
+    bad_split = J.RopeSpec(*J.layout_segments(21, 30, 52, 1, 218, 512, (21, 218)), 24, 128, (36, 46, 46))
+    assert lib.mmdit_rope3d(ctypes.byref(bad_split.desc), 256, 512, 1024, 1, None) == L.MMDIT_ERR_UNSUPPORTED
+    segs, n = J.layout_segments(21, 30, 52, 1, 218, 512, (21, 218))
+    segs[1]["offset"] -= 1                                            # overlaps the cond frame
+    ov = J.RopeSpec(segs, n, 24, 128, (32, 48, 48))
+    assert lib.mmdit_rope3d(ctypes.byref(ov.desc), 256, 512, 1024, 1, None) == L.MMDIT_ERR_INVALID_ARG
+    assert "overlap" in J.mmdit_last_error()
+    assert lib.mmdit_rope3d(ctypes.byref(good.desc), 256, 512, 1024, 9, None) == L.MMDIT_ERR_INVALID_ARG
+    assert lib.mmdit_rope3d(ctypes.byref(good.desc), 0, 512, 1024, 1, None) == L.MMDIT_ERR_INVALID_ARG
+    assert lib.mmdit_rope3d(None, 256, 512, 1024, 1, None) == L.MMDIT_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(zone=(8, 8, 6)), L.MMDIT_ERR_INVALID_ARG),
+    (dict(block=(2, 4, 4)), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(top_k=-1), L.MMDIT_ERR_INVALID_ARG),
+    (dict(top_p=1.5), L.MMDIT_ERR_INVALID_ARG),
+    (dict(top_p=float("nan")), L.MMDIT_ERR_INVALID_ARG),
+    (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
+    (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(ws_bytes=10), L.MMDIT_ERR_WORKSPACE),
+])
+def test_block_sparse_rejects_bad_arguments(over, status):
+    a = dict(T=24, H=64, W=112, heads=24, hd=128, zone=(8, 8, 8), block=(4, 4, 4), top_k=32,
+             top_p=0.9, ws_bytes=1 << 40)
+    a.update(over)
+    sd = J.sparse_desc(a["zone"], a["block"], a["top_k"], a["top_p"])
+    lib = J.lib()
+    st = lib.mmdit_block_sparse_attn(1 << 20, 1 << 30, 1 << 31, a["T"], a["H"], a["W"], a["heads"],
+                                     a["hd"], ctypes.byref(sd), 0.088, 1 << 36, None, None,
+                                     1 << 40, a["ws_bytes"], None)
+    assert st == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        L.lib()

@@ -1,0 +1,242 @@
+"""GPU parity: every C-ABI call against the fp64 oracle, stage by stage, on the
+tensors that stage consumed.  Floating point: max-abs 1e-4 on the fp32
+workload, 2e-2 on bf16 workloads (fp32 outputs); RoPE bf16 outputs within one
+bf16 ulp of the rounded oracle; block selection bit-exact."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import joint_video_audio_rope_amd as J
+from oracle import attention as A
+from oracle import block_sparse as B
+from oracle import rope as R
+from synth import WORKLOADS, joint_inputs, n_tokens, shrink, sparse_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_BF16 = 2e-2
+TOL_FP32 = 1e-4
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def tol(w):
+    return TOL_FP32 if w["dtype"] == "fp32" else TOL_BF16
+
+
+def bf16_ulp_diff(got_bf16, ref_f64):
+    """Distance in bf16 units of the last place between got and RNE(ref)."""
+    ref = torch.from_numpy(ref_f64).to(torch.float32).to(torch.bfloat16)
+    def ordered(t):
+        b = t.contiguous().view(torch.int16).to(torch.int32)
+        mag = b & 0x7FFF
+        return torch.where(b < 0, -mag, mag)
+    return (ordered(got_bf16.cpu()) - ordered(ref)).abs().max().item()
+
+
+def sample_rows(n, count, seed, must=()):
+    rng = np.random.default_rng(seed)
+    rows = set(int(r) for r in must if 0 <= r < n)
+    rows.update(int(r) for r in rng.choice(n, size=min(n, count), replace=False))
+    return np.array(sorted(rows))
+
+
+def rotated(w):
+    """Inputs of a workload with Q and K rotated on the GPU (and the originals)."""
+    x = joint_inputs(w, DEV)
+    q, k = x["q"].clone(), x["k"].clone()
+    J.mmdit_rope3d(J.rope_spec_for(w), q, k)
+    torch.cuda.synchronize()
+    return x, q, k
+
+
+# ---- RoPE ----------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "block", "480p", "720p"])
+def test_rope_parity(name):
+    w = WORKLOADS[name]
+    x, q, k = rotated(w)
+    pos, rot = R.token_positions(w)
+    n = n_tokens(w)
+    rows = np.arange(n) if name != "720p" else sample_rows(n, 6000, 1, must=[0, n - 1, 75599, 75600, 75817, 75818])
+    for src, got in ((x["q"], q), (x["k"], k)):
+        ref = R.apply_rope(f64(src[rows]), pos[rows], rot[rows], w["split"], w["theta"])
+        g = got[rows]
+        if w["dtype"] == "fp32":
+            assert np.max(np.abs(f64(g) - ref)) <= TOL_FP32
+        else:
+            assert bf16_ulp_diff(g, ref) <= 1
+        # text tokens are neither rotated nor touched
+        text = ~rot[rows]
+        if text.any():
+            assert torch.equal(g[torch.from_numpy(text).to(DEV)], src[rows][torch.from_numpy(text).to(DEV)])
+
+
+# ---- joint self-attention ---------------------------------------------------------
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("block", None), ("480p", 384), ("720p", 256)])
+def test_joint_attn_parity(name, rows):
+    w = WORKLOADS[name]
+    x, q, k = rotated(w)
+    v = x["v"]
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    n = n_tokens(w)
+    if rows is None:
+        r = np.arange(n)
+    else:
+        must = [0, 1, n - 1, n - 2, 127, 128, n // 2]
+        if x["outliers"].numel():
+            must += x["outliers"][:rows // 2].tolist()
+        r = sample_rows(n, rows, 2, must=must)
+    ref = A.attention(f64(q), f64(k), f64(v), rows=r)
+    err = np.max(np.abs(f64(o)[r] - ref))
+    assert err <= tol(w), err
+
+
+def test_video_to_text_parity():
+    w = WORKLOADS["480p"]
+    x = joint_inputs(w, DEV)
+    seg = A.joint_segments(w)
+    v0, v1 = seg["video_stream"]
+    t0, t1 = seg["text"]
+    qv = x["q"][v0:v1].contiguous()
+    kt, vt = x["k"][t0:t1].contiguous(), x["v"][t0:t1].contiguous()
+    o = J.mmdit_joint_attn(qv, kt, vt)
+    torch.cuda.synchronize()
+    r = sample_rows(v1 - v0, 512, 3, must=[0, v1 - v0 - 1])
+    ref = A.attention(f64(qv), f64(kt), f64(vt), rows=r)
+    assert np.max(np.abs(f64(o)[r] - ref)) <= TOL_BF16
+
+
+# ---- audio <-> video cross-attention ---------------------------------------------------
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("block", None), ("480p", 512), ("720p", 384)])
+def test_av_cross_attn_parity(name, rows):
+    w = WORKLOADS[name]
+    x, q, k = rotated(w)
+    v = x["v"]
+    seg = A.joint_segments(w)
+    v0, v1 = seg["video_stream"]
+    a0, a1 = seg["audio"]
+    parts = [t[s0:s1].contiguous() for t in (q, k, v) for (s0, s1) in ((v0, v1), (a0, a1))]
+    qv, qa, kv, ka, vv, va = parts
+    o_v, o_a = J.mmdit_av_cross_attn(qv, kv, vv, qa, ka, va)
+    torch.cuda.synchronize()
+    nv = v1 - v0
+    r = np.arange(nv) if rows is None else sample_rows(nv, rows, 4, must=[0, nv - 1])
+    ref_v = A.attention(f64(qv), f64(ka), f64(va), rows=r)
+    ref_a = A.attention(f64(qa), f64(kv), f64(vv))
+    assert np.max(np.abs(f64(o_v)[r] - ref_v)) <= tol(w)
+    assert np.max(np.abs(f64(o_a) - ref_a)) <= tol(w)
+
+
+# ---- edge cases of the dense kernel ---------------------------------------------------
+def _rand(shape, seed, dtype=torch.bfloat16, scale=1.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * scale).to(dtype)
+
+
+@pytest.mark.parametrize("nq,nkv,h,d", [(1000, 333, 3, 128), (77, 5000, 2, 128), (130, 65, 5, 64),
+                                        (1, 1, 1, 128), (300, 64, 2, 64), (129, 4097, 1, 128)])
+def test_ragged_and_split_shapes(nq, nkv, h, d):
+    q, k, v = _rand((nq, h, d), 10), _rand((nkv, h, d), 11), _rand((nkv, h, d), 12)
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    ref = A.attention(f64(q), f64(k), f64(v))
+    assert np.max(np.abs(f64(o) - ref)) <= TOL_BF16
+
+
+def test_single_key_and_empty_queries():
+    q, k, v = _rand((200, 2, 128), 13), _rand((1, 2, 128), 14), _rand((1, 2, 128), 15)
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f64(o) - f64(v)[0][None])) <= 1e-3
+    e = J.mmdit_joint_attn(q[:0], k, v)
+    assert e.shape == (0, 2, 128)
+
+
+def test_large_logits_softmax_range():
+    q, k, v = _rand((500, 2, 128), 16, scale=6.0), _rand((700, 2, 128), 17, scale=6.0), _rand((700, 2, 128), 18)
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    assert np.max(np.abs(f64(o) - A.attention(f64(q), f64(k), f64(v)))) <= TOL_BF16
+
+
+def test_repeat_is_bitwise_identical():
+    w = WORKLOADS["block"]
+    x = joint_inputs(w, DEV)
+    a = J.mmdit_joint_attn(x["q"], x["k"], x["v"])
+    b = J.mmdit_joint_attn(x["q"], x["k"], x["v"])
+    c1, c2 = J.mmdit_av_cross_attn(x["q"][:5376].contiguous(), x["k"][:5376].contiguous(),
+                                   x["v"][:5376].contiguous(), x["q"][5376:5594].contiguous(),
+                                   x["k"][5376:5594].contiguous(), x["v"][5376:5594].contiguous())
+    d1, d2 = J.mmdit_av_cross_attn(x["q"][:5376].contiguous(), x["k"][:5376].contiguous(),
+                                   x["v"][:5376].contiguous(), x["q"][5376:5594].contiguous(),
+                                   x["k"][5376:5594].contiguous(), x["v"][5376:5594].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c1, d1) and torch.equal(c2, d2)
+
+
+# ---- block-sparse ---------------------------------------------------------------------
+def _sparse_check(w, k_sel, p_sel, n_qblocks=None, seed=5):
+    x = sparse_inputs(w, DEV)
+    T, H, W = w["T"], w["H"], w["W"]
+    o, mask, cnt = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], T, H, W, w["zone"], w["block"],
+                                             k_sel, p_sel)
+    torch.cuda.synchronize()
+    idx = B.block_token_index(T, H, W, w["zone"], w["block"])
+    q64, k64 = f64(x["q"]), f64(x["k"])
+    P = B.block_probs(B.block_means(q64, idx), B.block_means(k64, idx))
+    m_ref, c_ref, margin = B.select_blocks(P, k_sel, p_sel)
+    assert margin["cumsum"] > 1e-12 and margin["rel_gap"] > 1e-12, margin
+    got_mask = mask.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got_mask, B.pack_mask(m_ref))
+    assert np.array_equal(cnt.cpu().numpy(), c_ref)
+    nb = idx.shape[0]
+    h = w["heads"]
+    out = f64(o)
+    v64 = f64(x["v"])
+    worst = 0.0
+    for hd in range(h):
+        if n_qblocks is None:
+            qbs = range(nb)
+        else:
+            qbs = sample_rows(nb, n_qblocks, seed + hd,
+                              must=[int(np.argmax(c_ref[hd])), int(np.argmin(c_ref[hd]))])
+        ref = B.block_sparse_attention(q64, k64, v64, idx, m_ref, query_blocks=qbs, heads=[hd])
+        for (hh, i), r in ref.items():
+            worst = max(worst, float(np.max(np.abs(out[idx[i], hh] - r))))
+    assert worst <= TOL_BF16, worst
+    return c_ref
+
+
+@pytest.mark.parametrize("k_sel,p_sel", [(4, 0.6), (0, 0.9), (2, 0.0), (64, 0.9), (1, 1.0)])
+def test_block_sparse_small_grid(k_sel, p_sel):
+    w = shrink("sparse2k", T=8, H=16, W=32, heads=4)
+    _sparse_check(w, k_sel, p_sel)
+
+
+def test_block_sparse_non_power_of_two_blocks():
+    w = shrink("sparse2k", T=8, H=8, W=24, heads=2, seed=9)
+    _sparse_check(w, 3, 0.7)
+
+
+def test_block_sparse_all_blocks_equals_dense():
+    w = shrink("sparse2k", T=8, H=16, W=32, heads=4, seed=6)
+    x = sparse_inputs(w, DEV)
+    o, _, cnt = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], 8, 16, 32, top_k=64, top_p=0.5)
+    d = J.mmdit_joint_attn(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    assert int(cnt.min()) == 64
+    assert (o - d).abs().max().item() <= TOL_BF16
+
+
+def test_block_sparse_full_size():
+    w = WORKLOADS["sparse2k"]
+    c = _sparse_check(w, w["top_k"], w["top_p"], n_qblocks=12)
+    dens = c.mean() / c.shape[1]
+    assert 0.05 < dens < 0.9
