@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse leg")
     ap.add_argument("--sparse-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the oracle sample (all heads, all keys)")
     return ap.parse_args()
 

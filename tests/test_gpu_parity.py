@@ -1,7 +1,7 @@
 """GPU parity: every C-ABI call against the fp64 oracle, stage by stage, on the
 tensors that stage consumed.  Floating point: max-abs 1e-4 on the fp32
-workload, 2e-2 on bf16 workloads (fp32 outputs); RoPE bf16 outputs within one
-bf16 ulp of the rounded oracle; block selection bit-exact."""
+workload, 2e-2 on bf16 workloads (fp32 outputs); RoPE bf16 outputs within the
+fp32 arithmetic error plus half a bf16 ulp; block selection bit-exact."""
 import math
 
 import numpy as np
@@ -26,6 +26,23 @@ def f64(t):
 
 def tol(w):
     return TOL_FP32 if w["dtype"] == "fp32" else TOL_BF16
+
+
+def rope_bf16_bound(src_f64, ref_f64):
+    """Largest |got - ref| a correct fp32 rotation rounded to bf16 can show.
+
+    fp32 table entries are within 2^-25 of cos and sin; the two products and
+    the sum add at most 2^-23 (|x0| + |x1|); so the fp32 result is within
+    e = 2^-22 (|x0| + |x1|) of the exact rotation, and rounding it to bf16
+    adds half a bf16 ulp at magnitude |ref| + e.  (One bf16 ulp of the
+    result alone is not a valid gate: where x0 cos - x1 sin cancels, the fp32
+    error of the terms is many ulps of the tiny result.)
+    """
+    pair = np.abs(src_f64[..., 0::2]) + np.abs(src_f64[..., 1::2])
+    e = np.repeat(pair, 2, axis=-1) * 2.0 ** -22
+    mag = np.abs(ref_f64) + e
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 0.0)
+    return 0.5 * ulp + e
 
 
 def bf16_ulp_diff(got_bf16, ref_f64):
@@ -68,7 +85,9 @@ def test_rope_parity(name):
         if w["dtype"] == "fp32":
             assert np.max(np.abs(f64(g) - ref)) <= TOL_FP32
         else:
-            assert bf16_ulp_diff(g, ref) <= 1
+            bound = rope_bf16_bound(f64(src[rows]), ref)
+            excess = np.abs(f64(g) - ref) - bound
+            assert np.max(excess) <= 0.0, (np.max(excess), bf16_ulp_diff(g, ref))
         # text tokens are neither rotated nor touched
         text = ~rot[rows]
         if text.any():
