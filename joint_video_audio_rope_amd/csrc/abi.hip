@@ -87,7 +87,8 @@ mmdit_status check_attn_args(const void* q, int64_t n_q, const void* k, const vo
     if (heads < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: heads %d < 1", who, heads);
     if (n_q < 0) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_q %lld < 0", who, (long long)n_q);
     if (n_kv < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_kv %lld < 1", who, (long long)n_kv);
-    if (!std::isfinite(scale)) return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale not finite", who);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
     const int64_t lim = (int64_t)1 << 31;
     if (n_q * heads >= lim || n_kv * heads >= lim)
         return fail(MMDIT_ERR_UNSUPPORTED, "%s: tokens * heads must stay below 2^31", who);
@@ -237,7 +238,7 @@ mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
 // ---- block sparse plan ------------------------------------------------------------
 struct SparsePlan {
     SparseGeom g{};
-    size_t off_qbar, off_kbar, off_scores, off_list, off_count, off_base, off_vt, total;
+    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, total;
 };
 
 mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_sparse_desc* sp,
@@ -260,6 +261,10 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     const int64_t n = (int64_t)T * H * W;
     if (n * heads >= ((int64_t)1 << 31))
         return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: tokens * heads must stay below 2^31");
+    // the sparse kernel addresses a key block's rows with 32-bit byte offsets
+    const int64_t span = ((int64_t)(sp->block[0] - 1) * H + sp->block[1]) * W;
+    if (span * heads * hd * 2 >= ((int64_t)1 << 32))
+        return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: a block spans 4 GiB or more of the K rows");
     const int64_t nb = n / kTileN;
     if (nb > 4096) return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: %lld blocks (max 4096)", (long long)nb);
     SparseGeom& g = p->g;
@@ -279,7 +284,7 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     p->off_qbar = take((size_t)heads * nb * hd * 8);
     p->off_kbar = take((size_t)heads * nb * hd * 8);
     p->off_scores = take((size_t)heads * nb * nb * 8);
-    p->off_list = take((size_t)heads * nb * nb * 2);
+    p->off_mask = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
     p->off_count = take((size_t)heads * nb * 4);
     p->off_base = take((size_t)nb * 4);
     p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
@@ -358,7 +363,7 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
         size_t t = 0;
         t += align256((size_t)heads * nb * head_dim * 8) * 2;
         t += align256((size_t)heads * nb * nb * 8);
-        t += align256((size_t)heads * nb * nb * 2);
+        t += align256((size_t)heads * nb * ((nb + 31) / 32) * 4);
         t += align256((size_t)heads * nb * 4);
         t += align256((size_t)nb * 4);
         t += align256((size_t)heads * nb * head_dim * kTileN * 2);
@@ -441,8 +446,8 @@ mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v
     SparsePlan p{};
     mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
     if (st != MMDIT_OK) return st;
-    if (!std::isfinite(softmax_scale))
-        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: softmax_scale not finite");
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: softmax_scale must be positive and finite");
     if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: null q, k, v or o");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: q, k, v, o must be 16-byte aligned");
@@ -458,7 +463,7 @@ mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v
     sw.qbar = (double*)(w + p.off_qbar);
     sw.kbar = (double*)(w + p.off_kbar);
     sw.scores = (double*)(w + p.off_scores);
-    sw.list = (uint16_t*)(w + p.off_list);
+    sw.mask = (uint32_t*)(w + p.off_mask);
     sw.count = (int32_t*)(w + p.off_count);
     sw.base = (int32_t*)(w + p.off_base);
     sw.vt = (_Float16*)(w + p.off_vt);

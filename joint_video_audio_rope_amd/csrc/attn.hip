@@ -50,15 +50,13 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
 }
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     using L = TileLayout<HD>;
-    constexpr int NT = 256;
+    constexpr int NW = 4;
     constexpr int KS = HD / 16;
-    constexpr int DB = HD / 32;
-    constexpr int KCH = kTileN * L::kKChunks / NT;   // K chunks per thread
-    constexpr int VCH = HD * 8 / NT;                 // V^T chunks per thread
-    __shared__ __attribute__((aligned(16))) char lk[L::kKBytes];
-    __shared__ __attribute__((aligned(16))) char lv[L::kVBytes];
+    constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);   // K copies per wave per tile
+    constexpr int VCH = HD * 8 / (kWave * NW);                 // V^T copies per wave per tile
+    __shared__ __attribute__((aligned(16))) char lds[2 * L::kBytes];
 
     const int total = a.q_tiles * a.heads * a.splits;
     const int per_xcd = (total + 7) >> 3;
@@ -71,96 +69,87 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     const int tile0 = split * a.tiles_per_split;
     const int tile1 = min(a.kv_tiles, tile0 + a.tiles_per_split);
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    const int w = wave_id();
+    const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
     const int m = lane & 31;
     const int64_t rstride = (int64_t)a.heads * HD;
+    const int64_t krb = rstride * 2;                            // bytes per key row
 
-    const int64_t qrow = (int64_t)qt * 128 + wave * 32 + m;
+    const int64_t qrow = (int64_t)qt * 128 + w * 32 + m;
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
         qf[ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
 
+    // Each lane's share of the tile copies, fixed for the whole key walk: the
+    // byte offset (from the tile's first key row) of the 16-byte chunk that
+    // belongs at its LDS position.
+    int krow[KCH];
+    uint32_t koff[KCH];
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+        int row, c;
+        L::k_at((w * KCH + i) * kWave + lane, row, c);
+        krow[i] = (row & ~31) | perm_row(row & 31);
+        koff[i] = (uint32_t)(krow[i] * krb + c * 16);
+    }
+    uint32_t voff[VCH];
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+        int d, c;
+        L::v_at((w * VCH + i) * kWave + lane, d, c);
+        voff[i] = (uint32_t)((d * a.n_pad + c * 8) * 2);
+    }
+    const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
+    const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)head * HD * a.n_pad);
+
+    auto issue = [&](int t, char* lb) {
+        const int64_t kv0 = (int64_t)t * kTileN;
+        const char* kt = kg + kv0 * krb;
+        if (kv0 + kTileN <= a.n_kv) {
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) dma16(kt + koff[i], lb + (w * KCH + i) * 1024);
+        } else {   // rows past n_kv re-read the last real row; their scores are masked
+            const int last = (int)(a.n_kv - kv0) - 1;
+#pragma unroll
+            for (int i = 0; i < KCH; ++i)
+                dma16(kt + (koff[i] - (uint32_t)((krow[i] - min(krow[i], last)) * krb)),
+                      lb + (w * KCH + i) * 1024);
+        }
+        const char* vt = vg + kv0 * 2;
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + L::kKBytes + (w * VCH + i) * 1024);
+    };
+
     SoftmaxState<HD> st;
     st.init();
-
-    uint4 kreg[KCH], vreg[VCH];
-    auto gload = [&](int t) {
-        const int64_t kv0 = (int64_t)t * kTileN;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int u = tid + i * NT;
-            const int row = u / L::kKChunks, c = u % L::kKChunks;
-            const int64_t key = kv0 + ((row & ~31) | perm_row(row & 31));
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            if (key < a.n_kv)
-                kreg[i] = *reinterpret_cast<const uint4*>(a.k + key * rstride + head * HD + c * 8);
-        }
-        const _Float16* vb = a.vt + (int64_t)head * HD * a.n_pad + kv0;
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + i * NT;
-            const int d = u >> 3, c = u & 7;
-            vreg[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)d * a.n_pad + c * 8);
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int u = tid + i * NT;
-            const int row = u / L::kKChunks, c = u % L::kKChunks;
-            *reinterpret_cast<uint4*>(lk + L::k_off(row, c)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + i * NT;
-            const int d = u >> 3, c = u & 7;
-            *reinterpret_cast<uint4*>(lv + L::v_off(d, c)) = vreg[i];
-        }
-    };
-
-    gload(tile0);
-    for (int t = tile0; t < tile1; ++t) {
+    // full tiles in the loop; a partial last tile (keys past n_kv masked) after it
+    const int64_t last_valid = a.n_kv - (int64_t)(tile1 - 1) * kTileN;
+    const int tfull = last_valid < kTileN ? tile1 - 1 : tile1;
+    issue(tile0, lds);
+    int t = tile0;
+    for (; t < tfull; ++t) {
+        char* cur = lds + ((t - tile0) & 1) * L::kBytes;
+        wait_dma();
+        __syncthreads();                       // tile t landed; every wave is done with tile t-1
+        if (t + 1 < tile1) issue(t + 1, lds + ((t + 1 - tile0) & 1) * L::kBytes);
+        attn_tile<HD, false>(cur, cur + L::kKBytes, qf, st, a.scale_log2, kTileN);
+    }
+    if (t < tile1) {
+        char* cur = lds + ((t - tile0) & 1) * L::kBytes;
+        wait_dma();
         __syncthreads();
-        lstore();
-        __syncthreads();
-        if (t + 1 < tile1) gload(t + 1);
-        const int64_t valid = a.n_kv - (int64_t)t * kTileN;
-        if (valid < kTileN)
-            attn_tile<HD, true>(lk, lv, qf, st, a.scale_log2, (int)valid);
-        else
-            attn_tile<HD, false>(lk, lv, qf, st, a.scale_log2, kTileN);
+        attn_tile<HD, true>(cur, cur + L::kKBytes, qf, st, a.scale_log2, (int)last_valid);
     }
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (qrow >= a.n_q) return;
     if (a.splits == 1) {
-        const float inv = 1.f / l_tot;
-        float* orow = a.o + qrow * rstride + head * HD;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hh;
-                *reinterpret_cast<float4*>(orow + d0) =
-                    make_float4(st.o[db][4 * g] * inv, st.o[db][4 * g + 1] * inv,
-                                st.o[db][4 * g + 2] * inv, st.o[db][4 * g + 3] * inv);
-            }
+        store_o<HD>(a.o + qrow * rstride + head * HD, st, 1.f / l_tot);
     } else {
         const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
-        float* orow = a.part_o + prow * HD;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hh;
-                *reinterpret_cast<float4*>(orow + d0) =
-                    make_float4(st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
-                                st.o[db][4 * g + 3]);
-            }
+        store_o<HD>(a.part_o + prow * HD, st, 1.f);
         if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m_run, l_tot);
     }
 }

@@ -83,7 +83,7 @@ struct SparseWs {
     double* qbar;       // [heads][nb][hd]
     double* kbar;       // [heads][nb][hd]
     double* scores;     // [heads][nb][nb] (logits, scaled)
-    uint16_t* list;     // [heads][nb][nb] selected key blocks, ascending
+    uint32_t* mask;     // [heads][nb][ceil(nb/32)] selected key blocks, bit j of word j/32
     int32_t* count;     // [heads][nb]
     int32_t* base;      // [nb] raster token index of each block's first token
     _Float16* vt;       // [heads][nb][hd][64]

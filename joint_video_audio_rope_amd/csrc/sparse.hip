@@ -11,7 +11,7 @@
 //   block_select   per (head, query block): fp64 softmax, sort by probability
 //                  (ties to the lower block id), fp64 running sum, keep the
 //                  longer of the top-k and top-p prefixes; emits the bitmask,
-//                  the count and an ascending list of selected blocks.
+//                  the count and the selection bitmask.
 //   sparse_attn    attention of each query block over its selected key blocks
 //                  with the same online-softmax tile loop as the dense kernel.
 // Selection runs in fp64 throughout: on smooth-field inputs the probability
@@ -194,7 +194,6 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(SparseGeom g,
     __shared__ double red[kSelThreads / 64];
     __shared__ double wsum[kSelThreads];
     __shared__ uint32_t words[kSelMax / 32];
-    __shared__ int wpos[kSelMax / 32 + 1];
     __shared__ int first_hit;
 
     const int nb = g.nb;
@@ -282,126 +281,124 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(SparseGeom g,
     const int nw = (nb + 31) >> 5;
     if (tid == 0) {
         int acc = 0;
-        for (int wd = 0; wd < nw; ++wd) {
-            wpos[wd] = acc;
-            acc += __popc(words[wd]);
-        }
-        wpos[nw] = acc;
+        for (int wd = 0; wd < nw; ++wd) acc += __popc(words[wd]);
         w.count[row] = acc;
         if (sel_count) sel_count[row] = acc;
     }
-    __syncthreads();
-    uint16_t* lst = w.list + (int64_t)row * nb;
     for (int wd = tid; wd < nw; wd += kSelThreads) {
-        uint32_t bits = words[wd];
-        if (sel_mask) sel_mask[(int64_t)row * nw + wd] = bits;
-        int pos = wpos[wd];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            lst[pos++] = (uint16_t)(wd * 32 + b);
-            bits &= bits - 1;
-        }
+        w.mask[(int64_t)row * nw + wd] = words[wd];
+        if (sel_mask) sel_mask[(int64_t)row * nw + wd] = words[wd];
     }
 }
 
-// Sparse attention: 2 waves (64 queries = one block) per workgroup.
+// Sparse attention.  A workgroup of 4 waves serves two query blocks of one
+// head, 2p and 2p + 1 (neighbours along w inside a zone, whose selections
+// mostly coincide): waves 0-1 own block 2p, waves 2-3 block 2p + 1.  The
+// workgroup walks the union of the two selections in ascending block id,
+// staging each key block's K rows (gathered from the raster layout) and its
+// fp16 V^T block in double-buffered LDS; a wave pair computes a tile only if
+// its own block selected it.
 template <int HD>
-__global__ __launch_bounds__(128) void sparse_attn_kernel(SparseGeom g, const __bf16* __restrict__ q,
-                                                          const __bf16* __restrict__ k,
-                                                          float scale_log2, SparseWs w,
-                                                          float* __restrict__ o) {
+__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const __bf16* __restrict__ q,
+                                                             const __bf16* __restrict__ k,
+                                                             float scale_log2, SparseWs w,
+                                                             float* __restrict__ o) {
     using L = TileLayout<HD>;
-    constexpr int NT = 128;
+    constexpr int NW = 4;
     constexpr int KS = HD / 16;
-    constexpr int DB = HD / 32;
-    constexpr int KCH = kTileN * L::kKChunks / NT;
-    constexpr int VCH = HD * 8 / NT;
-    __shared__ __attribute__((aligned(16))) char lk[L::kKBytes];
-    __shared__ __attribute__((aligned(16))) char lv[L::kVBytes];
+    constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);
+    constexpr int VCH = HD * 8 / (kWave * NW);
+    __shared__ __attribute__((aligned(16))) char lds[2 * L::kBytes];
+    __shared__ uint32_t msk[2][kSelMax / 32];
 
-    const int total = g.heads * g.nb;
+    const int pairs = (g.nb + 1) >> 1;
+    const int total = g.heads * pairs;
     const int per_xcd = (total + 7) >> 3;
     const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
     if (logical >= total) return;
-    const int head = logical / g.nb;
-    const int qb = logical - head * g.nb;
+    const int head = logical / pairs;
+    const int pr = logical - head * pairs;
+    const int nw = (g.nb + 31) >> 5;
+    const bool has_b = 2 * pr + 1 < g.nb;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + 2 * pr) * nw;
+    for (int i = threadIdx.x; i < 2 * nw; i += 256) {
+        const int sd = i / nw, wd = i - (i / nw) * nw;
+        msk[sd][wd] = (sd == 0 || has_b) ? mrow[sd * nw + wd] : 0u;
+    }
+
+    const int wv = wave_id();
+    const int side = wv >> 1;
+    const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
     const int m = lane & 31;
-    const int64_t rs = (int64_t)g.heads * HD;
+    const int qb = min(2 * pr + side, g.nb - 1);
+    const int64_t rstride = (int64_t)g.heads * HD;
+    const int64_t krb = rstride * 2;
 
-    const int64_t qtok = (int64_t)w.base[qb] + block_local(g, wave * 32 + m);
+    const int64_t qtok = (int64_t)w.base[qb] + block_local(g, (wv & 1) * 32 + m);
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = load_bf16x8(q + qtok * rs + head * HD + 16 * ks + 8 * hh, true);
+        qf[ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
 
-    // per-thread local token offsets of the K rows this thread stages
-    int64_t koff[KCH];
+    uint32_t kbyte[KCH];   // < 2^32: checked on the host (block span * row bytes)
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-        const int row = (tid + i * NT) / L::kKChunks;
-        koff[i] = block_local(g, (row & ~31) | perm_row(row & 31));
+        int row, c;
+        L::k_at((wv * KCH + i) * kWave + lane, row, c);
+        kbyte[i] = (uint32_t)(block_local(g, (row & ~31) | perm_row(row & 31)) * krb + c * 16);
     }
+    uint32_t voff[VCH];
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+        int d, c;
+        L::v_at((wv * VCH + i) * kWave + lane, d, c);
+        voff[i] = (uint32_t)((d * kTileN + c * 8) * 2);
+    }
+
+    auto issue = [&](int j, char* lb) {
+        const int64_t base = w.base[j];
+        const char* kt = reinterpret_cast<const char*>(k + base * rstride + head * HD);
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) dma16(kt + kbyte[i], lb + (wv * KCH + i) * 1024);
+        const char* vt = reinterpret_cast<const char*>(w.vt + ((int64_t)head * g.nb + j) * HD * kTileN);
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + L::kKBytes + (wv * VCH + i) * 1024);
+    };
+    __syncthreads();
+
+    // cursor over the union of both selections (uniform across the workgroup)
+    int word = 0;
+    uint32_t bits = __builtin_amdgcn_readfirstlane(msk[0][0] | msk[1][0]);
+    auto advance = [&]() -> int {
+        while (bits == 0u) {
+            if (++word >= nw) return -1;
+            bits = __builtin_amdgcn_readfirstlane(msk[0][word] | msk[1][word]);
+        }
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        return word * 32 + b;
+    };
 
     SoftmaxState<HD> st;
     st.init();
-    const int cnt = w.count[logical];
-    const uint16_t* lst = w.list + (int64_t)logical * g.nb;
-
-    uint4 kreg[KCH], vreg[VCH];
-    auto gload = [&](int t) {
-        const int j = lst[t];
-        const int64_t kb = w.base[j];
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = (tid + i * NT) % L::kKChunks;
-            kreg[i] = *reinterpret_cast<const uint4*>(k + (kb + koff[i]) * rs + head * HD + c * 8);
-        }
-        const _Float16* vb = w.vt + ((int64_t)head * g.nb + j) * HD * kTileN;
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + i * NT;
-            vreg[i] = *reinterpret_cast<const uint4*>(vb + (u >> 3) * kTileN + (u & 7) * 8);
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int u = tid + i * NT;
-            *reinterpret_cast<uint4*>(lk + L::k_off(u / L::kKChunks, u % L::kKChunks)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + i * NT;
-            *reinterpret_cast<uint4*>(lv + L::v_off(u >> 3, u & 7)) = vreg[i];
-        }
-    };
-
-    if (cnt > 0) gload(0);
-    for (int t = 0; t < cnt; ++t) {
+    int jc = advance();
+    if (jc >= 0) issue(jc, lds);
+    for (int it = 0; jc >= 0; ++it) {
+        char* cur = lds + (it & 1) * L::kBytes;
+        wait_dma();
         __syncthreads();
-        lstore();
-        __syncthreads();
-        if (t + 1 < cnt) gload(t + 1);
-        attn_tile<HD, false>(lk, lv, qf, st, scale_log2, kTileN);
+        const int jn = advance();
+        if (jn >= 0) issue(jn, lds + ((it + 1) & 1) * L::kBytes);
+        if ((msk[side][jc >> 5] >> (jc & 31)) & 1u)
+            attn_tile<HD, false>(cur, cur + L::kKBytes, qf, st, scale_log2, kTileN);
+        jc = jn;
     }
 
+    if (2 * pr + side >= g.nb) return;
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    const float inv = 1.f / l_tot;
-    float* orow = o + qtok * rs + head * HD;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            const int d0 = 32 * db + 8 * gg + 4 * hh;
-            *reinterpret_cast<float4*>(orow + d0) =
-                make_float4(st.o[db][4 * gg] * inv, st.o[db][4 * gg + 1] * inv,
-                            st.o[db][4 * gg + 2] * inv, st.o[db][4 * gg + 3] * inv);
-        }
+    store_o<HD>(o + qtok * rstride + head * HD, st, 1.f / l_tot);
 }
 
 }  // namespace
@@ -440,9 +437,9 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
-    const int total = g.heads * g.nb;
+    const int total = g.heads * ((g.nb + 1) / 2);
     const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
-    hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3(blocks), dim3(128), 0, s, g, q, k, scale_log2,
+    hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3(blocks), dim3(256), 0, s, g, q, k, scale_log2,
                        w, o);
     (void)hd;
     return hipGetLastError();

@@ -92,7 +92,7 @@ def test_workspace_plans():
     assert big > 24 * 128 * 34368 * 2
     sd = J.sparse_desc()
     b = ws(J.MMDIT_OP_BLOCK_SPARSE_ATTN, 172032, 172032, 24, 128, J.MMDIT_BF16, sd)
-    assert b >= 24 * 2688 * 2688 * (8 + 2) + 24 * 2688 * 128 * 64 * 2
+    assert b >= 24 * 2688 * 2688 * 8 + 24 * 2688 * 84 * 4 + 24 * 2688 * 128 * 64 * 2
 
 
 def _call_joint(**over):
