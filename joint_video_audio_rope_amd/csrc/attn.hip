@@ -85,14 +85,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // Each lane's share of the tile copies, fixed for the whole key walk: the
     // byte offset (from the tile's first key row) of the 16-byte chunk that
     // belongs at its LDS position.
-    int krow[KCH];
+    // tile row (after the pi permutation) and chunk a lane copies in K copy i
+    auto k_slot = [&](int i, int& krow, int& c) {
+        int row;
+        L::k_at((w * KCH + i) * kWave + lane, row, c);
+        krow = (row & ~31) | perm_row(row & 31);
+    };
     uint32_t koff[KCH];
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-        int row, c;
-        L::k_at((w * KCH + i) * kWave + lane, row, c);
-        krow[i] = (row & ~31) | perm_row(row & 31);
-        koff[i] = (uint32_t)(krow[i] * krb + c * 16);
+        int krow, c;
+        k_slot(i, krow, c);
+        koff[i] = (uint32_t)(krow * krb + c * 16);
     }
     uint32_t voff[VCH];
 #pragma unroll
@@ -104,7 +108,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
     const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)head * HD * a.n_pad);
 
-    auto issue = [&](int t, char* lb) {
+    // LDS: two K tiles and two V^T tiles.  The K ring runs one tile ahead of
+    // the V ring: step t reads K(t+1) and V(t) while K(t+2) and V(t+1) land.
+    auto kbuf = [&](int b) { return lds + b * L::kKBytes; };
+    auto vbuf = [&](int b) { return lds + 2 * L::kKBytes + b * L::kVBytes; };
+    auto issue_k = [&](int t, char* lb) {
         const int64_t kv0 = (int64_t)t * kTileN;
         const char* kt = kg + kv0 * krb;
         if (kv0 + kTileN <= a.n_kv) {
@@ -113,35 +121,75 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         } else {   // rows past n_kv re-read the last real row; their scores are masked
             const int last = (int)(a.n_kv - kv0) - 1;
 #pragma unroll
-            for (int i = 0; i < KCH; ++i)
-                dma16(kt + (koff[i] - (uint32_t)((krow[i] - min(krow[i], last)) * krb)),
-                      lb + (w * KCH + i) * 1024);
+            for (int i = 0; i < KCH; ++i) {
+                int krow, c;
+                k_slot(i, krow, c);
+                dma16(kt + (int64_t)min(krow, last) * krb + c * 16, lb + (w * KCH + i) * 1024);
+            }
         }
-        const char* vt = vg + kv0 * 2;
+    };
+    auto issue_v = [&](int t, char* lb) {
+        const char* vt = vg + (int64_t)t * kTileN * 2;
 #pragma unroll
-        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + L::kKBytes + (w * VCH + i) * 1024);
+        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + (w * VCH + i) * 1024);
     };
 
+    FragAddr<HD> fa;
+    fa.init();
     SoftmaxState<HD> st;
     st.init();
-    // full tiles in the loop; a partial last tile (keys past n_kv masked) after it
-    const int64_t last_valid = a.n_kv - (int64_t)(tile1 - 1) * kTileN;
-    const int tfull = last_valid < kTileN ? tile1 - 1 : tile1;
-    issue(tile0, lds);
-    int t = tile0;
-    for (; t < tfull; ++t) {
-        char* cur = lds + ((t - tile0) & 1) * L::kBytes;
-        wait_dma();
-        __syncthreads();                       // tile t landed; every wave is done with tile t-1
-        if (t + 1 < tile1) issue(t + 1, lds + ((t + 1 - tile0) & 1) * L::kBytes);
-        attn_tile<HD, false>(cur, cur + L::kKBytes, qf, st, a.scale_log2, kTileN);
-    }
-    if (t < tile1) {
-        char* cur = lds + ((t - tile0) & 1) * L::kBytes;
+    const int last_valid = (int)(a.n_kv - (int64_t)(tile1 - 1) * kTileN);   // 1..64
+    const bool last_partial = last_valid < kTileN;
+
+    issue_k(tile0, kbuf(0));
+    issue_v(tile0, vbuf(0));
+    if (tile0 + 1 < tile1) issue_k(tile0 + 1, kbuf(1));
+    wait_dma();
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    qk_tile<HD>(kbuf(0), fa, qf, sa);
+    float mx = (last_partial && tile0 + 1 == tile1) ? tile_max<true>(sa, a.scale_log2, last_valid)
+                                                    : tile_max<false>(sa, a.scale_log2, kTileN);
+
+    // Top of step t: K(t+1) and V(t) are published; every wave is done with
+    // K(t) and V(t-1), whose buffers receive K(t+2) and V(t+1).
+    auto top = [&](int t) {
+        const int b = (t - tile0) & 1;
         wait_dma();
         __syncthreads();
-        attn_tile<HD, true>(cur, cur + L::kKBytes, qf, st, a.scale_log2, (int)last_valid);
+        if (t + 2 < tile1) issue_k(t + 2, kbuf(b));
+        if (t + 1 < tile1) issue_v(t + 1, vbuf(b ^ 1));
+        maybe_rescale<HD>(st, mx);
+    };
+    // steps whose next tile is full
+    const int main_end = tile1 - 1 - (last_partial ? 1 : 0);
+    int t = tile0;
+    for (; t + 1 < main_end; t += 2) {
+        top(t);
+        mx = tile_step<HD, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                        st, a.scale_log2, kTileN);
+        top(t + 1);
+        mx = tile_step<HD, true, false>(kbuf((t + 2 - tile0) & 1), vbuf((t + 1 - tile0) & 1), fa, qf, sb,
+                                        sa, st, a.scale_log2, kTileN);
     }
+    if (t < main_end) {
+        top(t);
+        mx = tile_step<HD, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                        st, a.scale_log2, kTileN);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        ++t;
+    }
+    if (t + 1 < tile1) {   // the next tile is the partial last one
+        top(t);
+        mx = tile_step<HD, true, true>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                       st, a.scale_log2, last_valid);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        ++t;
+    }
+    top(t);
+    tile_step<HD, false, false>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN);
 
     const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
     if (qrow >= a.n_q) return;

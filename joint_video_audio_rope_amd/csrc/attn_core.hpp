@@ -24,8 +24,8 @@
 // fp16, and the O accumulators are touched by vector ALU instructions only on
 // those rare tiles instead of every tile.
 //
-// LDS layouts use an XOR swizzle on 16-byte chunks (chunk ^ (row & 7)) so the
-// 8 lanes that read one chunk column at a time hit 8 different bank groups.
+// LDS layouts XOR-swizzle the 16-byte chunks of each row so the 16 lanes
+// that read one chunk column at a time hit 16 different bank groups.
 // Tiles are copied global -> LDS with global_load_lds_dwordx4 (no register
 // staging): one instruction moves 64 lanes x 16 bytes into 1 KiB of LDS, lane
 // i landing at byte 16 i; each lane therefore fetches the global chunk that
@@ -55,20 +55,31 @@ struct TileLayout {
     static constexpr int kVRowBytes = kTileN * 2;      // fp16 row of V^T (64 keys)
     static constexpr int kVBytes = HD * kTileN * 2;
     static constexpr int kBytes = kKBytes + kVBytes;   // one K + V^T tile
+    // XOR applied to the chunk index of a row.  gfx950 LDS serves a 16-byte
+    // read of 16 consecutive lanes per cycle (256 B): those 16 lanes read one
+    // chunk column of 16 consecutive rows and must land in 16 different
+    // 16-byte slots of a 256-byte line.  256-byte rows: XOR with row & 15.
+    // 128-byte rows (two per line, the line half given by row & 1): XOR with
+    // (row ^ ((row & 31) >> 3)) & 7, which is distinct over 16 aligned rows
+    // together with row & 1 and over any 8 aligned rows by itself, and repeats
+    // every 32 rows (so 32-row blocks differ by a constant byte offset).
+    __device__ static int swz(int row, int chunks) {
+        return chunks >= 16 ? (row & 15) : ((row ^ ((row & 31) >> 3)) & 7);
+    }
     __device__ static int k_off(int row, int chunk) {
-        return row * kKRowBytes + ((chunk ^ (row & 7)) << 4);
+        return row * kKRowBytes + ((chunk ^ swz(row, kKChunks)) << 4);
     }
     __device__ static int v_off(int d, int chunk) {
-        return d * kVRowBytes + ((chunk ^ (d & 7)) << 4);
+        return d * kVRowBytes + ((chunk ^ swz(d, 8)) << 4);
     }
     // Inverse maps: which (row, chunk) lives at LDS chunk index L.
     __device__ static void k_at(int L, int& row, int& chunk) {
         row = L / kKChunks;
-        chunk = (L % kKChunks) ^ (row & 7);
+        chunk = (L % kKChunks) ^ swz(row, kKChunks);
     }
     __device__ static void v_at(int L, int& d, int& chunk) {
         d = L >> 3;
-        chunk = (L & 7) ^ (d & 7);
+        chunk = (L & 7) ^ swz(d, 8);
     }
 };
 
@@ -88,33 +99,66 @@ struct SoftmaxState {
     }
 };
 
-// One 64-key tile.  `valid` keys (<= 64) of the tile are real; with MASK the
-// rest are masked out.  qf: the wave's Q fragments (B operand), one per 16-d
-// step.  scale_log2 = softmax scale * log2(e) > 0.
-template <int HD, bool MASK>
-__device__ __forceinline__ void attn_tile(const char* __restrict__ lk, const char* __restrict__ lv,
-                                          const bf16x8 (&qf)[HD / 16], SoftmaxState<HD>& st,
-                                          float scale_log2, int valid) {
-    using L = TileLayout<HD>;
-    constexpr int KS = HD / 16;
-    constexpr int DB = HD / 32;
-    const int lane = threadIdx.x & 63;
-    const int hh = lane >> 5;
-    const int m = lane & 31;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-    f32x16 s[2];
+// Per-lane LDS byte offsets of the 16 K fragments (i = 2 ks + kb) and the 16
+// V^T fragments (i = 4 db + g) of a tile, relative to the tile's K / V^T base.
+template <int HD>
+struct FragAddr {
+    int k[HD / 16];   // K fragment of step ks for rows 0..31; rows 32..63 add 32 rows
+    int v[4];         // V^T fragment of key group g for d rows 0..31; block db adds 32 db rows
+    __device__ void init() {
+        using L = TileLayout<HD>;
+        const int lane = threadIdx.x & 63;
+        const int hh = lane >> 5, m = lane & 31;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int ks = 0; ks < HD / 16; ++ks) k[ks] = L::k_off(m, 2 * ks + hh);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) v[g] = L::v_off(m, 2 * g + hh);
+    }
+};
+
+// K fragment i = 2 ks + kb (the swizzle repeats every 16 rows, so rows
+// 32..63 sit 32 rows further on).
+template <int HD>
+__device__ __forceinline__ bf16x8 k_frag(const char* lk, const FragAddr<HD>& fa, int i) {
+    return *reinterpret_cast<const bf16x8*>(lk + fa.k[i >> 1] + (i & 1) * 32 * TileLayout<HD>::kKRowBytes);
+}
+
+// V^T fragment i = 4 db + g (the swizzle repeats every 32 rows).
+template <int HD>
+__device__ __forceinline__ f16x8 v_frag(const char* lv, const FragAddr<HD>& fa, int i) {
+    return *reinterpret_cast<const f16x8*>(lv + fa.v[i & 3] + (i >> 2) * 32 * TileLayout<HD>::kVRowBytes);
+}
+
+// Scores S^T = K Q^T of one tile (not overlapped; the first tile of a walk).
+template <int HD>
+__device__ __forceinline__ void qk_tile(const char* lk, const FragAddr<HD>& fa,
+                                        const bf16x8 (&qf)[HD / 16], f32x16 (&s)[2]) {
+    constexpr int NF = HD / 8;   // fragments per tile: 2 blocks x HD/16 steps
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(lk + L::k_off(32 * kb + m, 2 * ks + hh));
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-        }
-    }
+    for (int i = 0; i < NF; ++i)
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lk, fa, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+}
 
+// Maximum of x over lanes l and l ^ 32 (the two halves of one query's keys).
+// v_permlane32_swap with the same register as both operands returns the
+// lower half's values in every lane (first result) and the upper half's in
+// every lane (second result).
+__device__ __forceinline__ float pair_max(float x) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Scaled (log2-domain) maximum of a score tile over both halves of the
+// lane pair; with MASK, keys >= valid are set to -inf first.
+template <bool MASK>
+__device__ __forceinline__ float tile_max(f32x16 (&s)[2], float scale_log2, int valid) {
+    const int hh = (threadIdx.x & 63) >> 5;
     if (MASK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -127,39 +171,95 @@ __device__ __forceinline__ void attn_tile(const char* __restrict__ lk, const cha
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    return pair_max(mx) * scale_log2;
+}
 
+// Move the reference max when a tile's max exceeds it by more than 2^8
+// (wave-uniform branch, rare after the first tiles).
+template <int HD>
+__device__ __forceinline__ void maybe_rescale(SoftmaxState<HD>& st, float mx) {
     if (__any(mx > st.m_run + 8.f)) {
         const float m_new = fmaxf(st.m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
         st.m_run = m_new;
         st.l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     }
+}
+
+// One pipelined step for the wave's 32 queries.
+//   phase 1: P(t) = exp2(S(t) * scale - m) into fp16, interleaved with the
+//            16 MFMAs of S(t+1) = K(t+1) Q^T (when NEXT);
+//   phase 2: O^T += V(t)^T P(t)^T (16 MFMAs), interleaved with the row sum of
+//            P(t) (fp16 pairs through v_dot2, i.e. exactly the values the
+//            MFMA consumes) and, when NEXT, the maximum of S(t+1).
+// Returns the scaled maximum of S(t+1) (unused when !NEXT).
+template <int HD, bool NEXT, bool MASK_NEXT>
+__device__ __forceinline__ float tile_step(const char* __restrict__ lk_next,
+                                           const char* __restrict__ lv_cur, const FragAddr<HD>& fa,
+                                           const bf16x8 (&qf)[HD / 16], const f32x16 (&s_cur)[2],
+                                           f32x16 (&s_next)[2], SoftmaxState<HD>& st,
+                                           float scale_log2, int valid_next) {
+    constexpr int NF = HD / 8;        // MFMAs per phase (K fragments = V^T fragments)
+    constexpr int EP = 32 / NF;       // score elements per lane handled per MFMA slot
+    constexpr int DP = 16 / NF;       // fp16 pairs summed per MFMA slot
     const float mneg = -st.m_run;
 
-    float ls = 0.f;
+    // ---- phase 1 ----
+    constexpr int PD = 2;             // LDS fragment prefetch depth
+    bf16x8 kf[PD];
+    if (NEXT) {
+#pragma unroll
+        for (int j = 0; j < PD; ++j) kf[j] = k_frag<HD>(lk_next, fa, j);
+    }
     f16x8 pf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < NF; ++i) {
+        if (NEXT) {
+            const int kb = i & 1;
+            if (i < 2) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, mneg));
-            ls += p;
+                for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
+            }
+            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % PD], qf[i >> 1], s_next[kb], 0, 0, 0);
+            if (i + PD < NF) kf[i % PD] = k_frag<HD>(lk_next, fa, i + PD);
+        }
+#pragma unroll
+        for (int e = i * EP; e < (i + 1) * EP; ++e) {
+            const int kb = e >> 4, r = e & 15;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], scale_log2, mneg));
             pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
         }
-    st.l_run += ls;
+    }
 
+    // ---- phase 2 ----
+    f16x8 vf[PD];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int j = 0; j < PD; ++j) vf[j] = v_frag<HD>(lv_cur, fa, j);
+    float ls = 0.f;
+    float mx = -__builtin_inff();
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(lv + L::v_off(32 * db + m, 2 * g + hh));
-            st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pf[g], st.o[db], 0, 0, 0);
+    for (int i = 0; i < NF; ++i) {
+        st.o[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % PD], pf[i & 3], st.o[i >> 2], 0, 0, 0);
+        if (i + PD < NF) vf[i % PD] = v_frag<HD>(lv_cur, fa, i + PD);
+#pragma unroll
+        for (int q = i * DP; q < (i + 1) * DP; ++q) {
+            const f16x2 pair = {pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]};
+            ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
         }
+        if (NEXT && !MASK_NEXT) {
+#pragma unroll
+            for (int e = i * EP; e < (i + 1) * EP; ++e) mx = fmaxf(mx, s_next[e >> 4][e & 15]);
+        }
+    }
+    st.l_run += ls;
+    if (!NEXT) return 0.f;
+    if (MASK_NEXT) return tile_max<true>(s_next, scale_log2, valid_next);
+    return pair_max(mx) * scale_log2;
 }
 
 // 16-byte global load as a bf16 fragment (zero when !ok).

@@ -381,6 +381,9 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
         return word * 32 + b;
     };
 
+    FragAddr<HD> fa;
+    fa.init();
+    f32x16 sc[2], sd[2];
     SoftmaxState<HD> st;
     st.init();
     int jc = advance();
@@ -391,8 +394,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
         __syncthreads();
         const int jn = advance();
         if (jn >= 0) issue(jn, lds + ((it + 1) & 1) * L::kBytes);
-        if ((msk[side][jc >> 5] >> (jc & 31)) & 1u)
-            attn_tile<HD, false>(cur, cur + L::kKBytes, qf, st, scale_log2, kTileN);
+        if ((msk[side][jc >> 5] >> (jc & 31)) & 1u) {
+            qk_tile<HD>(cur, fa, qf, sc);
+            maybe_rescale<HD>(st, tile_max<false>(sc, scale_log2, kTileN));
+            tile_step<HD, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN);
+        }
         jc = jn;
     }
 
