@@ -56,8 +56,8 @@ AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
     AttnPlan p{};
     if (dtype != MMDIT_BF16) return p;   // the fp32 kernel needs no workspace
     p.n_pad = round_up(n_kv, kTileN);
-    p.q_tiles = (int32_t)((n_q + 127) / 128);
-    p.n_q_pad = (int64_t)p.q_tiles * 128;
+    p.q_tiles = (int32_t)((n_q + kDenseQ - 1) / kDenseQ);
+    p.n_q_pad = (int64_t)p.q_tiles * kDenseQ;
     p.kv_tiles = (int32_t)(p.n_pad / kTileN);
     const int64_t base = (int64_t)p.q_tiles * heads;
     int splits = 1;

@@ -8,9 +8,10 @@
 // (paper.rainbus.top analysis, workflow step 3 and novelty 2; trdm.cn
 // article, sections 2.1-2.2).
 //
-// bf16 path: 256-thread workgroups (4 waves x 32 queries = 128 queries) walk
-// the key range in 64-key tiles staged through LDS; the next tile's global
-// loads are in flight in registers while the current tile is computed.  When
+// bf16 path: 512-thread workgroups (8 waves x 32 queries = 256 queries, one
+// workgroup and two waves per SIMD on a CU) walk the key range in 64-key
+// tiles staged through LDS by direct global -> LDS copies; a K tile is shared
+// by 256 queries, which halves copy traffic per FLOP against 128-query tiles.  When
 // there are too few query tiles to fill 256 CUs (audio queries against video
 // keys) the key range is split and a combine kernel merges the partial
 // results by their log-sum-exp.  Workgroup ids are remapped so that the
@@ -50,9 +51,9 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     using L = TileLayout<HD>;
-    constexpr int NW = 4;
+    constexpr int NW = kDenseThreads / kWave;
     constexpr int KS = HD / 16;
     constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);   // K copies per wave per tile
     constexpr int VCH = HD * 8 / (kWave * NW);                 // V^T copies per wave per tile
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int64_t rstride = (int64_t)a.heads * HD;
     const int64_t krb = rstride * 2;                            // bytes per key row
 
-    const int64_t qrow = (int64_t)qt * 128 + w * 32 + m;
+    const int64_t qrow = (int64_t)qt * kDenseQ + w * 32 + m;
     bf16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -285,9 +286,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s) {
     const int total = a.q_tiles * a.heads * a.splits;
     const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
     if (hd == 128)
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kDenseThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kDenseThreads), 0, s, a);
     return hipGetLastError();
 }
 

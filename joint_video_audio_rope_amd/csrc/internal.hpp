@@ -18,6 +18,9 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 // Keys per K/V tile of the attention kernels.
 constexpr int kTileN = 64;
+// Dense bf16 attention workgroup: threads and queries (32 per wave).
+constexpr int kDenseThreads = 512;
+constexpr int kDenseQ = kDenseThreads / kWave * 32;
 
 // ---- RoPE ------------------------------------------------------------------
 struct RopeSeg {
@@ -54,7 +57,7 @@ struct AttnArgs {
     float* part_ml;        // [splits][heads][n_q_pad][2]
     int64_t n_q, n_kv, n_pad, n_q_pad;
     int32_t heads;
-    int32_t q_tiles;       // ceil(n_q / 128)
+    int32_t q_tiles;       // ceil(n_q / kDenseQ)
     int32_t splits;
     int32_t tiles_per_split;
     int32_t kv_tiles;
