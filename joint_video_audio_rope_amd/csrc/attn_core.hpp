@@ -286,6 +286,40 @@ __device__ __forceinline__ float tile_step(const char* __restrict__ lk_next,
     return pair_max(mx) * scale_log2;
 }
 
+// P(t) = exp2(S(t) * scale - m) in fp16 (non-pipelined form).
+template <int HD>
+__device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], const SoftmaxState<HD>& st,
+                                          float scale_log2, f16x8 (&pf)[4]) {
+    const float mneg = -st.m_run;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int kb = e >> 4, r = e & 15;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, mneg));
+        pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
+    }
+}
+
+// O^T += V^T P^T for one tile plus the row sum of P (non-pipelined form).
+template <int HD>
+__device__ __forceinline__ void pv_tile(const char* __restrict__ lv, const FragAddr<HD>& fa,
+                                        const f16x8 (&pf)[4], SoftmaxState<HD>& st) {
+    constexpr int NF = HD / 8;
+    constexpr int NDB = HD / 32;
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const int g = i / NDB, db = i % NDB;   // key group outer: independent accumulators back to back
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag<HD>(lv, fa, 4 * db + g), pf[g], st.o[db], 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const f16x2 pair = {pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]};
+        ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
+    }
+    st.l_run += ls;
+}
+
 // 16-byte global load as a bf16 fragment (zero when !ok).
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p, bool ok) {
     uint4 u = make_uint4(0, 0, 0, 0);
@@ -305,6 +339,14 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
 // tiles is preceded by this explicit wait (s_waitcnt vmcnt(0); the immediate
 // keeps expcnt and lgkmcnt at their no-wait maxima).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's global -> LDS copies are outstanding
+// (copies complete in issue order).  N < 16.
+template <int N>
+__device__ __forceinline__ void wait_dma_upto() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Wave index as a scalar (uniform) value.
 __device__ __forceinline__ int wave_id() {

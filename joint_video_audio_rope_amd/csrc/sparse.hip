@@ -293,11 +293,16 @@ __global__ __launch_bounds__(kSelThreads) void block_select_kernel(SparseGeom g,
 
 // Sparse attention.  A workgroup of 4 waves serves two query blocks of one
 // head, 2p and 2p + 1 (neighbours along w inside a zone, whose selections
-// mostly coincide): waves 0-1 own block 2p, waves 2-3 block 2p + 1.  The
+// largely coincide): waves 0-1 own block 2p, waves 2-3 block 2p + 1.  The
 // workgroup walks the union of the two selections in ascending block id,
 // staging each key block's K rows (gathered from the raster layout) and its
 // fp16 V^T block in double-buffered LDS; a wave pair computes a tile only if
-// its own block selected it.
+// its own block selected it.  Sharing a staged tile between two blocks cuts
+// the gather traffic (the kernel is bound by it: a head's K and V^T are
+// 88 MB, far beyond L2) at the price of idle waves on tiles only one block
+// selected.  Dispatch keeps all XCDs on one head at a time (its K/V^T stay
+// in the last-level cache) and gives each XCD a contiguous eighth of that
+// head's blocks (spatial neighbours, similar selections).
 template <int HD>
 __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const __bf16* __restrict__ q,
                                                              const __bf16* __restrict__ k,
@@ -312,12 +317,11 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
     __shared__ uint32_t msk[2][kSelMax / 32];
 
     const int pairs = (g.nb + 1) >> 1;
-    const int total = g.heads * pairs;
-    const int per_xcd = (total + 7) >> 3;
-    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (logical >= total) return;
-    const int head = logical / pairs;
-    const int pr = logical - head * pairs;
+    const int per = (pairs + 7) >> 3;
+    const int slot = (int)(blockIdx.x >> 3);
+    const int head = slot / per;
+    const int pr = (int)(blockIdx.x & 7) * per + (slot - head * per);
+    if (head >= g.heads || pr >= pairs) return;
     const int nw = (g.nb + 31) >> 5;
     const bool has_b = 2 * pr + 1 < g.nb;
 
@@ -443,8 +447,7 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
-    const int total = g.heads * ((g.nb + 1) / 2);
-    const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    const unsigned blocks = (unsigned)(8 * ((((g.nb + 1) / 2) + 7) / 8) * g.heads);
     hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3(blocks), dim3(256), 0, s, g, q, k, scale_log2,
                        w, o);
     (void)hd;
