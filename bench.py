@@ -42,15 +42,145 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the oracle sample (all heads, all keys)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 1 GiB device copy (counter calibration) and three joint-attention "
+                         "calls on the 480p-latent layer, then exit (profile with rocprofv3 --pmc)")
+    ap.add_argument("--summarize", nargs="+", metavar="CSV",
+                    help="print markdown summaries of rocprofv3 csv output (kernel_trace.csv, "
+                         "or FETCH_SIZE and WRITE_SIZE counter_collection.csv), then exit")
+    ap.add_argument("--traffic-out", metavar="JSON",
+                    help="with --summarize over the two counter files of a --traffic-probe run: "
+                         "write the copy-calibrated HBM bytes per joint-attention call here")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("attn.hip", "attn_core.hpp", "internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "joint_attn_480p_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "joint_video_audio_rope_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per joint-attention launch from the committed counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30            # the probe's device copy: 1 GiB read + 1 GiB written
+
+
+def traffic_from_counters(means):
+    """HBM bytes of one joint-attention call (V^T staging + attention kernel)
+    from mean FETCH_SIZE / WRITE_SIZE KiB per dispatch, each scaled by what the
+    counter reads for the 1 GiB copy."""
+    def mean(part, counter):
+        v = [x for (k, c), x in means.items() if part in k and c == counter]
+        if len(v) != 1:
+            raise SystemExit("expected one %s entry for %s, found %d" % (counter, part, len(v)))
+        return v[0]
+
+    f_scale = COPY_BYTES / (mean("copyBuffer", "FETCH_SIZE") * 1024.0)
+    w_scale = COPY_BYTES / (mean("copyBuffer", "WRITE_SIZE") * 1024.0)
+    out = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    total = 0.0
+    for part in ("vt_dense_kernel", "attn_bf16_kernel"):
+        fb = mean(part, "FETCH_SIZE") * 1024.0 * f_scale
+        wb = mean(part, "WRITE_SIZE") * 1024.0 * w_scale
+        out["kernels"][part] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
+        total += fb + wb
+    out["bytes_per_launch"] = round(total)
+    out["source_sha256"] = kernel_source_hash()
+    return out
+
+
+def summarize(paths, traffic_out=None):
+    import collections
+    import csv
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0][:64]
+
+    means = {}
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        print("### %s\n" % os.path.basename(path))
+        if rows and "Counter_Name" in rows[0]:
+            g = collections.defaultdict(list)
+            for r in rows:
+                g[(short(r["Kernel_Name"]), r["Grid_Size"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+            print("| kernel | grid (threads) | counter | dispatches | mean KiB per dispatch |")
+            print("|---|---|---|---|---|")
+            for (k, gs, c), v in sorted(g.items()):
+                print("| %s | %s | %s | %d | %.0f |" % (k, gs, c, len(v), sum(v) / len(v)))
+                means[(k, c)] = sum(v) / len(v)
+        else:
+            g = collections.defaultdict(list)
+            for r in rows:
+                g[(short(r["Kernel_Name"]), r["Grid_Size_X"], r["Workgroup_Size_X"])].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+            print("| kernel | grid x (threads) | workgroup | calls | avg ms | min ms | max ms |")
+            print("|---|---|---|---|---|---|---|")
+            for (k, gs, wg), v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+                if sum(v) >= 0.05:
+                    print("| %s | %s | %s | %d | %.3f | %.3f | %.3f |" % (k, gs, wg, len(v), sum(v) / len(v), min(v), max(v)))
+        print()
+    if traffic_out:
+        t = traffic_from_counters(means)
+        with open(traffic_out, "w") as f:
+            json.dump(t, f, indent=1)
+        print("traffic per joint-attention call: %.4g bytes (%s)" % (t["bytes_per_launch"], traffic_out))
+
+
+def traffic_probe():
+    import torch
+
+    import joint_video_audio_rope_amd as J
+    from synth import WORKLOADS, joint_inputs
+
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    x = joint_inputs(WORKLOADS["480p"], "cuda")
+    n = x["q"].shape[0]
+    o = torch.empty((n, 24, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, 24, 128, J.MMDIT_BF16),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        J.mmdit_joint_attn(x["q"], x["k"], x["v"], o=o, ws=ws)
+    torch.cuda.synchronize()
+    print("traffic probe done: 1 GiB copy x2, joint attention x3", flush=True)
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.traffic_out)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        traffic_probe()
+        return
     import torch
 
     import joint_video_audio_rope_amd as J
@@ -142,7 +272,7 @@ def main():
                        "pct_bf16_peak": round(100.0 * joint_tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(joint_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(joint_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "kernel": "joint attention call (V^T staging + attn_bf16_kernel<128>), "
                                "4*N^2*d*h = %.4g FLOP per call" % fl_joint},
     }
