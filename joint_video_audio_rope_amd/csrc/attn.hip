@@ -50,10 +50,10 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
     }
 }
 
-template <int HD>
-__global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a) {
+template <int HD, int QB>
+__global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArgs a) {
     using L = TileLayout<HD>;
-    constexpr int NW = kDenseThreads / kWave;
+    constexpr int NW = dense_threads(QB) / kWave;
     constexpr int KS = HD / 16;
     constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);   // K copies per wave per tile
     constexpr int VCH = HD * 8 / (kWave * NW);                 // V^T copies per wave per tile
@@ -77,11 +77,16 @@ __global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a)
     const int64_t rstride = (int64_t)a.heads * HD;
     const int64_t krb = rstride * 2;                            // bytes per key row
 
-    const int64_t qrow = (int64_t)qt * kDenseQ + w * 32 + m;
-    bf16x8 qf[KS];
+    // query row of this lane in query block qb: qrow0 + 32 qb
+    const int64_t qrow0 = (int64_t)qt * kDenseQ + w * 32 * QB + m;
+    bf16x8 qf[QB][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int64_t qrow = qrow0 + 32 * qb;
+            qf[qb][ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
+        }
 
     // Each lane's share of the tile copies, fixed for the whole key walk: the
     // byte offset (from the tile's first key row) of the 16-byte chunk that
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a)
 
     FragAddr<HD> fa;
     fa.init();
-    SoftmaxState<HD> st;
+    SoftmaxState<HD, QB> st;
     st.init();
     const int last_valid = (int)(a.n_kv - (int64_t)(tile1 - 1) * kTileN);   // 1..64
     const bool last_partial = last_valid < kTileN;
@@ -147,10 +152,13 @@ __global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a)
     if (tile0 + 1 < tile1) issue_k(tile0 + 1, kbuf(1));
     wait_dma();
     __syncthreads();
-    f32x16 sa[2], sb[2];
-    qk_tile<HD>(kbuf(0), fa, qf, sa);
-    float mx = (last_partial && tile0 + 1 == tile1) ? tile_max<true>(sa, a.scale_log2, last_valid)
-                                                    : tile_max<false>(sa, a.scale_log2, kTileN);
+    f32x16 sa[QB][2], sb[QB][2];
+    qk_tile<HD, QB>(kbuf(0), fa, qf, sa);
+    float mx[QB];
+    if (last_partial && tile0 + 1 == tile1)
+        tile_max<true, QB>(sa, a.scale_log2, last_valid, mx);
+    else
+        tile_max<false, QB>(sa, a.scale_log2, kTileN, mx);
 
     // Top of step t: K(t+1) and V(t) are published; every wave is done with
     // K(t) and V(t-1), whose buffers receive K(t+2) and V(t+1).
@@ -160,46 +168,55 @@ __global__ __launch_bounds__(kDenseThreads, 1) void attn_bf16_kernel(AttnArgs a)
         __syncthreads();
         if (t + 2 < tile1) issue_k(t + 2, kbuf(b));
         if (t + 1 < tile1) issue_v(t + 1, vbuf(b ^ 1));
-        maybe_rescale<HD>(st, mx);
+        maybe_rescale<HD, QB>(st, mx);
     };
     // steps whose next tile is full
     const int main_end = tile1 - 1 - (last_partial ? 1 : 0);
     int t = tile0;
     for (; t + 1 < main_end; t += 2) {
         top(t);
-        mx = tile_step<HD, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
-                                        st, a.scale_log2, kTileN);
+        tile_step<HD, QB, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                       st, a.scale_log2, kTileN, mx);
         top(t + 1);
-        mx = tile_step<HD, true, false>(kbuf((t + 2 - tile0) & 1), vbuf((t + 1 - tile0) & 1), fa, qf, sb,
-                                        sa, st, a.scale_log2, kTileN);
+        tile_step<HD, QB, true, false>(kbuf((t + 2 - tile0) & 1), vbuf((t + 1 - tile0) & 1), fa, qf, sb,
+                                       sa, st, a.scale_log2, kTileN, mx);
     }
     if (t < main_end) {
         top(t);
-        mx = tile_step<HD, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
-                                        st, a.scale_log2, kTileN);
+        tile_step<HD, QB, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                       st, a.scale_log2, kTileN, mx);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[qb][kb] = sb[qb][kb];
         ++t;
     }
     if (t + 1 < tile1) {   // the next tile is the partial last one
         top(t);
-        mx = tile_step<HD, true, true>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
-                                       st, a.scale_log2, last_valid);
+        tile_step<HD, QB, true, true>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+                                      st, a.scale_log2, last_valid, mx);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[qb][kb] = sb[qb][kb];
         ++t;
     }
     top(t);
-    tile_step<HD, false, false>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN);
+    tile_step<HD, QB, false, false>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN,
+                                    mx);
 
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    if (qrow >= a.n_q) return;
-    if (a.splits == 1) {
-        store_o<HD>(a.o + qrow * rstride + head * HD, st, 1.f / l_tot);
-    } else {
-        const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
-        store_o<HD>(a.part_o + prow * HD, st, 1.f);
-        if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m_run, l_tot);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32);
+        const int64_t qrow = qrow0 + 32 * qb;
+        if (qrow >= a.n_q) continue;
+        if (a.splits == 1) {
+            store_o<HD>(a.o + qrow * rstride + head * HD, st.o[qb], 1.f / l_tot);
+        } else {
+            const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
+            store_o<HD>(a.part_o + prow * HD, st.o[qb], 1.f);
+            if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m_run[qb], l_tot);
+        }
     }
 }
 
@@ -285,10 +302,11 @@ hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int hea
 hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s) {
     const int total = a.q_tiles * a.heads * a.splits;
     const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    constexpr int QB = kDenseQB;
     if (hd == 128)
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(kDenseThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, QB>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
     else
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(kDenseThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, QB>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
     return hipGetLastError();
 }
 

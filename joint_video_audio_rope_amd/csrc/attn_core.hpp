@@ -1,6 +1,6 @@
 // Shared inner loop of the bf16 attention kernels (dense and block-sparse).
 //
-// One wavefront owns 32 queries.  Per 64-key tile it computes the transposed
+// One wavefront owns QB blocks of 32 queries.  Per 64-key tile it computes the transposed
 // score block S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as the A
 // operand, the wave's Q rows held in registers as the B operand), runs the
 // fp32 online softmax in the exp2 domain, and accumulates O^T += V^T P^T with
@@ -83,19 +83,24 @@ struct TileLayout {
     }
 };
 
-template <int HD>
+// Online-softmax state of a wave's QB query blocks of 32 queries each; lane
+// l owns query l % 32 of every block.
+template <int HD, int QB = 1>
 struct SoftmaxState {
     static constexpr int DB = HD / 32;
-    f32x16 o[DB];
-    float m_run;   // reference max of scaled logits (log2 domain)
-    float l_run;   // running sum over this lane's half of the keys
+    f32x16 o[QB][DB];
+    float m_run[QB];   // reference max of scaled logits (log2 domain)
+    float l_run[QB];   // running sum over this lane's half of the keys
     __device__ void init() {
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
+        for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-        m_run = -__builtin_inff();
-        l_run = 0.f;
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[qb][i][r] = 0.f;
+            m_run[qb] = -__builtin_inff();
+            l_run[qb] = 0.f;
+        }
     }
 };
 
@@ -136,17 +141,24 @@ __device__ __forceinline__ f16x8 v_frag(const char* lv, const FragAddr<HD>& fa, 
 }
 
 // Scores S^T = K Q^T of one tile (not overlapped; the first tile of a walk).
-template <int HD>
+// Each K fragment read from LDS feeds the QB query blocks.
+template <int HD, int QB>
 __device__ __forceinline__ void qk_tile(const char* lk, const FragAddr<HD>& fa,
-                                        const bf16x8 (&qf)[HD / 16], f32x16 (&s)[2]) {
+                                        const bf16x8 (&qf)[QB][HD / 16], f32x16 (&s)[QB][2]) {
     constexpr int NF = HD / 8;   // fragments per tile: 2 blocks x HD/16 steps
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < NF; ++i)
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lk, fa, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+            for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        const bf16x8 kf = k_frag<HD>(lk, fa, i);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            s[qb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][i >> 1], s[qb][i & 1], 0, 0, 0);
+    }
 }
 
 // Maximum of x over lanes l and l ^ 32 (the two halves of one query's keys).
@@ -158,59 +170,71 @@ __device__ __forceinline__ float pair_max(float x) {
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
-// Scaled (log2-domain) maximum of a score tile over both halves of the
-// lane pair; with MASK, keys >= valid are set to -inf first.
-template <bool MASK>
-__device__ __forceinline__ float tile_max(f32x16 (&s)[2], float scale_log2, int valid) {
+// Scaled (log2-domain) maximum of each query block's score tile over both
+// halves of the lane pair; with MASK, keys >= valid are set to -inf first.
+template <bool MASK, int QB>
+__device__ __forceinline__ void tile_max(f32x16 (&s)[QB][2], float scale_log2, int valid, float (&mx)[QB]) {
     const int hh = (threadIdx.x & 63) >> 5;
-    if (MASK) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        if (MASK) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (tile_key(kb, r, hh) >= valid) s[qb][kb][r] = -__builtin_inff();
+        }
+        float x = s[qb][0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (tile_key(kb, r, hh) >= valid) s[kb][r] = -__builtin_inff();
+            for (int r = 0; r < 16; ++r) x = fmaxf(x, s[qb][kb][r]);
+        mx[qb] = pair_max(x) * scale_log2;
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    return pair_max(mx) * scale_log2;
 }
 
 // Move the reference max when a tile's max exceeds it by more than 2^8
 // (wave-uniform branch, rare after the first tiles).
-template <int HD>
-__device__ __forceinline__ void maybe_rescale(SoftmaxState<HD>& st, float mx) {
-    if (__any(mx > st.m_run + 8.f)) {
-        const float m_new = fmaxf(st.m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
-        st.m_run = m_new;
-        st.l_run *= alpha;
+template <int HD, int QB>
+__device__ __forceinline__ void maybe_rescale(SoftmaxState<HD, QB>& st, const float (&mx)[QB]) {
+    bool up = false;
 #pragma unroll
-        for (int db = 0; db < HD / 32; ++db)
+    for (int qb = 0; qb < QB; ++qb) up |= mx[qb] > st.m_run[qb] + 8.f;
+    if (__any(up)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+        for (int qb = 0; qb < QB; ++qb) {
+            const float m_new = fmaxf(st.m_run[qb], mx[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+            st.m_run[qb] = m_new;
+            st.l_run[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.o[qb][db][r] *= alpha;
+        }
     }
 }
 
-// One pipelined step for the wave's 32 queries.
+// One pipelined step for the wave's QB x 32 queries.
 //   phase 1: P(t) = exp2(S(t) * scale - m) into fp16, interleaved with the
-//            16 MFMAs of S(t+1) = K(t+1) Q^T (when NEXT);
-//   phase 2: O^T += V(t)^T P(t)^T (16 MFMAs), interleaved with the row sum of
-//            P(t) (fp16 pairs through v_dot2, i.e. exactly the values the
+//            16 QB MFMAs of S(t+1) = K(t+1) Q^T (when NEXT);
+//   phase 2: O^T += V(t)^T P(t)^T (16 QB MFMAs), interleaved with the row sum
+//            of P(t) (fp16 pairs through v_dot2, i.e. exactly the values the
 //            MFMA consumes) and, when NEXT, the maximum of S(t+1).
-// Returns the scaled maximum of S(t+1) (unused when !NEXT).
-template <int HD, bool NEXT, bool MASK_NEXT>
-__device__ __forceinline__ float tile_step(const char* __restrict__ lk_next,
-                                           const char* __restrict__ lv_cur, const FragAddr<HD>& fa,
-                                           const bf16x8 (&qf)[HD / 16], const f32x16 (&s_cur)[2],
-                                           f32x16 (&s_next)[2], SoftmaxState<HD>& st,
-                                           float scale_log2, int valid_next) {
-    constexpr int NF = HD / 8;        // MFMAs per phase (K fragments = V^T fragments)
-    constexpr int EP = 32 / NF;       // score elements per lane handled per MFMA slot
-    constexpr int DP = 16 / NF;       // fp16 pairs summed per MFMA slot
-    const float mneg = -st.m_run;
+// Every fragment read from LDS feeds QB MFMAs.  Writes the scaled maximum of
+// S(t+1) per query block to mx (untouched when !NEXT).
+template <int HD, int QB, bool NEXT, bool MASK_NEXT>
+__device__ __forceinline__ void tile_step(const char* __restrict__ lk_next,
+                                          const char* __restrict__ lv_cur, const FragAddr<HD>& fa,
+                                          const bf16x8 (&qf)[QB][HD / 16], const f32x16 (&s_cur)[QB][2],
+                                          f32x16 (&s_next)[QB][2], SoftmaxState<HD, QB>& st,
+                                          float scale_log2, int valid_next, float (&mx)[QB]) {
+    constexpr int NF = HD / 8;        // fragments per phase (K fragments = V^T fragments)
+    constexpr int EP = 32 / NF;       // score elements per lane and query block per fragment
+    constexpr int DP = 16 / NF;       // fp16 pairs summed per query block per fragment
+    float mneg[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mneg[qb] = -st.m_run[qb];
 
     // ---- phase 1 ----
     constexpr int PD = 4;             // LDS fragment prefetch depth
@@ -219,105 +243,94 @@ __device__ __forceinline__ float tile_step(const char* __restrict__ lk_next,
 #pragma unroll
         for (int j = 0; j < PD; ++j) kf[j] = k_frag<HD>(lk_next, fa, j);
     }
-    f16x8 pf[4];
+    f16x8 pf[QB][4];
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-        if (NEXT) {
-            const int kb = i & 1;
-            if (i < 2) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
+        for (int qb = 0; qb < QB; ++qb) {
+            if (NEXT) {
+                const int kb = i & 1;
+                if (i < 2) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s_next[qb][kb][r] = 0.f;
+                }
+                s_next[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % PD], qf[qb][i >> 1],
+                                                                         s_next[qb][kb], 0, 0, 0);
             }
-            s_next[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % PD], qf[i >> 1], s_next[kb], 0, 0, 0);
-            if (i + PD < NF) kf[i % PD] = k_frag<HD>(lk_next, fa, i + PD);
-        }
 #pragma unroll
-        for (int e = i * EP; e < (i + 1) * EP; ++e) {
-            const int kb = e >> 4, r = e & 15;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][r], scale_log2, mneg));
-            pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
+            for (int e = i * EP; e < (i + 1) * EP; ++e) {
+                const int kb = e >> 4, r = e & 15;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][kb][r], scale_log2, mneg[qb]));
+                pf[qb][2 * kb + (r >> 3)][r & 7] = (_Float16)p;
+            }
         }
+        if (NEXT && i + PD < NF) kf[i % PD] = k_frag<HD>(lk_next, fa, i + PD);
     }
 
     // ---- phase 2 ----
     f16x8 vf[PD];
 #pragma unroll
     for (int j = 0; j < PD; ++j) vf[j] = v_frag<HD>(lv_cur, fa, j);
-    float ls = 0.f;
-    float mx = -__builtin_inff();
+    float ls[QB], mxl[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        ls[qb] = 0.f;
+        mxl[qb] = -__builtin_inff();
+    }
     const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-        st.o[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % PD], pf[i & 3], st.o[i >> 2], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            st.o[qb][i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % PD], pf[qb][i & 3], st.o[qb][i >> 2],
+                                                                      0, 0, 0);
+#pragma unroll
+            for (int q = i * DP; q < (i + 1) * DP; ++q) {
+                const f16x2 pair = {pf[qb][q >> 2][2 * (q & 3)], pf[qb][q >> 2][2 * (q & 3) + 1]};
+                ls[qb] = __builtin_amdgcn_fdot2(pair, ones, ls[qb], false);
+            }
+            if (NEXT && !MASK_NEXT) {
+#pragma unroll
+                for (int e = i * EP; e < (i + 1) * EP; ++e) mxl[qb] = fmaxf(mxl[qb], s_next[qb][e >> 4][e & 15]);
+            }
+        }
         if (i + PD < NF) vf[i % PD] = v_frag<HD>(lv_cur, fa, i + PD);
-#pragma unroll
-        for (int q = i * DP; q < (i + 1) * DP; ++q) {
-            const f16x2 pair = {pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]};
-            ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
-        }
-        if (NEXT && !MASK_NEXT) {
-#pragma unroll
-            for (int e = i * EP; e < (i + 1) * EP; ++e) mx = fmaxf(mx, s_next[e >> 4][e & 15]);
-        }
     }
-    st.l_run += ls;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += ls[qb];
     if (NEXT && !MASK_NEXT) {
         // Pin the interleave of the hot step for the instruction scheduler
         // (groups are filled in program order): LDS fragment reads run PD
-        // MFMAs ahead, and each MFMA slot carries its share of the softmax.
+        // fragments ahead, and each MFMA slot carries its share of the softmax.
         sched_group(kSchedDsRead, PD);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
-            sched_group(kSchedMfma, 1);
-            if (i + PD < NF) sched_group(kSchedDsRead, 1);
-            sched_group(kSchedValu, EP / 2 + EP);   // fma x EP + cvt x EP/2
-            sched_group(kSchedTrans, EP);           // exp x EP
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                sched_group(kSchedMfma, 1);
+                if (qb == 0 && i + PD < NF) sched_group(kSchedDsRead, 1);
+                sched_group(kSchedValu, EP / 2 + EP);   // fma x EP + cvt x EP/2
+                sched_group(kSchedTrans, EP);           // exp x EP
+            }
         }
         sched_group(kSchedDsRead, PD);
 #pragma unroll
         for (int i = 0; i < NF; ++i) {
-            sched_group(kSchedMfma, 1);
-            if (i + PD < NF) sched_group(kSchedDsRead, 1);
-            sched_group(kSchedValu, DP + (EP + 1) / 2);   // dot2 + max
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                sched_group(kSchedMfma, 1);
+                if (qb == 0 && i + PD < NF) sched_group(kSchedDsRead, 1);
+                sched_group(kSchedValu, DP + (EP + 1) / 2);   // dot2 + max
+            }
         }
     }
-    if (!NEXT) return 0.f;
-    if (MASK_NEXT) return tile_max<true>(s_next, scale_log2, valid_next);
-    return pair_max(mx) * scale_log2;
-}
-
-// P(t) = exp2(S(t) * scale - m) in fp16 (non-pipelined form).
-template <int HD>
-__device__ __forceinline__ void softmax_p(const f32x16 (&s)[2], const SoftmaxState<HD>& st,
-                                          float scale_log2, f16x8 (&pf)[4]) {
-    const float mneg = -st.m_run;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-        const int kb = e >> 4, r = e & 15;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], scale_log2, mneg));
-        pf[2 * kb + (r >> 3)][r & 7] = (_Float16)p;
-    }
-}
-
-// O^T += V^T P^T for one tile plus the row sum of P (non-pipelined form).
-template <int HD>
-__device__ __forceinline__ void pv_tile(const char* __restrict__ lv, const FragAddr<HD>& fa,
-                                        const f16x8 (&pf)[4], SoftmaxState<HD>& st) {
-    constexpr int NF = HD / 8;
-    constexpr int NDB = HD / 32;
-    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
-    float ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-        const int g = i / NDB, db = i % NDB;   // key group outer: independent accumulators back to back
-        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag<HD>(lv, fa, 4 * db + g), pf[g], st.o[db], 0, 0, 0);
+    if (!NEXT) return;
+    if (MASK_NEXT) {
+        tile_max<true, QB>(s_next, scale_log2, valid_next, mx);
+        return;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const f16x2 pair = {pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]};
-        ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
-    }
-    st.l_run += ls;
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = pair_max(mxl[qb]) * scale_log2;
 }
 
 // 16-byte global load as a bf16 fragment (zero when !ok).
@@ -353,9 +366,10 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
-// Store the normalised (or raw) O^T accumulators of this lane's query row.
+// Store the normalised (or raw) O^T accumulators of one query block for this
+// lane's query row.
 template <int HD>
-__device__ __forceinline__ void store_o(float* orow, const SoftmaxState<HD>& st, float mul) {
+__device__ __forceinline__ void store_o(float* orow, const f32x16 (&o)[HD / 32], float mul) {
     const int hh = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db)
@@ -363,8 +377,8 @@ __device__ __forceinline__ void store_o(float* orow, const SoftmaxState<HD>& st,
         for (int g = 0; g < 4; ++g) {
             const int d0 = 32 * db + 8 * g + 4 * hh;
             *reinterpret_cast<float4*>(orow + d0) =
-                make_float4(st.o[db][4 * g] * mul, st.o[db][4 * g + 1] * mul,
-                            st.o[db][4 * g + 2] * mul, st.o[db][4 * g + 3] * mul);
+                make_float4(o[db][4 * g] * mul, o[db][4 * g + 1] * mul,
+                            o[db][4 * g + 2] * mul, o[db][4 * g + 3] * mul);
         }
 }
 

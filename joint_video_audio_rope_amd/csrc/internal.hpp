@@ -18,9 +18,14 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 // Keys per K/V tile of the attention kernels.
 constexpr int kTileN = 64;
-// Dense bf16 attention workgroup: threads and queries (32 per wave).
-constexpr int kDenseThreads = 512;
-constexpr int kDenseQ = kDenseThreads / kWave * 32;
+// Dense bf16 attention workgroup: 256 queries, each wave holding kDenseQB
+// blocks of 32 queries (so 8 / kDenseQB waves).  Two blocks per wave halve
+// the LDS fragment reads per MFMA but need ~420 registers, i.e. one wave per
+// SIMD with the accumulators in AGPRs; on gfx950 that measured 1.5x slower
+// than one block per wave with two waves per SIMD.
+constexpr int kDenseQ = 256;
+constexpr int kDenseQB = 1;
+constexpr int dense_threads(int qb) { return kDenseQ / (32 * qb) * kWave; }
 
 // ---- RoPE ------------------------------------------------------------------
 struct RopeSeg {

@@ -155,180 +155,251 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
     }
 }
 
-constexpr int kSelThreads = 256;
-constexpr int kSelMax = 4096;   // largest sortable row (power of two)
+constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup
+constexpr int kSelMax = 4096;   // largest row (blocks per head)
+// Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
+// Measured on the 24 x 64 x 112 grid (density 27.6 %): groups of 4 blocks
+// (47 % of the union tiles per block, 8 waves) ran 17 % slower than pairs
+// (66 %), with a 2- or 4-tile ring alike, so tile-copy latency is hidden and
+// the idle waves on tiles that only some blocks selected decide.
+constexpr int kSparseGroup = 2;
+constexpr int kSparseRing = 2;
 
-__device__ __forceinline__ double block_reduce_max(double x, double* red) {
-    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
-    const int wv = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[wv] = x;
-    __syncthreads();
-    double r = red[0];
-    for (int i = 1; i < kSelThreads / 64; ++i) r = fmax(r, red[i]);
-    return r;
-}
-
-__device__ __forceinline__ double block_reduce_sum(double x, double* red) {
+// Wave-wide reductions.  The xor butterfly combines the same two partial
+// results in every lane at every level (addition and max are commutative), so
+// every lane ends with the same bits: decisions taken on them are uniform.
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    const int wv = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[wv] = x;
-    __syncthreads();
-    double r = red[0];
-    for (int i = 1; i < kSelThreads / 64; ++i) r += red[i];
-    return r;
+    return x;
+}
+__device__ __forceinline__ double wave_max(double x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+    return x;
 }
 
-// a goes before b: larger probability first, equal probabilities by lower id.
-__device__ __forceinline__ bool sel_before(double pa, int ja, double pb, int jb) {
-    return pa > pb || (pa == pb && ja < jb);
-}
+__device__ __forceinline__ double key_value(uint64_t key) { return __longlong_as_double((long long)key); }
+__device__ __forceinline__ uint64_t value_key(double x) { return (uint64_t)__double_as_longlong(x); }
 
-__global__ __launch_bounds__(kSelThreads) void block_select_kernel(SparseGeom g, int top_k,
-                                                                   double top_p, SparseWs w,
-                                                                   uint32_t* __restrict__ sel_mask,
-                                                                   int32_t* __restrict__ sel_count) {
-    __shared__ double P[kSelMax];
-    __shared__ uint16_t id[kSelMax];
-    __shared__ double red[kSelThreads / 64];
-    __shared__ double wsum[kSelThreads];
-    __shared__ uint32_t words[kSelMax / 32];
-    __shared__ int first_hit;
-
+// Selection of one row of block probabilities, one wave per row.  Lane l
+// holds blocks j = l + 64 r.  The blocks in descending order of probability
+// (equal probabilities by ascending id) are never sorted: for a non-negative
+// double the bit pattern read as an unsigned integer orders like the value,
+// so the row is searched by bisection over that integer range.
+//   top-p: the element e at which the descending running sum first reaches p
+//          is the largest key x with sum(P >= x) >= p; within a run of equal
+//          values the running sum advances one element at a time.
+//   top-k: the k-th element is the largest key x with count(P >= x) >= k.
+// The selection is the longer of the two prefixes.  Slots past the row hold
+// P = -1, which no threshold >= 0 admits.
+template <int EM>   // elements per lane: nb <= 64 EM
+__global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom g, int top_k,
+                                                                      double top_p, SparseWs w,
+                                                                      uint32_t* __restrict__ sel_mask,
+                                                                      int32_t* __restrict__ sel_count) {
     const int nb = g.nb;
-    const int row = blockIdx.x;                 // head * nb + i
+    const int row = (int)blockIdx.x * kSelWaves + wave_id();   // head * nb + i
+    if (row >= g.heads * nb) return;
+    const int lane = threadIdx.x & 63;
     const double* L = w.scores + (int64_t)row * nb;
-    int ns = 1;
-    while (ns < nb) ns <<= 1;
-    const int tid = threadIdx.x;
 
     // softmax over the row, fp64
+    double P[EM];
     double mx = -__builtin_inf();
-    for (int j = tid; j < nb; j += kSelThreads) mx = fmax(mx, L[j]);
-    mx = block_reduce_max(mx, red);
+#pragma unroll
+    for (int r = 0; r < EM; ++r) {
+        const int j = lane + 64 * r;
+        P[r] = j < nb ? L[j] : -__builtin_inf();
+        mx = fmax(mx, P[r]);
+    }
+    mx = wave_max(mx);
     double se = 0.0;
-    for (int j = tid; j < nb; j += kSelThreads) {
-        const double e = exp(L[j] - mx);
-        P[j] = e;
-        se += e;
-    }
-    se = block_reduce_sum(se, red);
-    for (int j = tid; j < ns; j += kSelThreads) {
+#pragma unroll
+    for (int r = 0; r < EM; ++r) {
+        const int j = lane + 64 * r;
         if (j < nb) {
-            P[j] = P[j] / se;
-            id[j] = (uint16_t)j;
+            P[r] = exp(P[r] - mx);
+            se += P[r];
+        }
+    }
+    se = wave_sum(se);
+    double tot = 0.0;
+#pragma unroll
+    for (int r = 0; r < EM; ++r) {
+        const int j = lane + 64 * r;
+        if (j < nb) {
+            P[r] = P[r] / se;
+            tot += P[r];
         } else {
-            P[j] = -1.0;
-            id[j] = 0xffff;
+            P[r] = -1.0;
         }
     }
-    for (int wd = tid; wd < kSelMax / 32; wd += kSelThreads) words[wd] = 0u;
-    if (tid == 0) first_hit = nb;
-    __syncthreads();
+    tot = wave_sum(tot);
 
-    // bitonic sort, "before" order first
-    for (int size = 2; size <= ns; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < (ns >> 1); t += kSelThreads) {
-                const int lo = 2 * t - (t & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const double pl = P[lo], ph = P[hi];
-                const int jl = id[lo], jh = id[hi];
-                const bool swap = up ? sel_before(ph, jh, pl, jl) : sel_before(pl, jl, ph, jh);
-                if (swap) {
-                    P[lo] = ph, P[hi] = pl;
-                    id[lo] = (uint16_t)jh, id[hi] = (uint16_t)jl;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    auto count_ge = [&](double t) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r)
+            c += __popcll(__ballot(P[r] >= t));
+        return c;
+    };
+    auto count_eq = [&](double t) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r)
+            c += __popcll(__ballot(P[r] == t));
+        return c;
+    };
+    auto count_in = [&](double lo, double hi) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r)
+            c += __popcll(__ballot(P[r] >= lo && P[r] < hi));
+        return c;
+    };
+    auto sum_ge = [&](double t) {
+        double x = 0.0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r)
+            if (P[r] >= t) x += P[r];
+        return wave_sum(x);
+    };
+    // the one value left in [lo, hi) once the bisection stops
+    auto value_in = [&](double lo, double hi) {
+        double x = -1.0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r)
+            if (P[r] >= lo && P[r] < hi) x = fmax(x, P[r]);
+        return wave_max(x);
+    };
+    const uint64_t kInf = 0x7FF0000000000000ull;   // +inf: above every probability
 
-    // running sum in sorted order: each thread owns a contiguous run
+    // top-p prefix: n_p elements, the last one of value vp, the mp-th of its run
     int n_p = nb;
-    if (top_p < 1.0) {
-        const int per = ns / kSelThreads > 0 ? ns / kSelThreads : 1;
-        const int r0 = tid * per;
-        double part = 0.0;
-        for (int r = r0; r < r0 + per && r < nb; ++r) part += P[r];
-        wsum[tid] = part;
-        __syncthreads();
-        // exclusive prefix of the per-thread parts (sequential per thread: 256 adds)
-        double pre = 0.0;
-        for (int t = 0; t < tid; ++t) pre += wsum[t];
-        double run = pre;
-        for (int r = r0; r < r0 + per && r < nb; ++r) {
-            run += P[r];
-            if (run >= top_p) {
-                atomicMin(&first_hit, r);
-                break;
+    double vp = -1.0;
+    int mp = 0;
+    if (top_p < 1.0 && tot >= top_p) {
+        if (top_p <= 0.0) {
+            double x = P[0];
+#pragma unroll
+            for (int r = 1; r < EM; ++r) x = fmax(x, P[r]);
+            vp = wave_max(x);
+            mp = 1;
+            n_p = 1;
+        } else {
+            uint64_t lo = 0, hi = kInf;   // sum(P >= lo) >= p > sum(P >= hi)
+            while (hi - lo > 1 && count_in(key_value(lo), key_value(hi)) > 1) {
+                const uint64_t mid = lo + ((hi - lo) >> 1);
+                if (sum_ge(key_value(mid)) >= top_p)
+                    lo = mid;
+                else
+                    hi = mid;
             }
+            vp = value_in(key_value(lo), key_value(hi));
+            // within the run of elements equal to vp, in id order
+            const uint64_t above = value_key(vp) + 1;
+            double acc = sum_ge(key_value(above));
+            const int c_above = count_ge(key_value(above));
+            const int run = count_eq(vp);
+            mp = 1;
+            acc += vp;
+            while (acc < top_p && mp < run) {
+                acc += vp;
+                ++mp;
+            }
+            n_p = c_above + mp;
         }
-        __syncthreads();
-        n_p = first_hit < nb ? first_hit + 1 : nb;
     }
+
+    // top-k prefix
     const int kk = top_k < nb ? top_k : nb;
+    double vk = -1.0;
+    int mk = 0;
+    if (kk > 0 && kk < nb) {
+        uint64_t lo = 0, hi = kInf;   // count(P >= lo) >= k > count(P >= hi)
+        while (hi - lo > 1 && count_in(key_value(lo), key_value(hi)) > 1) {
+            const uint64_t mid = lo + ((hi - lo) >> 1);
+            if (count_ge(key_value(mid)) >= kk)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        vk = value_in(key_value(lo), key_value(hi));
+        mk = kk - count_ge(key_value(value_key(vk) + 1));
+    }
+
+    // the longer prefix: every element above the last value, plus the first
+    // m of that value's run in id order (all elements when it covers the row)
     const int K = kk > n_p ? kk : n_p;
-
-    for (int r = tid; r < K; r += kSelThreads) {
-        const int j = id[r];
-        atomicOr(&words[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-
+    const bool all = K >= nb;
+    const double v = kk > n_p ? vk : vp;
+    const int mrun = kk > n_p ? mk : mp;
     const int nw = (nb + 31) >> 5;
-    if (tid == 0) {
-        int acc = 0;
-        for (int wd = 0; wd < nw; ++wd) acc += __popc(words[wd]);
-        w.count[row] = acc;
-        if (sel_count) sel_count[row] = acc;
+    uint32_t* mrow = w.mask + (int64_t)row * nw;
+    uint32_t* srow = sel_mask ? sel_mask + (int64_t)row * nw : nullptr;
+    int before = 0;   // run elements with a lower id
+#pragma unroll
+    for (int r = 0; r < EM; ++r) {
+        const bool valid = P[r] >= 0.0;
+        const uint64_t eq = __ballot(valid && P[r] == v);
+        const int rank = before + __popcll(eq & ((1ull << lane) - 1ull));
+        before += __popcll(eq);
+        const bool sel = valid && (all || P[r] > v || (P[r] == v && rank < mrun));
+        const uint64_t b = __ballot(sel);
+        const int wd = 2 * r + lane;
+        if (lane < 2 && wd < nw) {   // words past the row hold no bits
+            const uint32_t word = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
+            mrow[wd] = word;
+            if (srow) srow[wd] = word;
+        }
     }
-    for (int wd = tid; wd < nw; wd += kSelThreads) {
-        w.mask[(int64_t)row * nw + wd] = words[wd];
-        if (sel_mask) sel_mask[(int64_t)row * nw + wd] = words[wd];
+    if (lane == 0) {
+        w.count[row] = K;
+        if (sel_count) sel_count[row] = K;
     }
 }
 
-// Sparse attention.  A workgroup of 4 waves serves two query blocks of one
-// head, 2p and 2p + 1 (neighbours along w inside a zone, whose selections
-// largely coincide): waves 0-1 own block 2p, waves 2-3 block 2p + 1.  The
-// workgroup walks the union of the two selections in ascending block id,
-// staging each key block's K rows (gathered from the raster layout) and its
-// fp16 V^T block in double-buffered LDS; a wave pair computes a tile only if
-// its own block selected it.  Sharing a staged tile between two blocks cuts
-// the gather traffic (the kernel is bound by it: a head's K and V^T are
-// 88 MB, far beyond L2) at the price of idle waves on tiles only one block
-// selected.  Dispatch keeps all XCDs on one head at a time (its K/V^T stay
-// in the last-level cache) and gives each XCD a contiguous eighth of that
-// head's blocks (spatial neighbours, similar selections).
-template <int HD>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const __bf16* __restrict__ q,
-                                                             const __bf16* __restrict__ k,
-                                                             float scale_log2, SparseWs w,
-                                                             float* __restrict__ o) {
+// Sparse attention.  A workgroup of 2 G waves serves G consecutive query
+// blocks of one head (neighbours inside a zone, whose selections largely
+// coincide): waves 2 b and 2 b + 1 own block G p + b.  The workgroup walks the
+// union of the G selections in ascending block id, staging each key block's
+// K rows (gathered from the raster layout) and its fp16 V^T block in a ring
+// of R LDS tiles whose copies run R - 1 tiles ahead; a wave pair computes a
+// tile only if its own block selected it.  Sharing a staged tile between
+// blocks cuts the gather traffic (the kernel is bound by it: a head's K and
+// V^T are 88 MB, far beyond L2) at the price of idle waves on tiles that only
+// some blocks selected.  Dispatch keeps all XCDs on one head at a time (its
+// K/V^T stay in the last-level cache) and gives each XCD a contiguous eighth
+// of that head's blocks (spatial neighbours, similar selections).
+template <int HD, int G, int R>
+__global__ __launch_bounds__(G * 128, G == 2 ? 2 : 1) void sparse_attn_kernel(
+        SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
+        SparseWs w, float* __restrict__ o) {
     using L = TileLayout<HD>;
-    constexpr int NW = 4;
+    constexpr int NW = 2 * G;
     constexpr int KS = HD / 16;
     constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);
     constexpr int VCH = HD * 8 / (kWave * NW);
-    __shared__ __attribute__((aligned(16))) char lds[2 * L::kBytes];
-    __shared__ uint32_t msk[2][kSelMax / 32];
+    constexpr int PW = KCH + VCH;                     // copies per wave per tile
+    static_assert(R >= 2 && (R & (R - 1)) == 0, "ring of a power-of-two number of tiles");
+    static_assert((R - 2) * PW < 16, "vmcnt immediate");
+    __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
+    __shared__ uint32_t msk[G][kSelMax / 32];
 
-    const int pairs = (g.nb + 1) >> 1;
-    const int per = (pairs + 7) >> 3;
+    const int groups = (g.nb + G - 1) / G;
+    const int per = (groups + 7) >> 3;
     const int slot = (int)(blockIdx.x >> 3);
     const int head = slot / per;
-    const int pr = (int)(blockIdx.x & 7) * per + (slot - head * per);
-    if (head >= g.heads || pr >= pairs) return;
+    const int grp = (int)(blockIdx.x & 7) * per + (slot - head * per);
+    if (head >= g.heads || grp >= groups) return;
     const int nw = (g.nb + 31) >> 5;
-    const bool has_b = 2 * pr + 1 < g.nb;
+    const int b0 = G * grp;
 
-    const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + 2 * pr) * nw;
-    for (int i = threadIdx.x; i < 2 * nw; i += 256) {
+    const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + b0) * nw;
+    for (int i = threadIdx.x; i < G * nw; i += G * 128) {
         const int sd = i / nw, wd = i - (i / nw) * nw;
-        msk[sd][wd] = (sd == 0 || has_b) ? mrow[sd * nw + wd] : 0u;
+        msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
     }
 
     const int wv = wave_id();
@@ -336,15 +407,15 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
     const int m = lane & 31;
-    const int qb = min(2 * pr + side, g.nb - 1);
+    const int qb = min(b0 + side, g.nb - 1);
     const int64_t rstride = (int64_t)g.heads * HD;
     const int64_t krb = rstride * 2;
 
     const int64_t qtok = (int64_t)w.base[qb] + block_local(g, (wv & 1) * 32 + m);
-    bf16x8 qf[KS];
+    bf16x8 qf[1][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
+        qf[0][ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
 
     uint32_t kbyte[KCH];   // < 2^32: checked on the host (block span * row bytes)
 #pragma unroll
@@ -361,6 +432,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
         voff[i] = (uint32_t)((d * kTileN + c * 8) * 2);
     }
 
+    auto tile = [&](int it) { return lds + (it & (R - 1)) * L::kBytes; };
     auto issue = [&](int j, char* lb) {
         const int64_t base = w.base[j];
         const char* kt = reinterpret_cast<const char*>(k + base * rstride + head * HD);
@@ -372,13 +444,19 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
     };
     __syncthreads();
 
-    // cursor over the union of both selections (uniform across the workgroup)
+    // cursor over the union of the selections (uniform across the workgroup)
     int word = 0;
-    uint32_t bits = __builtin_amdgcn_readfirstlane(msk[0][0] | msk[1][0]);
+    auto union_word = [&](int wd) {
+        uint32_t u = 0u;
+#pragma unroll
+        for (int sd = 0; sd < G; ++sd) u |= msk[sd][wd];
+        return __builtin_amdgcn_readfirstlane(u);
+    };
+    uint32_t bits = union_word(0);
     auto advance = [&]() -> int {
         while (bits == 0u) {
             if (++word >= nw) return -1;
-            bits = __builtin_amdgcn_readfirstlane(msk[0][word] | msk[1][word]);
+            bits = union_word(word);
         }
         const int b = __builtin_ctz(bits);
         bits &= bits - 1u;
@@ -387,28 +465,43 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SparseGeom g, const
 
     FragAddr<HD> fa;
     fa.init();
-    f32x16 sc[2], sd[2];
-    SoftmaxState<HD> st;
+    f32x16 sc[1][2], sd[1][2];
+    float mx[1];
+    SoftmaxState<HD, 1> st;
     st.init();
-    int jc = advance();
-    if (jc >= 0) issue(jc, lds);
-    for (int it = 0; jc >= 0; ++it) {
-        char* cur = lds + (it & 1) * L::kBytes;
-        wait_dma();
-        __syncthreads();
-        const int jn = advance();
-        if (jn >= 0) issue(jn, lds + ((it + 1) & 1) * L::kBytes);
+    // ids of the tiles in flight: ahead[0] is the current one, ahead[i] the
+    // i-th after it (-1 past the end of the union)
+    int ahead[R - 1];
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) {
+        ahead[i] = advance();
+        if (ahead[i] >= 0) issue(ahead[i], tile(i));
+    }
+    for (int it = 0; ahead[0] >= 0; ++it) {
+        // this wave's copies of the current tile have landed once at most the
+        // copies of the R - 2 tiles after it are outstanding
+        if (ahead[R - 2] >= 0)
+            wait_dma_upto<(R - 2) * PW>();
+        else
+            wait_dma();
+        __syncthreads();   // every wave's share landed; tile it - 1 is free
+        const int jc = ahead[0];
+#pragma unroll
+        for (int i = 0; i + 1 < R - 1; ++i) ahead[i] = ahead[i + 1];
+        ahead[R - 2] = advance();
+        if (ahead[R - 2] >= 0) issue(ahead[R - 2], tile(it + R - 1));
         if ((msk[side][jc >> 5] >> (jc & 31)) & 1u) {
-            qk_tile<HD>(cur, fa, qf, sc);
-            maybe_rescale<HD>(st, tile_max<false>(sc, scale_log2, kTileN));
-            tile_step<HD, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN);
+            char* cur = tile(it);
+            qk_tile<HD, 1>(cur, fa, qf, sc);
+            tile_max<false, 1>(sc, scale_log2, kTileN, mx);
+            maybe_rescale<HD, 1>(st, mx);
+            tile_step<HD, 1, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN, mx);
         }
-        jc = jn;
     }
 
-    if (2 * pr + side >= g.nb) return;
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
-    store_o<HD>(o + qtok * rstride + head * HD, st, 1.f / l_tot);
+    if (b0 + side >= g.nb) return;
+    const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
+    store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
 }
 
 }  // namespace
@@ -440,16 +533,28 @@ hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const 
 
 hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s) {
-    hipLaunchKernelGGL(block_select_kernel, dim3(g.heads * g.nb), dim3(kSelThreads), 0, s, g, top_k,
-                       top_p, w, sel_mask, sel_count);
+    const unsigned blocks = (unsigned)((g.heads * g.nb + kSelWaves - 1) / kSelWaves);
+    const dim3 grid(blocks), block(64 * kSelWaves);
+    const int em = (g.nb + 63) / 64;
+    if (em <= 8)
+        hipLaunchKernelGGL(block_select_kernel<8>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+    else if (em <= 16)
+        hipLaunchKernelGGL(block_select_kernel<16>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+    else if (em <= 32)
+        hipLaunchKernelGGL(block_select_kernel<32>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+    else if (em <= 48)
+        hipLaunchKernelGGL(block_select_kernel<48>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+    else
+        hipLaunchKernelGGL(block_select_kernel<64>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
-    const unsigned blocks = (unsigned)(8 * ((((g.nb + 1) / 2) + 7) / 8) * g.heads);
-    hipLaunchKernelGGL(sparse_attn_kernel<128>, dim3(blocks), dim3(256), 0, s, g, q, k, scale_log2,
-                       w, o);
+    constexpr int G = kSparseGroup, R = kSparseRing;
+    const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
+    hipLaunchKernelGGL((sparse_attn_kernel<128, G, R>), dim3(blocks), dim3(G * 128), 0, s, g, q, k,
+                       scale_log2, w, o);
     (void)hd;
     return hipGetLastError();
 }
