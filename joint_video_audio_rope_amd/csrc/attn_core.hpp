@@ -354,11 +354,13 @@ __device__ __forceinline__ void dma16(const void* g, char* lds_wave_base) {
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Wait until at most N of this wave's global -> LDS copies are outstanding
-// (copies complete in issue order).  N < 16.
+// (copies complete in issue order).  The 6-bit vmcnt field of the s_waitcnt
+// immediate is split over bits 3:0 and 15:14; expcnt and lgkmcnt stay at
+// their no-wait maxima.
 template <int N>
 __device__ __forceinline__ void wait_dma_upto() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Wave index as a scalar (uniform) value.

@@ -164,6 +164,13 @@ constexpr int kSelMax = 4096;   // largest row (blocks per head)
 // the idle waves on tiles that only some blocks selected decide.
 constexpr int kSparseGroup = 2;
 constexpr int kSparseRing = 2;
+// Producer-wave variant: query blocks per workgroup and ring depth.
+#ifndef MMDIT_SPARSE_STREAM
+#define MMDIT_SPARSE_STREAM 1
+#endif
+constexpr bool kSparseStream = MMDIT_SPARSE_STREAM;
+constexpr int kStreamGroup = 4;
+constexpr int kStreamRing = 4;
 
 // Wave-wide reductions.  The xor butterfly combines the same two partial
 // results in every lane at every level (addition and max are commutative), so
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(G * 128, G == 2 ? 2 : 1) void sparse_attn_kernel(
     constexpr int VCH = HD * 8 / (kWave * NW);
     constexpr int PW = KCH + VCH;                     // copies per wave per tile
     static_assert(R >= 2 && (R & (R - 1)) == 0, "ring of a power-of-two number of tiles");
-    static_assert((R - 2) * PW < 16, "vmcnt immediate");
+    static_assert((R - 2) * PW < 64, "vmcnt immediate");
     __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
     __shared__ uint32_t msk[G][kSelMax / 32];
 
@@ -504,6 +511,219 @@ __global__ __launch_bounds__(G * 128, G == 2 ? 2 : 1) void sparse_attn_kernel(
     store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
 }
 
+// Sparse attention with a producer wave.  A workgroup serves G consecutive
+// query blocks of one head with 2 G consumer waves (waves 2 b, 2 b + 1 own
+// block G p + b) and one producer wave.  The producer streams the union of
+// the G selections, in ascending block id, into a ring of R LDS tiles (K rows
+// gathered from the raster layout, the block's fp16 V^T); consumers follow the
+// same walk and compute only the tiles their block selected.  There is no
+// workgroup barrier in the walk: the producer publishes each landed tile
+// through an LDS flag, and reuses a ring slot once every consumer has released
+// the tile in it, so the consumers run up to R - 1 tiles apart and none waits
+// on another's compute except through a full ring.  Larger groups share each
+// staged tile among more blocks (a tile costs the same 32 KB however many
+// blocks use it), and the decoupled walk keeps the waves of blocks that did
+// not select a tile from idling on it.
+//
+// Flags: ready[s] = t + 1 once tile t (slot s = t mod R) has landed;
+// released[s] counts consumer waves done with slot s over all its uses.
+constexpr int kSpinLimit = 1 << 18;
+typedef __attribute__((address_space(3))) int lds_int;
+
+__device__ __forceinline__ int lds_load(lds_int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Publish v into an LDS flag once at most N of this wave's copies are
+// outstanding.  The compiler puts a full vmcnt(0) before any LDS store that
+// follows global -> LDS copies (it cannot tell the flag from the copy
+// target), which would also wait for the copies of the next tile; the wait
+// and the store are therefore issued together.  A store has no result
+// register, and an LDS operation the compiler does not see only makes its
+// own lgkmcnt waits stricter.
+template <int N>
+__device__ __forceinline__ void publish_after(lds_int* flag, int v) {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __asm__ volatile("s_waitcnt vmcnt(%2)\n\tds_write_b32 %0, %1" ::"v"(flag), "v"(v), "n"(N) : "memory");
+}
+
+// Wait until *p >= v.  After kSpinLimit sleeps the wait gives up and marks
+// the workgroup broken, which ends every later wait at once: a broken
+// protocol costs one bounded wait per workgroup and wrong results.
+__device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken) {
+    for (int i = 0;; ++i) {
+        if (__builtin_amdgcn_readfirstlane(lds_load(p)) >= v) break;
+        if (__builtin_amdgcn_readfirstlane(lds_load(broken)) != 0) break;
+        if (i == kSpinLimit) {
+            __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __asm__ volatile("" ::: "memory");
+}
+
+template <int HD, int G, int R>
+__global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_kernel(
+        SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
+        SparseWs w, float* __restrict__ o) {
+    using L = TileLayout<HD>;
+    constexpr int NC = 2 * G;                          // consumer waves; wave NC produces
+    constexpr int KS = HD / 16;
+    constexpr int KCP = kTileN * L::kKChunks / kWave;  // producer copies per tile: K
+    constexpr int VCP = HD * 8 / kWave;                //                          V^T
+    static_assert(R >= 2 && (R & (R - 1)) == 0, "ring of a power-of-two number of tiles");
+    static_assert(KCP + VCP < 64, "vmcnt immediate");
+    __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
+    __shared__ uint32_t msk[G][kSelMax / 32];
+    __shared__ int ready[R], released[R], broken;
+
+    const int groups = (g.nb + G - 1) / G;
+    const int per = (groups + 7) >> 3;
+    const int slot = (int)(blockIdx.x >> 3);
+    const int head = slot / per;
+    const int grp = (int)(blockIdx.x & 7) * per + (slot - head * per);
+    if (head >= g.heads || grp >= groups) return;
+    const int nw = (g.nb + 31) >> 5;
+    const int b0 = G * grp;
+
+    const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + b0) * nw;
+    for (int i = threadIdx.x; i < G * nw; i += (NC + 1) * kWave) {
+        const int sd = i / nw, wd = i - (i / nw) * nw;
+        msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
+    }
+    if (threadIdx.x < R) {
+        ready[threadIdx.x] = 0;
+        released[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) broken = 0;
+    __syncthreads();
+
+    const int wv = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int64_t rstride = (int64_t)g.heads * HD;
+    const int64_t krb = rstride * 2;
+
+    // cursor over the union of the selections (the same walk in every wave)
+    int word = 0;
+    auto union_word = [&](int wd) {
+        uint32_t u = 0u;
+#pragma unroll
+        for (int sd = 0; sd < G; ++sd) u |= msk[sd][wd];
+        return __builtin_amdgcn_readfirstlane(u);
+    };
+    uint32_t bits = union_word(0);
+    auto advance = [&]() -> int {
+        while (bits == 0u) {
+            if (++word >= nw) return -1;
+            bits = union_word(word);
+        }
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        return word * 32 + b;
+    };
+    auto ready_at = [&](int s) { return (lds_int*)&ready[s]; };
+    // Tiles are published in order, so every tile up to the largest flag
+    // minus one has been published: one read of the R flags clears a run.
+    int pub = -1;
+    auto wait_published = [&](int t) {
+        for (int i = 0; t > pub; ++i) {
+            int hi = 0;
+#pragma unroll
+            for (int s2 = 0; s2 < R; ++s2) hi = max(hi, lds_load(ready_at(s2)));
+            pub = __builtin_amdgcn_readfirstlane(hi) - 1;
+            if (t <= pub) break;
+            if (__builtin_amdgcn_readfirstlane(lds_load((lds_int*)&broken)) != 0) break;
+            if (i == kSpinLimit) {
+                __hip_atomic_store((lds_int*)&broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        __asm__ volatile("" ::: "memory");
+    };
+    auto released_at = [&](int s) { return (lds_int*)&released[s]; };
+    lds_int* brk = (lds_int*)&broken;
+
+    if (wv == NC) {
+        // ---- producer: all copies of every tile ----
+        uint32_t kbyte[KCP];   // < 2^32: checked on the host (block span * row bytes)
+#pragma unroll
+        for (int i = 0; i < KCP; ++i) {
+            int row, c;
+            L::k_at(i * kWave + lane, row, c);
+            kbyte[i] = (uint32_t)(block_local(g, (row & ~31) | perm_row(row & 31)) * krb + c * 16);
+        }
+        uint32_t voff[VCP];
+#pragma unroll
+        for (int i = 0; i < VCP; ++i) {
+            int d, c;
+            L::v_at(i * kWave + lane, d, c);
+            voff[i] = (uint32_t)((d * kTileN + c * 8) * 2);
+        }
+        int t = 0;
+        for (int j = advance(); j >= 0; j = advance(), ++t) {
+            const int sl = t & (R - 1);
+            if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk);   // tile t - R is done
+            char* lb = lds + sl * L::kBytes;
+            // the block's first token from the geometry (scalar arithmetic): a
+            // vector load of it would have to wait for every copy in flight
+            const char* kt = reinterpret_cast<const char*>(k + block_token(g, j, 0) * rstride + head * HD);
+#pragma unroll
+            for (int i = 0; i < KCP; ++i) dma16(kt + kbyte[i], lb + i * 1024);
+            const char* vt = reinterpret_cast<const char*>(w.vt + ((int64_t)head * g.nb + j) * HD * kTileN);
+#pragma unroll
+            for (int i = 0; i < VCP; ++i) dma16(vt + voff[i], lb + L::kKBytes + i * 1024);
+            // tile t - 1 has landed once only tile t's copies are outstanding
+            if (t >= 1) publish_after<KCP + VCP>(ready_at((t - 1) & (R - 1)), t);
+        }
+        if (t >= 1) publish_after<0>(ready_at((t - 1) & (R - 1)), t);
+        return;
+    }
+
+    // ---- consumers ----
+    const int side = wv >> 1;
+    const int hh = lane >> 5;
+    const int m = lane & 31;
+    const int qb = min(b0 + side, g.nb - 1);
+    const int64_t qtok = (int64_t)w.base[qb] + block_local(g, (wv & 1) * 32 + m);
+    bf16x8 qf[1][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[0][ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
+
+    FragAddr<HD> fa;
+    fa.init();
+    f32x16 sc[1][2], sd[1][2];
+    float mx[1];
+    SoftmaxState<HD, 1> st;
+    st.init();
+    int t = 0;
+    for (int j = advance(); j >= 0; j = advance(), ++t) {
+        const int sl = t & (R - 1);
+        // Wait for the tile even when this block skips it: released[] counts
+        // every use of a slot, so a wave may release tile t only once tile
+        // t has been published, i.e. once every wave released tile t - R.
+        // Otherwise a wave skipping ahead could release t and t + R before
+        // a slower wave is done with t, and the producer would overwrite it.
+        wait_published(t);
+        if ((msk[side][j >> 5] >> (j & 31)) & 1u) {
+            const char* cur = lds + sl * L::kBytes;
+            qk_tile<HD, 1>(cur, fa, qf, sc);
+            tile_max<false, 1>(sc, scale_log2, kTileN, mx);
+            maybe_rescale<HD, 1>(st, mx);
+            tile_step<HD, 1, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN, mx);
+        }
+        // this wave's reads of the slot are done (LDS serves a wave in order)
+        __asm__ volatile("" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(released_at(sl), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+
+    if (b0 + side >= g.nb) return;
+    const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
+    store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
+}
+
 }  // namespace
 
 hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
@@ -551,11 +771,18 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
-    constexpr int G = kSparseGroup, R = kSparseRing;
-    const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
-    hipLaunchKernelGGL((sparse_attn_kernel<128, G, R>), dim3(blocks), dim3(G * 128), 0, s, g, q, k,
-                       scale_log2, w, o);
     (void)hd;
+    if (kSparseStream) {
+        constexpr int G = kStreamGroup, R = kStreamRing;
+        const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
+        hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 1) * kWave), 0, s,
+                           g, q, k, scale_log2, w, o);
+    } else {
+        constexpr int G = kSparseGroup, R = kSparseRing;
+        const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
+        hipLaunchKernelGGL((sparse_attn_kernel<128, G, R>), dim3(blocks), dim3(G * 128), 0, s, g, q, k,
+                           scale_log2, w, o);
+    }
     return hipGetLastError();
 }
 
