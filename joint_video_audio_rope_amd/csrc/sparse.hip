@@ -158,17 +158,11 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
 constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup
 constexpr int kSelMax = 4096;   // largest row (blocks per head)
 // Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
-// Measured on the 24 x 64 x 112 grid (density 27.6 %): groups of 4 blocks
-// (47 % of the union tiles per block, 8 waves) ran 17 % slower than pairs
-// (66 %), with a 2- or 4-tile ring alike, so tile-copy latency is hidden and
-// the idle waves on tiles that only some blocks selected decide.
-constexpr int kSparseGroup = 2;
-constexpr int kSparseRing = 2;
-// Producer-wave variant: query blocks per workgroup and ring depth.
-#ifndef MMDIT_SPARSE_STREAM
-#define MMDIT_SPARSE_STREAM 1
-#endif
-constexpr bool kSparseStream = MMDIT_SPARSE_STREAM;
+// Measured on the 24 x 64 x 112 grid (density 27.6 %): a group stages on
+// average 0.73 (pairs), 0.62 (triples), 0.50 (4 blocks) of the tiles its
+// blocks select; with workgroup barriers per tile, pairs (two workgroups per
+// CU) took 164 ms and groups of 4 (idle waves on tiles only some blocks
+// selected) 205 ms, while groups of 4 fed by a producer wave take 142 ms.
 constexpr int kStreamGroup = 4;
 constexpr int kStreamRing = 4;
 
@@ -365,150 +359,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
         w.count[row] = K;
         if (sel_count) sel_count[row] = K;
     }
-}
-
-// Sparse attention.  A workgroup of 2 G waves serves G consecutive query
-// blocks of one head (neighbours inside a zone, whose selections largely
-// coincide): waves 2 b and 2 b + 1 own block G p + b.  The workgroup walks the
-// union of the G selections in ascending block id, staging each key block's
-// K rows (gathered from the raster layout) and its fp16 V^T block in a ring
-// of R LDS tiles whose copies run R - 1 tiles ahead; a wave pair computes a
-// tile only if its own block selected it.  Sharing a staged tile between
-// blocks cuts the gather traffic (the kernel is bound by it: a head's K and
-// V^T are 88 MB, far beyond L2) at the price of idle waves on tiles that only
-// some blocks selected.  Dispatch keeps all XCDs on one head at a time (its
-// K/V^T stay in the last-level cache) and gives each XCD a contiguous eighth
-// of that head's blocks (spatial neighbours, similar selections).
-template <int HD, int G, int R>
-__global__ __launch_bounds__(G * 128, G == 2 ? 2 : 1) void sparse_attn_kernel(
-        SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-        SparseWs w, float* __restrict__ o) {
-    using L = TileLayout<HD>;
-    constexpr int NW = 2 * G;
-    constexpr int KS = HD / 16;
-    constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);
-    constexpr int VCH = HD * 8 / (kWave * NW);
-    constexpr int PW = KCH + VCH;                     // copies per wave per tile
-    static_assert(R >= 2 && (R & (R - 1)) == 0, "ring of a power-of-two number of tiles");
-    static_assert((R - 2) * PW < 64, "vmcnt immediate");
-    __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
-    __shared__ uint32_t msk[G][kSelMax / 32];
-
-    const int groups = (g.nb + G - 1) / G;
-    const int per = (groups + 7) >> 3;
-    const int slot = (int)(blockIdx.x >> 3);
-    const int head = slot / per;
-    const int grp = (int)(blockIdx.x & 7) * per + (slot - head * per);
-    if (head >= g.heads || grp >= groups) return;
-    const int nw = (g.nb + 31) >> 5;
-    const int b0 = G * grp;
-
-    const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + b0) * nw;
-    for (int i = threadIdx.x; i < G * nw; i += G * 128) {
-        const int sd = i / nw, wd = i - (i / nw) * nw;
-        msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
-    }
-
-    const int wv = wave_id();
-    const int side = wv >> 1;
-    const int lane = threadIdx.x & 63;
-    const int hh = lane >> 5;
-    const int m = lane & 31;
-    const int qb = min(b0 + side, g.nb - 1);
-    const int64_t rstride = (int64_t)g.heads * HD;
-    const int64_t krb = rstride * 2;
-
-    const int64_t qtok = (int64_t)w.base[qb] + block_local(g, (wv & 1) * 32 + m);
-    bf16x8 qf[1][KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qf[0][ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
-
-    uint32_t kbyte[KCH];   // < 2^32: checked on the host (block span * row bytes)
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-        int row, c;
-        L::k_at((wv * KCH + i) * kWave + lane, row, c);
-        kbyte[i] = (uint32_t)(block_local(g, (row & ~31) | perm_row(row & 31)) * krb + c * 16);
-    }
-    uint32_t voff[VCH];
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-        int d, c;
-        L::v_at((wv * VCH + i) * kWave + lane, d, c);
-        voff[i] = (uint32_t)((d * kTileN + c * 8) * 2);
-    }
-
-    auto tile = [&](int it) { return lds + (it & (R - 1)) * L::kBytes; };
-    auto issue = [&](int j, char* lb) {
-        const int64_t base = w.base[j];
-        const char* kt = reinterpret_cast<const char*>(k + base * rstride + head * HD);
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) dma16(kt + kbyte[i], lb + (wv * KCH + i) * 1024);
-        const char* vt = reinterpret_cast<const char*>(w.vt + ((int64_t)head * g.nb + j) * HD * kTileN);
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + L::kKBytes + (wv * VCH + i) * 1024);
-    };
-    __syncthreads();
-
-    // cursor over the union of the selections (uniform across the workgroup)
-    int word = 0;
-    auto union_word = [&](int wd) {
-        uint32_t u = 0u;
-#pragma unroll
-        for (int sd = 0; sd < G; ++sd) u |= msk[sd][wd];
-        return __builtin_amdgcn_readfirstlane(u);
-    };
-    uint32_t bits = union_word(0);
-    auto advance = [&]() -> int {
-        while (bits == 0u) {
-            if (++word >= nw) return -1;
-            bits = union_word(word);
-        }
-        const int b = __builtin_ctz(bits);
-        bits &= bits - 1u;
-        return word * 32 + b;
-    };
-
-    FragAddr<HD> fa;
-    fa.init();
-    f32x16 sc[1][2], sd[1][2];
-    float mx[1];
-    SoftmaxState<HD, 1> st;
-    st.init();
-    // ids of the tiles in flight: ahead[0] is the current one, ahead[i] the
-    // i-th after it (-1 past the end of the union)
-    int ahead[R - 1];
-#pragma unroll
-    for (int i = 0; i < R - 1; ++i) {
-        ahead[i] = advance();
-        if (ahead[i] >= 0) issue(ahead[i], tile(i));
-    }
-    for (int it = 0; ahead[0] >= 0; ++it) {
-        // this wave's copies of the current tile have landed once at most the
-        // copies of the R - 2 tiles after it are outstanding
-        if (ahead[R - 2] >= 0)
-            wait_dma_upto<(R - 2) * PW>();
-        else
-            wait_dma();
-        __syncthreads();   // every wave's share landed; tile it - 1 is free
-        const int jc = ahead[0];
-#pragma unroll
-        for (int i = 0; i + 1 < R - 1; ++i) ahead[i] = ahead[i + 1];
-        ahead[R - 2] = advance();
-        if (ahead[R - 2] >= 0) issue(ahead[R - 2], tile(it + R - 1));
-        if ((msk[side][jc >> 5] >> (jc & 31)) & 1u) {
-            char* cur = tile(it);
-            qk_tile<HD, 1>(cur, fa, qf, sc);
-            tile_max<false, 1>(sc, scale_log2, kTileN, mx);
-            maybe_rescale<HD, 1>(st, mx);
-            tile_step<HD, 1, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN, mx);
-        }
-    }
-
-    if (b0 + side >= g.nb) return;
-    const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
-    store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
 }
 
 // Sparse attention with a producer wave.  A workgroup serves G consecutive
@@ -772,17 +622,10 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
     (void)hd;
-    if (kSparseStream) {
-        constexpr int G = kStreamGroup, R = kStreamRing;
-        const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
-        hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 1) * kWave), 0, s,
-                           g, q, k, scale_log2, w, o);
-    } else {
-        constexpr int G = kSparseGroup, R = kSparseRing;
-        const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
-        hipLaunchKernelGGL((sparse_attn_kernel<128, G, R>), dim3(blocks), dim3(G * 128), 0, s, g, q, k,
-                           scale_log2, w, o);
-    }
+    constexpr int G = kStreamGroup, R = kStreamRing;
+    const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
+    hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 1) * kWave), 0, s, g,
+                       q, k, scale_log2, w, o);
     return hipGetLastError();
 }
 
