@@ -426,6 +426,7 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     static_assert(KCP + VCP < 64, "vmcnt immediate");
     __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
     __shared__ uint32_t msk[G][kSelMax / 32];
+    __shared__ int bbase[kSelMax];   // first raster token of every block
     __shared__ int ready[R], released[R], broken;
 
     const int groups = (g.nb + G - 1) / G;
@@ -442,6 +443,7 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
         const int sd = i / nw, wd = i - (i / nw) * nw;
         msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
     }
+    for (int i = threadIdx.x; i < g.nb; i += (NC + 1) * kWave) bbase[i] = w.base[i];
     if (threadIdx.x < R) {
         ready[threadIdx.x] = 0;
         released[threadIdx.x] = 0;
@@ -516,9 +518,9 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
             const int sl = t & (R - 1);
             if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk);   // tile t - R is done
             char* lb = lds + sl * L::kBytes;
-            // the block's first token from the geometry (scalar arithmetic): a
-            // vector load of it would have to wait for every copy in flight
-            const char* kt = reinterpret_cast<const char*>(k + block_token(g, j, 0) * rstride + head * HD);
+            // the block's first token from LDS: a vector load of it would have
+            // to wait for every copy in flight
+            const char* kt = reinterpret_cast<const char*>(k + (int64_t)bbase[j] * rstride + head * HD);
 #pragma unroll
             for (int i = 0; i < KCP; ++i) dma16(kt + kbyte[i], lb + i * 1024);
             const char* vt = reinterpret_cast<const char*>(w.vt + ((int64_t)head * g.nb + j) * HD * kTileN);
@@ -532,7 +534,12 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     }
 
     // ---- consumers ----
-    const int side = wv >> 1;
+    // Waves w and w + 4 share a SIMD.  Blocks of a group are a 2 x 2 (h, w)
+    // square of neighbours; the selections of edge neighbours correlate most,
+    // so each SIMD gets one wave of each block of a diagonal pair (blocks 0
+    // and 3 on SIMDs 0-1, 1 and 2 on SIMDs 2-3) and concurrent work on edge
+    // neighbours spreads over all four SIMDs.
+    const int side = G == 4 ? (wv < 4 ? (wv >> 1) : 3 - ((wv - 4) >> 1)) : (wv >> 1);
     const int hh = lane >> 5;
     const int m = lane & 31;
     const int qb = min(b0 + side, g.nb - 1);
@@ -549,15 +556,21 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     SoftmaxState<HD, 1> st;
     st.init();
     int t = 0;
+    int own_word = -1;      // word of this block's mask held in own
+    uint32_t own = 0u;
     for (int j = advance(); j >= 0; j = advance(), ++t) {
         const int sl = t & (R - 1);
+        if ((j >> 5) != own_word) {
+            own_word = j >> 5;
+            own = __builtin_amdgcn_readfirstlane(msk[side][own_word]);
+        }
         // Wait for the tile even when this block skips it: released[] counts
         // every use of a slot, so a wave may release tile t only once tile
         // t has been published, i.e. once every wave released tile t - R.
         // Otherwise a wave skipping ahead could release t and t + R before
         // a slower wave is done with t, and the producer would overwrite it.
         wait_published(t);
-        if ((msk[side][j >> 5] >> (j & 31)) & 1u) {
+        if ((own >> (j & 31)) & 1u) {
             const char* cur = lds + sl * L::kBytes;
             qk_tile<HD, 1>(cur, fa, qf, sc);
             tile_max<false, 1>(sc, scale_log2, kTileN, mx);
