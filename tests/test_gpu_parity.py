@@ -259,3 +259,52 @@ def test_block_sparse_full_size():
     c = _sparse_check(w, w["top_k"], w["top_p"], n_qblocks=12)
     dens = c.mean() / c.shape[1]
     assert 0.05 < dens < 0.9
+
+
+def _sparse_tie_case(w, k_sel, p_sel, twin):
+    """Key blocks copied onto other key blocks give bitwise-equal block
+    probabilities; the selection must take equal values in ascending block id
+    (Prism page, "Metodo" section 3: top-k and top-p are prefixes of one order)."""
+    x = sparse_inputs(w, DEV)
+    T, H, W = w["T"], w["H"], w["W"]
+    idx = B.block_token_index(T, H, W, w["zone"], w["block"])
+    it = torch.as_tensor(np.asarray(idx), device=DEV)
+    k = x["k"].clone()
+    for dst, src in twin:
+        k[it[dst]] = k[it[src]]
+    o, mask, cnt = J.mmdit_block_sparse_attn(x["q"], k, x["v"], T, H, W, w["zone"], w["block"], k_sel, p_sel)
+    torch.cuda.synchronize()
+    q64, k64, v64 = f64(x["q"]), f64(k), f64(x["v"])
+    P = B.block_probs(B.block_means(q64, idx), B.block_means(k64, idx))
+    m_ref, c_ref, _ = B.select_blocks(P, k_sel, p_sel)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), B.pack_mask(m_ref))
+    assert np.array_equal(cnt.cpu().numpy(), c_ref)
+    ref = B.block_sparse_attention(q64, k64, v64, idx, m_ref, query_blocks=range(idx.shape[0]),
+                                   heads=range(w["heads"]))
+    out = f64(o)
+    worst = max(float(np.max(np.abs(out[idx[i], hh] - r))) for (hh, i), r in ref.items())
+    assert worst <= TOL_BF16, worst
+    return c_ref
+
+
+def test_block_sparse_ties_all_equal():
+    # every key block equal: uniform probabilities 1/64 (exact), so top-p 0.3
+    # needs 20 blocks and the first 20 ids are taken
+    w = shrink("sparse2k", T=8, H=16, W=32, heads=2, seed=11)
+    c = _sparse_tie_case(w, 5, 0.3, [(j, 0) for j in range(1, 64)])
+    assert (c == 20).all()
+
+
+def test_block_sparse_ties_twins():
+    # key blocks in equal pairs: every cut can fall between twins
+    w = shrink("sparse2k", T=8, H=16, W=32, heads=2, seed=12)
+    _sparse_tie_case(w, 7, 0.5, [(j + 1, j) for j in range(0, 64, 2)])
+
+
+def test_block_sparse_repeat_is_bitwise_identical():
+    w = shrink("sparse2k", T=16, H=32, W=48, heads=3, seed=13)
+    x = sparse_inputs(w, DEV)
+    a = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], 16, 32, 48)
+    b = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], 16, 32, 48)
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
