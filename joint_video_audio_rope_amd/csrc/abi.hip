@@ -238,8 +238,29 @@ mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
 // ---- block sparse plan ------------------------------------------------------------
 struct SparsePlan {
     SparseGeom g{};
-    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, total;
+    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, total;
 };
+
+// Workspace layout of a block-sparse call (shared by the plan and the size
+// query): fp64 block means, fp64 scores, selection bitmask and counts, block
+// first tokens, per-block fp16 V^T and per-block K tile images.
+void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    p->off_qbar = take((size_t)heads * nb * hd * 8);
+    p->off_kbar = take((size_t)heads * nb * hd * 8);
+    p->off_scores = take((size_t)heads * nb * nb * 8);
+    p->off_mask = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
+    p->off_count = take((size_t)heads * nb * 4);
+    p->off_base = take((size_t)nb * 4);
+    p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
+    p->off_kimg = take((size_t)heads * nb * hd * kTileN * 2);
+    p->total = off;
+}
 
 mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_sparse_desc* sp,
                          SparsePlan* p) {
@@ -261,10 +282,6 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     const int64_t n = (int64_t)T * H * W;
     if (n * heads >= ((int64_t)1 << 31))
         return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: tokens * heads must stay below 2^31");
-    // the sparse kernel addresses a key block's rows with 32-bit byte offsets
-    const int64_t span = ((int64_t)(sp->block[0] - 1) * H + sp->block[1]) * W;
-    if (span * heads * hd * 2 >= ((int64_t)1 << 32))
-        return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: a block spans 4 GiB or more of the K rows");
     const int64_t nb = n / kTileN;
     if (nb > 4096) return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: %lld blocks (max 4096)", (long long)nb);
     SparseGeom& g = p->g;
@@ -275,20 +292,7 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     g.bz_t = g.ZT / g.BT, g.bz_h = g.ZH / g.BH, g.bz_w = g.ZW / g.BW;
     g.nb = (int32_t)nb;
     g.heads = heads;
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        const size_t o = off;
-        off += align256(bytes);
-        return o;
-    };
-    p->off_qbar = take((size_t)heads * nb * hd * 8);
-    p->off_kbar = take((size_t)heads * nb * hd * 8);
-    p->off_scores = take((size_t)heads * nb * nb * 8);
-    p->off_mask = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
-    p->off_count = take((size_t)heads * nb * 4);
-    p->off_base = take((size_t)nb * 4);
-    p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
-    p->total = off;
+    sparse_layout(nb, heads, hd, p);
     return MMDIT_OK;
 }
 
@@ -358,16 +362,10 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
     }
     if (op == MMDIT_OP_BLOCK_SPARSE_ATTN) {
         if (!sp) return 0;
-        // T, H, W are not known here; the plan depends on them only through nb.
-        const int64_t nb = n_q / kTileN;
-        size_t t = 0;
-        t += align256((size_t)heads * nb * head_dim * 8) * 2;
-        t += align256((size_t)heads * nb * nb * 8);
-        t += align256((size_t)heads * nb * ((nb + 31) / 32) * 4);
-        t += align256((size_t)heads * nb * 4);
-        t += align256((size_t)nb * 4);
-        t += align256((size_t)heads * nb * head_dim * kTileN * 2);
-        return t;
+        // T, H, W are not known here; the layout depends on them only through nb.
+        SparsePlan p;
+        sparse_layout(n_q / kTileN, heads, head_dim, &p);
+        return p.total;
     }
     return 0;
 }
@@ -467,11 +465,12 @@ mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v
     sw.count = (int32_t*)(w + p.off_count);
     sw.base = (int32_t*)(w + p.off_base);
     sw.vt = (_Float16*)(w + p.off_vt);
+    sw.kimg = (__bf16*)(w + p.off_kimg);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse pool");
-    if ((e = launch_vt_blocks(p.g, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
+    if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse vt");
     if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse scores");

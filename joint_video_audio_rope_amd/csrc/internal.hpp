@@ -94,12 +94,13 @@ struct SparseWs {
     uint32_t* mask;     // [heads][nb][ceil(nb/32)] selected key blocks, bit j of word j/32
     int32_t* count;     // [heads][nb]
     int32_t* base;      // [nb] raster token index of each block's first token
-    _Float16* vt;       // [heads][nb][hd][64]
+    _Float16* vt;       // [heads][nb][hd * 64]: each key block's V^T in LDS tile order
+    __bf16* kimg;       // [heads][nb][64 * hd]: each key block's K rows in LDS tile order
 };
 
 hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                              const SparseWs& w, hipStream_t s);
-hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* v, int hd, const SparseWs& w,
+hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* k, const __bf16* v, int hd, const SparseWs& w,
                             hipStream_t s);
 hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w,
                                hipStream_t s);

@@ -76,10 +76,15 @@ __global__ __launch_bounds__(512) void block_pool_kernel(SparseGeom g, const __b
     }
 }
 
-// One workgroup per (block, head): gather 64 rows of V, write fp16 [d][64].
+// One workgroup per (block, head): gather the block's 64 rows of K and of V
+// and write each as the exact image of its LDS tile (K rows in the MFMA row
+// order, V transposed to fp16 [d][64], 16-byte chunks swizzled), so that the
+// attention kernel stages a tile with two contiguous 16 KB copies instead of
+// 64 scattered 256-byte rows.
 template <int HD>
-__global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf16* __restrict__ v,
-                                                        SparseWs w) {
+__global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf16* __restrict__ k,
+                                                        const __bf16* __restrict__ v, SparseWs w) {
+    using L = TileLayout<HD>;
     __shared__ _Float16 tile[kTileN][HD + 2];
     const int j = blockIdx.x, head = blockIdx.y;
     const int64_t base = block_token(g, j, 0);
@@ -92,14 +97,26 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
 #pragma unroll
         for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)(float)x[i];
     }
+    // K image: LDS chunk index u holds (row, chunk) = k_at(u) of the tile,
+    // row counted after the MFMA row permutation of each 32-row half
+    __bf16* kdst = w.kimg + ((int64_t)head * g.nb + j) * (kTileN * HD);
+    for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
+        int row, c;
+        L::k_at(u, row, c);
+        const int64_t tok = base + block_local(g, (row & ~31) | perm_row(row & 31));
+        *reinterpret_cast<bf16x8*>(kdst + u * 8) = load_bf16x8(k + tok * rs + head * HD + c * 8, true);
+    }
     __syncthreads();
+    // V^T image: LDS chunk index u holds keys 8 c .. 8 c + 7 of d row d,
+    // (d, c) = v_at(u)
     _Float16* dst = w.vt + ((int64_t)head * g.nb + j) * HD * kTileN;
     for (int u = threadIdx.x; u < HD * (kTileN / 8); u += 256) {
-        const int d = u / (kTileN / 8), c = u % (kTileN / 8);
+        int d, c;
+        L::v_at(u, d, c);
         f16x8 y;
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = tile[c * 8 + i][d];
-        *reinterpret_cast<f16x8*>(dst + d * kTileN + c * 8) = y;
+        *reinterpret_cast<f16x8*>(dst + u * 8) = y;
     }
 }
 
@@ -426,7 +443,6 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     static_assert(KCP + VCP < 64, "vmcnt immediate");
     __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
     __shared__ uint32_t msk[G][kSelMax / 32];
-    __shared__ int bbase[kSelMax];   // first raster token of every block
     __shared__ int ready[R], released[R], broken;
 
     const int groups = (g.nb + G - 1) / G;
@@ -443,7 +459,6 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
         const int sd = i / nw, wd = i - (i / nw) * nw;
         msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
     }
-    for (int i = threadIdx.x; i < g.nb; i += (NC + 1) * kWave) bbase[i] = w.base[i];
     if (threadIdx.x < R) {
         ready[threadIdx.x] = 0;
         released[threadIdx.x] = 0;
@@ -454,7 +469,6 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     const int wv = wave_id();
     const int lane = threadIdx.x & 63;
     const int64_t rstride = (int64_t)g.heads * HD;
-    const int64_t krb = rstride * 2;
 
     // cursor over the union of the selections (the same walk in every wave)
     int word = 0;
@@ -499,33 +513,20 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
 
     if (wv == NC) {
         // ---- producer: all copies of every tile ----
-        uint32_t kbyte[KCP];   // < 2^32: checked on the host (block span * row bytes)
-#pragma unroll
-        for (int i = 0; i < KCP; ++i) {
-            int row, c;
-            L::k_at(i * kWave + lane, row, c);
-            kbyte[i] = (uint32_t)(block_local(g, (row & ~31) | perm_row(row & 31)) * krb + c * 16);
-        }
-        uint32_t voff[VCP];
-#pragma unroll
-        for (int i = 0; i < VCP; ++i) {
-            int d, c;
-            L::v_at(i * kWave + lane, d, c);
-            voff[i] = (uint32_t)((d * kTileN + c * 8) * 2);
-        }
+        // K image and V^T of a block are contiguous 16 KB runs laid out as
+        // the LDS tile: copy i of a lane moves bytes 1024 i + 16 lane
         int t = 0;
         for (int j = advance(); j >= 0; j = advance(), ++t) {
             const int sl = t & (R - 1);
             if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk);   // tile t - R is done
             char* lb = lds + sl * L::kBytes;
-            // the block's first token from LDS: a vector load of it would have
-            // to wait for every copy in flight
-            const char* kt = reinterpret_cast<const char*>(k + (int64_t)bbase[j] * rstride + head * HD);
+            const int64_t blk = (int64_t)head * g.nb + j;
+            const char* kt = reinterpret_cast<const char*>(w.kimg + blk * (kTileN * HD)) + 16 * lane;
 #pragma unroll
-            for (int i = 0; i < KCP; ++i) dma16(kt + kbyte[i], lb + i * 1024);
-            const char* vt = reinterpret_cast<const char*>(w.vt + ((int64_t)head * g.nb + j) * HD * kTileN);
+            for (int i = 0; i < KCP; ++i) dma16(kt + i * 1024, lb + i * 1024);
+            const char* vt = reinterpret_cast<const char*>(w.vt + blk * (HD * kTileN)) + 16 * lane;
 #pragma unroll
-            for (int i = 0; i < VCP; ++i) dma16(vt + voff[i], lb + L::kKBytes + i * 1024);
+            for (int i = 0; i < VCP; ++i) dma16(vt + i * 1024, lb + L::kKBytes + i * 1024);
             // tile t - 1 has landed once only tile t's copies are outstanding
             if (t >= 1) publish_after<KCP + VCP>(ready_at((t - 1) & (R - 1)), t);
         }
@@ -598,9 +599,9 @@ hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16*
     return hipGetLastError();
 }
 
-hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* v, int hd, const SparseWs& w,
+hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* k, const __bf16* v, int hd, const SparseWs& w,
                             hipStream_t s) {
-    hipLaunchKernelGGL(vt_blocks_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, v, w);
+    hipLaunchKernelGGL(vt_blocks_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, k, v, w);
     (void)hd;
     return hipGetLastError();
 }

@@ -166,3 +166,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         L.lib()
+
+
+def test_block_sparse_workspace_query_matches_the_call():
+    # the call's own requirement (quoted in its error) equals the size query
+    sd = J.sparse_desc()
+    T, H, W, h = 24, 64, 112, 24
+    need = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN, T * H * W, T * H * W, h, 128, J.MMDIT_BF16, sd)
+    lib = J.lib()
+    st = lib.mmdit_block_sparse_attn(1 << 20, 1 << 30, 1 << 31, T, H, W, h, 128, ctypes.byref(sd), 0.088,
+                                     1 << 36, None, None, 1 << 40, need - 1, None)
+    assert st == L.MMDIT_ERR_WORKSPACE
+    assert int(re.search(r"required (\d+)", J.mmdit_last_error()).group(1)) == need
