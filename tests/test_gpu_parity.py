@@ -308,3 +308,48 @@ def test_block_sparse_repeat_is_bitwise_identical():
     b = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], 16, 32, 48)
     torch.cuda.synchronize()
     assert all(torch.equal(u, v) for u, v in zip(a, b))
+
+
+def test_rope_two_conditioning_frames():
+    # conditioning frames c = 0, 1 of 2 sit at t = -2, -1 (SkyReels-V4 analysis,
+    # workflow step 1: references take negative temporal indices)
+    w = shrink("block", T=5, H=6, W=8, n_cond_frames=2, n_audio=40, n_text=16, heads=3)
+    x, q, k = rotated(w)
+    pos, rot = R.token_positions(w)
+    assert pos[0][0] == -2 and pos[48][0] == -1
+    for src, got in ((x["q"], q), (x["k"], k)):
+        ref = R.apply_rope(f64(src), pos, rot, w["split"], w["theta"])
+        excess = np.abs(f64(got) - ref) - rope_bf16_bound(f64(src), ref)
+        assert np.max(excess) <= 0.0
+
+
+@pytest.mark.parametrize("nq,nkv,h,d", [(500, 700, 2, 128), (257, 63, 3, 64)])
+def test_fp32_path_beyond_tiny(nq, nkv, h, d):
+    q, k, v = (_rand(s, seed, torch.float32) for s, seed in (((nq, h, d), 20), ((nkv, h, d), 21), ((nkv, h, d), 22)))
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f64(o) - A.attention(f64(q), f64(k), f64(v)))) <= TOL_FP32
+
+
+def test_explicit_softmax_scale():
+    q, k, v = _rand((400, 2, 128), 23), _rand((900, 2, 128), 24), _rand((900, 2, 128), 25)
+    o = J.mmdit_joint_attn(q, k, v, softmax_scale=0.05)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f64(o) - A.attention(f64(q), f64(k), f64(v), scale=0.05))) <= TOL_BF16
+
+
+def test_block_sparse_explicit_softmax_scale():
+    w = shrink("sparse2k", T=8, H=16, W=32, heads=2, seed=14)
+    x = sparse_inputs(w, DEV)
+    s = 0.2
+    o, mask, cnt = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], 8, 16, 32, top_k=3, top_p=0.6,
+                                             softmax_scale=s)
+    torch.cuda.synchronize()
+    idx = B.block_token_index(8, 16, 32, w["zone"], w["block"])
+    q64, k64, v64 = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    P = B.block_probs(B.block_means(q64, idx), B.block_means(k64, idx), scale=s)
+    m_ref, c_ref, _ = B.select_blocks(P, 3, 0.6)
+    assert np.array_equal(mask.cpu().numpy().view(np.uint32), B.pack_mask(m_ref))
+    ref = B.block_sparse_attention(q64, k64, v64, idx, m_ref, scale=s)
+    worst = max(float(np.max(np.abs(f64(o)[idx[i], hh] - r))) for (hh, i), r in ref.items())
+    assert worst <= TOL_BF16, worst
