@@ -106,9 +106,6 @@ struct SoftmaxState {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100, kSchedTrans = 0x400;
-#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // Per-lane LDS byte offsets of the 16 K fragments (i = 2 ks + kb) and the 16
 // V^T fragments (i = 4 db + g) of a tile, relative to the tile's K / V^T base.
@@ -222,7 +219,10 @@ __device__ __forceinline__ void maybe_rescale(SoftmaxState<HD, QB>& st, const fl
 //            of P(t) (fp16 pairs through v_dot2, i.e. exactly the values the
 //            MFMA consumes) and, when NEXT, the maximum of S(t+1).
 // Every fragment read from LDS feeds QB MFMAs.  Writes the scaled maximum of
-// S(t+1) per query block to mx (untouched when !NEXT).
+// S(t+1) per query block to mx (untouched when !NEXT).  The interleave is left
+// to the instruction scheduler: pinning it with sched_group_barrier (reads PD
+// fragments ahead, each MFMA slot with its share of the softmax) measured
+// 2.4 % slower on the 35050-token joint attention.
 template <int HD, int QB, bool NEXT, bool MASK_NEXT>
 __device__ __forceinline__ void tile_step(const char* __restrict__ lk_next,
                                           const char* __restrict__ lv_cur, const FragAddr<HD>& fa,
@@ -298,32 +298,6 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ lk_next,
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += ls[qb];
-    if (NEXT && !MASK_NEXT) {
-        // Pin the interleave of the hot step for the instruction scheduler
-        // (groups are filled in program order): LDS fragment reads run PD
-        // fragments ahead, and each MFMA slot carries its share of the softmax.
-        sched_group(kSchedDsRead, PD);
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                sched_group(kSchedMfma, 1);
-                if (qb == 0 && i + PD < NF) sched_group(kSchedDsRead, 1);
-                sched_group(kSchedValu, EP / 2 + EP);   // fma x EP + cvt x EP/2
-                sched_group(kSchedTrans, EP);           // exp x EP
-            }
-        }
-        sched_group(kSchedDsRead, PD);
-#pragma unroll
-        for (int i = 0; i < NF; ++i) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                sched_group(kSchedMfma, 1);
-                if (qb == 0 && i + PD < NF) sched_group(kSchedDsRead, 1);
-                sched_group(kSchedValu, DP + (EP + 1) / 2);   // dot2 + max
-            }
-        }
-    }
     if (!NEXT) return;
     if (MASK_NEXT) {
         tile_max<true, QB>(s_next, scale_log2, valid_next, mx);
