@@ -21,8 +21,12 @@ constexpr int kTileN = 64;
 // Dense bf16 attention workgroup: 256 queries, each wave holding kDenseQB
 // blocks of 32 queries (so 8 / kDenseQB waves).  Two blocks per wave halve
 // the LDS fragment reads per MFMA but need ~420 registers, i.e. one wave per
-// SIMD with the accumulators in AGPRs; on gfx950 that measured 1.5x slower
-// than one block per wave with two waves per SIMD.
+// SIMD with Q and O in AGPRs.  With the compiler placing the accumulators it
+// measured 1.5x slower than one block per wave with two waves per SIMD; with
+// Q and O pinned to AGPRs (matrix-core products in inline assembly) still
+// 1.1x slower: at the 256-VGPR limit the scheduler issues each fragment read
+// just before its product, and a lone wave per SIMD waits out every LDS
+// latency that the second wave hides here.
 constexpr int kDenseQ = 256;
 constexpr int kDenseQB = 1;
 constexpr int dense_threads(int qb) { return kDenseQ / (32 * qb) * kWave; }
