@@ -8,7 +8,8 @@ numpy so that a reader can check each step against the pages by eye:
 
   rope.py          time-shifted 3D RoPE (SkyReels-V4 pages)
   attention.py     dense softmax attention: joint, A<->V and video->text
+  attention_bwd.py log-sum-exp and gradients of (masked) softmax attention
   block_sparse.py  Prism block pooling, hybrid top-k/top-p, sparse attention
   brute.py         pure-Python loop versions used to cross-check the above
 """
-from . import rope, attention, block_sparse, brute  # noqa: F401
+from . import rope, attention, attention_bwd, block_sparse, brute  # noqa: F401
