@@ -9,7 +9,10 @@
  *                             any query set against any key set (video->text);
  *   - mmdit_av_cross_attn     bidirectional audio<->video cross-attention;
  *   - mmdit_block_sparse_attn mean-pooled block scores, hybrid top-k/top-p block
- *                             selection, attention over the selected blocks.
+ *                             selection, attention over the selected blocks;
+ *   - mmdit_joint_attn_fwd    mmdit_joint_attn that also returns the per-query
+ *                             log-sum-exp a training step keeps for the backward;
+ *   - mmdit_joint_attn_bwd    gradients of that attention with respect to q, k, v.
  *
  * Conventions shared by every call
  *   Layout     Q, K, V and O are contiguous [tokens][heads][head_dim] (head_dim
@@ -43,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 1
+#define MMDIT_ABI_VERSION 2
 #define MMDIT_MAX_SEGMENTS 16
 
 typedef enum {
@@ -61,7 +64,8 @@ typedef enum { MMDIT_SEG_VIDEO = 0, MMDIT_SEG_AUDIO = 1, MMDIT_SEG_TEXT = 2 } mm
 typedef enum {
     MMDIT_OP_JOINT_ATTN = 0,
     MMDIT_OP_AV_CROSS_ATTN = 1,
-    MMDIT_OP_BLOCK_SPARSE_ATTN = 2
+    MMDIT_OP_BLOCK_SPARSE_ATTN = 2,
+    MMDIT_OP_JOINT_ATTN_BWD = 3
 } mmdit_op;
 
 /* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
@@ -126,7 +130,8 @@ size_t mmdit_rope3d_table_floats(const mmdit_rope_desc* desc);
 mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* desc, float* host_table);
 
 /* Workspace bytes `op` needs for these sizes (0 if none).  JOINT_ATTN: n_q, n_kv
- * as in mmdit_joint_attn.  AV_CROSS_ATTN: n_q = n_video, n_kv = n_audio.
+ * as in mmdit_joint_attn (also for mmdit_joint_attn_fwd).  JOINT_ATTN_BWD: as
+ * in mmdit_joint_attn_bwd.  AV_CROSS_ATTN: n_q = n_video, n_kv = n_audio.
  * BLOCK_SPARSE_ATTN: n_q = n_kv = T*H*W and `sp` gives the block geometry. */
 size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
                              int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp);
@@ -156,6 +161,39 @@ mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const v
                               int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
                               float softmax_scale, float* o, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* mmdit_joint_attn for a training step: the same output o, plus
+ * lse [heads][n_q] fp32, the natural log of sum_j exp(softmax_scale * <q_i, k_j>)
+ * per head and query, which mmdit_joint_attn_bwd takes to rebuild the
+ * attention probabilities.  Sources: SkyReels-V4 analysis, workflow step 4
+ * (the joint model is trained with a flow-matching objective); Prism page,
+ * "Resultados" (training-step time of the attention at 2K).  Arguments and
+ * workspace as in mmdit_joint_attn; lse is caller-owned device memory,
+ * 4-byte aligned, and must not alias o or an input (may be NULL only when
+ * n_q == 0). */
+mmdit_status mmdit_joint_attn_fwd(const void* q, int64_t n_q, const void* k, const void* v,
+                                  int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  float softmax_scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Gradients of O = softmax(softmax_scale * Q K^T) V per head (sources as for
+ * mmdit_joint_attn_fwd).  With P the attention probabilities, rebuilt from q,
+ * k and lse, and d_o the gradient of the loss with respect to O:
+ *   dv = P^T d_o,  dS = P o (d_o v^T - D),  D_i = <d_o_i, o_i>,
+ *   dq = softmax_scale * dS k,  dk = softmax_scale * dS^T q.
+ * q, k, v, n_q, n_kv, heads, head_dim, dtype and softmax_scale as passed to
+ * mmdit_joint_attn_fwd; o [n_q][heads][head_dim] fp32 and lse [heads][n_q]
+ * fp32 are its outputs; d_o [n_q][heads][head_dim] in `dtype`.
+ * dq [n_q][heads][head_dim], dk and dv [n_kv][heads][head_dim] fp32, written
+ * (not accumulated), must not overlap each other or any input.  bf16: the
+ * five products on bf16 matrix cores (P and dS rounded to bf16) with fp32
+ * accumulation; fp32: fp32 throughout.  n_q == 0 gives dk = dv = 0.
+ * Deterministic: the same inputs give bitwise the same gradients.
+ * Workspace: mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_BWD, ...). */
+mmdit_status mmdit_joint_attn_bwd(const void* q, int64_t n_q, const void* k, const void* v,
+                                  int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  float softmax_scale, const float* o, const float* lse, const void* d_o,
+                                  float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* Both directions of the audio<->video cross-attention of one block.
  * Sources: SkyReels-V4 analysis, workflow step 3 and novelty 2 (bidirectional

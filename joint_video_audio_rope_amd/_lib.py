@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmmdit.so")
 MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMDIT_ERR_HIP = range(5)
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
-MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN = 0, 1, 2
+MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD = 0, 1, 2, 3
 MMDIT_MAX_SEGMENTS = 16
 
 _STATUS = {1: "MMDIT_ERR_INVALID_ARG", 2: "MMDIT_ERR_UNSUPPORTED", 3: "MMDIT_ERR_WORKSPACE",
@@ -75,6 +75,11 @@ def lib():
         L.mmdit_rope3d.argtypes = [ctypes.POINTER(RopeDesc), vp, vp, vp, i32, vp]
         L.mmdit_joint_attn.restype = i32
         L.mmdit_joint_attn.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, sz, vp]
+        L.mmdit_joint_attn_fwd.restype = i32
+        L.mmdit_joint_attn_fwd.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+        L.mmdit_joint_attn_bwd.restype = i32
+        L.mmdit_joint_attn_bwd.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
         L.mmdit_av_cross_attn.restype = i32
         L.mmdit_av_cross_attn.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i32, i32, i32, f32,
                                           vp, vp, vp, sz, vp]
@@ -221,6 +226,51 @@ def mmdit_joint_attn(q, k, v, softmax_scale=None, o=None, ws=None, stream=None):
     _check(lib().mmdit_joint_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
                                   _ptr(o), _ptr(ws), wsb, _stream(stream)))
     return o
+
+
+def mmdit_joint_attn_fwd(q, k, v, softmax_scale=None, o=None, lse=None, ws=None, stream=None):
+    """mmdit_joint_attn plus the log-sum-exp: returns (o fp32 [n_q, h, d],
+    lse fp32 [h, n_q], natural log)."""
+    n_q, h, d = q.shape
+    n_kv = k.shape[0]
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if o is None:
+        o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((h, n_q), dtype=torch.float32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_joint_attn_fwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
+                                      _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(stream)))
+    return o, lse
+
+
+def mmdit_joint_attn_bwd(q, k, v, o, lse, d_o, softmax_scale=None, dq=None, dk=None, dv=None, ws=None,
+                         stream=None):
+    """Gradients (dq, dk, dv), fp32, of the attention that mmdit_joint_attn_fwd
+    computed as (o, lse); d_o has the dtype of q."""
+    n_q, h, d = q.shape
+    n_kv = k.shape[0]
+    for t in (q, k, v, o, lse, d_o):
+        assert t.is_contiguous()
+    assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype == d_o.dtype
+    assert o.shape == d_o.shape == (n_q, h, d) and o.dtype == torch.float32
+    assert lse.shape == (h, n_q) and lse.dtype == torch.float32
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if dq is None:
+        dq = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_BWD, n_q, n_kv, h, d, _dtype(q))
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_joint_attn_bwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
+                                      _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                      wsb, _stream(stream)))
+    return dq, dk, dv
 
 
 def mmdit_av_cross_attn(q_v, k_v, v_v, q_a, k_a, v_a, softmax_scale=None, o_video=None,

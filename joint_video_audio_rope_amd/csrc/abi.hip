@@ -92,6 +92,9 @@ mmdit_status check_attn_args(const void* q, int64_t n_q, const void* k, const vo
     const int64_t lim = (int64_t)1 << 31;
     if (n_q * heads >= lim || n_kv * heads >= lim)
         return fail(MMDIT_ERR_UNSUPPORTED, "%s: tokens * heads must stay below 2^31", who);
+    // per-lane byte offsets into the [heads][head_dim][tokens] operands are 32-bit
+    if (n_q >= ((int64_t)1 << 24) || n_kv >= ((int64_t)1 << 24))
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: at most 2^24 - 1 tokens per side", who);
     if (!k || !v) return fail(MMDIT_ERR_INVALID_ARG, "%s: null k or v", who);
     if (!aligned16(k) || !aligned16(v))
         return fail(MMDIT_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", who);
@@ -111,13 +114,13 @@ mmdit_status check_attn_args(const void* q, int64_t n_q, const void* k, const vo
 
 // Enqueue one attention after its arguments and workspace were checked.
 mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, int64_t n_kv,
-                      int heads, int hd, int dtype, float scale, float* o, char* ws,
+                      int heads, int hd, int dtype, float scale, float* o, float* lse, char* ws,
                       const AttnPlan& p, hipStream_t s, const char* who) {
     if (n_q == 0) return MMDIT_OK;
     hipError_t e;
     if (dtype == MMDIT_FP32) {
         e = launch_attn_fp32((const float*)q, n_q, (const float*)k, (const float*)v, n_kv, heads,
-                             hd, scale, o, s);
+                             hd, scale, o, lse, s);
         return e == hipSuccess ? MMDIT_OK : hip_fail(e, who);
     }
     AttnArgs a{};
@@ -125,6 +128,7 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
     a.k = (const __bf16*)k;
     a.vt = (const _Float16*)ws;
     a.o = o;
+    a.lse = lse;
     a.part_o = p.splits > 1 ? (float*)(ws + p.vt_bytes) : nullptr;
     a.part_ml = p.splits > 1 ? (float*)(ws + p.vt_bytes + p.part_o_bytes) : nullptr;
     a.n_q = n_q;
@@ -146,6 +150,38 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
         if (e != hipSuccess) return hip_fail(e, who);
     }
     return MMDIT_OK;
+}
+
+// ---- dense attention backward plan -------------------------------------------------
+struct BwdPlan {
+    int64_t n_q_pad = 0, n_kv_pad = 0;
+    size_t off_dd = 0, off_ls2 = 0, off_qt = 0, off_dot = 0, off_kt = 0, total = 0;
+};
+
+// bf16: D and lse2 [heads][n_q_pad] fp32, Q^T and dO^T [heads][hd][n_q_pad] and
+// K^T [heads][hd][n_kv_pad] bf16 (pads: multiples of 64).  fp32: D [heads][n_q].
+BwdPlan plan_bwd(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
+    BwdPlan p;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    if (dtype == MMDIT_FP32) {
+        p.n_q_pad = n_q;
+        p.off_dd = take((size_t)heads * n_q * 4);
+    } else {
+        p.n_q_pad = round_up(n_q, kTileN);
+        p.n_kv_pad = round_up(n_kv, kTileN);
+        p.off_dd = take((size_t)heads * p.n_q_pad * 4);
+        p.off_ls2 = take((size_t)heads * p.n_q_pad * 4);
+        p.off_qt = take((size_t)heads * hd * p.n_q_pad * 2);
+        p.off_dot = take((size_t)heads * hd * p.n_q_pad * 2);
+        p.off_kt = take((size_t)heads * hd * p.n_kv_pad * 2);
+    }
+    p.total = off;
+    return p;
 }
 
 // ---- RoPE ----------------------------------------------------------------------
@@ -360,6 +396,10 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
         return plan_attn(n_q, n_kv, heads, head_dim, dtype).total() +
                plan_attn(n_kv, n_q, heads, head_dim, dtype).total();
     }
+    if (op == MMDIT_OP_JOINT_ATTN_BWD) {
+        if (n_kv < 1) return 0;
+        return plan_bwd(n_q, n_kv, heads, head_dim, dtype).total;
+    }
     if (op == MMDIT_OP_BLOCK_SPARSE_ATTN) {
         if (!sp) return 0;
         // T, H, W are not known here; the layout depends on them only through nb.
@@ -394,8 +434,105 @@ mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const v
     if (st != MMDIT_OK) return st;
     const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
     if (n_q > 0 && (st = check_ws(ws, ws_bytes, p.total(), "joint_attn")) != MMDIT_OK) return st;
-    return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, (char*)ws, p,
+    return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, nullptr, (char*)ws, p,
                     (hipStream_t)stream, "joint_attn");
+}
+
+mmdit_status mmdit_joint_attn_fwd(const void* q, int64_t n_q, const void* k, const void* v,
+                                  int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  float softmax_scale, float* o, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    mmdit_status st = check_attn_args(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale,
+                                      o, "joint_attn_fwd");
+    if (st != MMDIT_OK) return st;
+    if (n_q > 0) {
+        if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+            return fail(MMDIT_ERR_INVALID_ARG, "joint_attn_fwd: lse must be a 4-byte aligned pointer");
+        const size_t lb = (size_t)n_q * heads * 4, es = elem_size(dtype);
+        if (overlaps(lse, lb, o, (size_t)n_q * heads * head_dim * 4) ||
+            overlaps(lse, lb, q, (size_t)n_q * heads * head_dim * es) ||
+            overlaps(lse, lb, k, (size_t)n_kv * heads * head_dim * es) ||
+            overlaps(lse, lb, v, (size_t)n_kv * heads * head_dim * es))
+            return fail(MMDIT_ERR_INVALID_ARG, "joint_attn_fwd: lse aliases o or an input");
+    }
+    const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
+    if (n_q > 0 && (st = check_ws(ws, ws_bytes, p.total(), "joint_attn_fwd")) != MMDIT_OK) return st;
+    return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, lse, (char*)ws, p,
+                    (hipStream_t)stream, "joint_attn_fwd");
+}
+
+mmdit_status mmdit_joint_attn_bwd(const void* q, int64_t n_q, const void* k, const void* v,
+                                  int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                                  float softmax_scale, const float* o, const float* lse, const void* d_o,
+                                  float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+    const char* who = "joint_attn_bwd";
+    mmdit_status st = check_attn_args(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, dq, who);
+    if (st != MMDIT_OK) return st;
+    if (!dk || !dv || !aligned16(dk) || !aligned16(dv))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: dk and dv must be non-null and 16-byte aligned", who);
+    const size_t es = elem_size(dtype);
+    const size_t qb = (size_t)n_q * heads * head_dim, kb = (size_t)n_kv * heads * head_dim;
+    if (n_q > 0) {
+        if (!o || !d_o || !aligned16(o) || !aligned16(d_o))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: o and d_o must be non-null and 16-byte aligned", who);
+        if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: lse must be a 4-byte aligned pointer", who);
+    }
+    // outputs against each other and against every input
+    const void* outs[3] = {dq, dk, dv};
+    const size_t osz[3] = {qb * 4, kb * 4, kb * 4};
+    const void* ins[6] = {q, k, v, o, lse, d_o};
+    const size_t isz[6] = {qb * es, kb * es, kb * es, qb * 4, (size_t)n_q * heads * 4, qb * es};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i] || osz[i] == 0) continue;
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[j] && overlaps(outs[i], osz[i], outs[j], osz[j]))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: dq, dk and dv must not overlap", who);
+        for (int j = 0; j < 6; ++j)
+            if (ins[j] && isz[j] && overlaps(outs[i], osz[i], ins[j], isz[j]))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: a gradient aliases an input", who);
+    }
+    const BwdPlan p = plan_bwd(n_q, n_kv, heads, head_dim, dtype);
+    if ((st = check_ws(ws, ws_bytes, p.total, who)) != MMDIT_OK) return st;
+    char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    float* dd = (float*)(w + p.off_dd);
+    if (dtype == MMDIT_FP32) {
+        if ((e = launch_bwd_rowterm(o, d_o, dtype, lse, n_q, n_q, heads, head_dim, dd, nullptr, s)) != hipSuccess)
+            return hip_fail(e, who);
+        e = launch_bwd_fp32((const float*)q, (const float*)k, (const float*)v, (const float*)d_o, lse, dd, n_q,
+                            n_kv, heads, head_dim, softmax_scale, dq, dk, dv, s);
+        return e == hipSuccess ? MMDIT_OK : hip_fail(e, who);
+    }
+    BwdArgs a{};
+    a.q = (const __bf16*)q;
+    a.k = (const __bf16*)k;
+    a.v = (const __bf16*)v;
+    a.d_o = (const __bf16*)d_o;
+    a.qt = (const __bf16*)(w + p.off_qt);
+    a.dot = (const __bf16*)(w + p.off_dot);
+    a.kt = (const __bf16*)(w + p.off_kt);
+    a.ls2 = (const float*)(w + p.off_ls2);
+    a.dd = dd;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.n_q_pad = p.n_q_pad;
+    a.n_kv_pad = p.n_kv_pad;
+    a.heads = heads;
+    a.scale = softmax_scale;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    if ((e = launch_bwd_rowterm(o, d_o, dtype, lse, n_q, p.n_q_pad, heads, head_dim, dd, (float*)a.ls2, s)) !=
+            hipSuccess ||
+        (e = launch_transpose(a.q, n_q, p.n_q_pad, heads, head_dim, (__bf16*)a.qt, s)) != hipSuccess ||
+        (e = launch_transpose(a.d_o, n_q, p.n_q_pad, heads, head_dim, (__bf16*)a.dot, s)) != hipSuccess ||
+        (e = launch_transpose(a.k, n_kv, p.n_kv_pad, heads, head_dim, (__bf16*)a.kt, s)) != hipSuccess ||
+        (e = launch_bwd_dkdv(a, head_dim, s)) != hipSuccess || (e = launch_bwd_dq(a, head_dim, s)) != hipSuccess)
+        return hip_fail(e, who);
+    return MMDIT_OK;
 }
 
 mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v_v,
@@ -429,10 +566,10 @@ mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v
         return st;
     char* w = (char*)ws;
     st = run_attn(q_v, n_video, k_a, v_a, n_audio, heads, head_dim, dtype, softmax_scale, o_video,
-                  w, pva, (hipStream_t)stream, "av_cross_attn (video->audio)");
+                  nullptr, w, pva, (hipStream_t)stream, "av_cross_attn (video->audio)");
     if (st != MMDIT_OK) return st;
     return run_attn(q_a, n_audio, k_v, v_v, n_video, heads, head_dim, dtype, softmax_scale,
-                    o_audio, w ? w + pva.total() : nullptr, pav, (hipStream_t)stream,
+                    o_audio, nullptr, w ? w + pva.total() : nullptr, pav, (hipStream_t)stream,
                     "av_cross_attn (audio->video)");
 }
 

@@ -212,6 +212,9 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
         if (qrow >= a.n_q) continue;
         if (a.splits == 1) {
             store_o<HD>(a.o + qrow * rstride + head * HD, st.o[qb], 1.f / l_tot);
+            // log-sum-exp of the scaled logits, natural log: the reference
+            // maximum and the running sum are in the exp2 domain
+            if (a.lse && hh == 0) a.lse[(int64_t)head * a.n_q + qrow] = (st.m_run[qb] + log2f(l_tot)) * kLn2;
         } else {
             const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
             store_o<HD>(a.part_o + prow * HD, st.o[qb], 1.f);
@@ -247,6 +250,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const float inv = 1.f / den;
     *reinterpret_cast<float4*>(a.o + (q * a.heads + head) * HD + c4 * 4) =
         make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    if (a.lse && c4 == 0) a.lse[(int64_t)head * a.n_q + q] = (M + log2f(den)) * kLn2;
 }
 
 // fp32 path: one lane per (query, head), keys walked in order with an online
@@ -255,7 +259,8 @@ template <int HD>
 __global__ __launch_bounds__(64) void attn_fp32_kernel(const float* __restrict__ q, int64_t n_q,
                                                        const float* __restrict__ k,
                                                        const float* __restrict__ v, int64_t n_kv,
-                                                       int heads, float scale, float* __restrict__ o) {
+                                                       int heads, float scale, float* __restrict__ o,
+                                                       float* __restrict__ lse) {
     const int head = blockIdx.y;
     const int64_t qi = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (qi >= n_q) return;
@@ -285,6 +290,7 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(const float* __restrict__
     const float inv = 1.f / l;
 #pragma unroll
     for (int d = 0; d < HD; ++d) o[qi * rs + head * HD + d] = acc[d] * inv;
+    if (lse) lse[(int64_t)head * n_q + qi] = mr + logf(l);
 }
 
 }  // namespace
@@ -321,15 +327,15 @@ hipError_t launch_attn_combine(const AttnArgs& a, int hd, hipStream_t s) {
 }
 
 hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const float* v,
-                            int64_t n_kv, int heads, int hd, float scale, float* o,
+                            int64_t n_kv, int heads, int hd, float scale, float* o, float* lse,
                             hipStream_t s) {
     dim3 grid((unsigned)((n_q + 63) / 64), (unsigned)heads);
     if (hd == 128)
         hipLaunchKernelGGL(attn_fp32_kernel<128>, grid, dim3(64), 0, s, q, n_q, k, v, n_kv, heads,
-                           scale, o);
+                           scale, o, lse);
     else
         hipLaunchKernelGGL(attn_fp32_kernel<64>, grid, dim3(64), 0, s, q, n_q, k, v, n_kv, heads,
-                           scale, o);
+                           scale, o, lse);
     return hipGetLastError();
 }
 

@@ -14,6 +14,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+
 // Threads per 64-lane wavefront on CDNA.
 constexpr int kWave = 64;
 // Keys per K/V tile of the attention kernels.
@@ -64,6 +67,7 @@ struct AttnArgs {
     float* o;              // [n_q][heads][hd], used when splits == 1
     float* part_o;         // [splits][heads][n_q_pad][hd], splits > 1
     float* part_ml;        // [splits][heads][n_q_pad][2]
+    float* lse;            // [heads][n_q] natural-log log-sum-exp, or null
     int64_t n_q, n_kv, n_pad, n_q_pad;
     int32_t heads;
     int32_t q_tiles;       // ceil(n_q / kDenseQ)
@@ -77,8 +81,49 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, int hd, hipStream_t s);
 
 hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const float* v,
-                            int64_t n_kv, int heads, int hd, float scale, float* o,
+                            int64_t n_kv, int heads, int hd, float scale, float* o, float* lse,
                             hipStream_t s);
+
+// ---- dense attention backward --------------------------------------------------
+// dK/dV workgroup: kBwdKvWaves waves of 32 keys, one wave per SIMD (each holds
+// its keys' K and V rows and fp32 dK^T, dV^T accumulators: ~300 registers).
+constexpr int kBwdKvWaves = 4;
+constexpr int kBwdKvKeys = 32 * kBwdKvWaves;
+// dQ workgroup: kBwdDqWaves waves of 32 queries, two waves per SIMD.
+constexpr int kBwdDqWaves = 8;
+constexpr int kBwdDqQueries = 32 * kBwdDqWaves;
+
+struct BwdArgs {
+    const __bf16* q;       // [n_q][heads][hd]
+    const __bf16* k;       // [n_kv][heads][hd]
+    const __bf16* v;
+    const __bf16* d_o;     // [n_q][heads][hd]
+    const __bf16* qt;      // [heads][hd][n_q_pad]
+    const __bf16* dot;     // [heads][hd][n_q_pad]
+    const __bf16* kt;      // [heads][hd][n_kv_pad]
+    const float* ls2;      // [heads][n_q_pad] lse * log2(e), +inf past n_q
+    const float* dd;       // [heads][n_q_pad] <dO_i, O_i>, 0 past n_q
+    float* dq;             // [n_q][heads][hd]
+    float* dk;             // [n_kv][heads][hd]
+    float* dv;
+    int64_t n_q, n_kv, n_q_pad, n_kv_pad;   // pads: multiples of 64
+    int32_t heads;
+    float scale;           // softmax scale
+    float scale_log2;      // softmax scale * log2(e)
+};
+
+// D = <dO, O> (and, when ls2 is not null, lse * log2(e)) per (head, query),
+// written [heads][n_q_pad] with D = 0 and +inf past n_q.
+hipError_t launch_bwd_rowterm(const float* o, const void* d_o, int dtype, const float* lse, int64_t n_q,
+                              int64_t n_q_pad, int heads, int hd, float* dd, float* ls2, hipStream_t s);
+// [n][heads][hd] bf16 -> [heads][hd][n_pad] bf16, zero past n.
+hipError_t launch_transpose(const __bf16* src, int64_t n, int64_t n_pad, int heads, int hd, __bf16* dst,
+                            hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int hd, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int hd, hipStream_t s);
+hipError_t launch_bwd_fp32(const float* q, const float* k, const float* v, const float* d_o, const float* lse,
+                           const float* dd, int64_t n_q, int64_t n_kv, int heads, int hd, float scale, float* dq,
+                           float* dk, float* dv, hipStream_t s);
 
 // ---- block sparse -------------------------------------------------------------
 struct SparseGeom {

@@ -105,3 +105,31 @@ def row_dot(o, d_o):
     because O_i = sum_j P_ij v_j)."""
     o64, g64 = np.asarray(o, dtype=np.float64), np.asarray(d_o, dtype=np.float64)
     return np.einsum("qhd,qhd->hq", o64, g64)
+
+
+def key_rows_grads(q, k, v, d_o, keys, heads, scale=None, chunk=2048):
+    """dK and dV rows of the listed keys for the listed heads (fp64), each
+    [len(keys), len(heads), d], from the same definitions as attention_bwd.
+
+    A key's gradient needs every query's probabilities, so each query's
+    log-sum-exp and D_i = sum_j P_ij dP_ij are formed over all keys first,
+    in chunks of `chunk` query rows (the full score matrix never exists).
+    """
+    q64, k64, v64, g64 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, d_o))
+    nq, _, d = q64.shape
+    s = _scale(d, scale)
+    keys = np.asarray(keys)
+    dk = np.zeros((len(keys), len(heads), d))
+    dv = np.zeros((len(keys), len(heads), v64.shape[2]))
+    for hi, hd in enumerate(heads):
+        kh, vh = k64[:, hd], v64[:, hd]
+        for r0 in range(0, nq, chunk):
+            qh, gh = q64[r0:r0 + chunk, hd], g64[r0:r0 + chunk, hd]
+            p, _ = _probs(qh, kh, s, None)
+            dd = (p * (gh @ vh.T)).sum(axis=1, keepdims=True)
+            pk = p[:, keys]                               # [rows, len(keys)]
+            dpk = gh @ vh[keys].T
+            dsk = pk * (dpk - dd)
+            dv[:, hi] += pk.T @ gh
+            dk[:, hi] += s * (dsk.T @ qh)
+    return dk, dv

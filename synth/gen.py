@@ -113,6 +113,28 @@ def sparse_inputs(w, device="cpu"):
     return out
 
 
+def normal_tensors(shapes, seed, dtype="bf16", device="cpu", scale=1.0):
+    """One seeded generator, N(0, scale^2) fp32 tensors of the given shapes in
+    order, each rounded to `dtype` by round-to-nearest-even."""
+    g = _gen(seed, device)
+    dt = _DTYPES[dtype]
+    out = []
+    for shape in shapes:
+        x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(float(scale))
+        out.append(x.to(dt).contiguous())
+    return out
+
+
+def upstream_grad(w, device="cpu"):
+    """dO of a backward pass over a workload's joint sequence: N(0, 1) entries
+    [N, heads, head_dim] from a generator seeded with the workload's seed +
+    7919 (a stream separate from Q, K, V), rounded to the workload dtype."""
+    shape = (n_tokens(w), w["heads"], w["head_dim"])
+    return normal_tensors([shape], int(w["seed"]) + 7919, w["dtype"], device)[0]
+
+
 def segment_sizes(w):
     """Token counts per modality (re-exported for callers)."""
     return layout_counts(w)

@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
+              "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
               "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
         assert n in names
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert J.mmdit_abi_version() == 1
+    assert J.mmdit_abi_version() == 2
     assert isinstance(J.mmdit_last_error(), str)
 
 
@@ -121,6 +122,54 @@ def test_joint_attn_rejects_bad_arguments(over, status):
     # fake, never-dereferenced addresses: validation fails before any HIP call
     assert _call_joint(**over) == status
     assert J.mmdit_last_error() != ""
+
+
+def _call_bwd(**over):
+    # q, k, v, d_o: 10 x 2 x 64 bf16 = 2560 B; o, dq, dk, dv: 5120 B; lse: 80 B
+    a = dict(q=1 << 20, n_q=10, k=2 << 20, v=3 << 20, n_kv=10, heads=2, hd=64, dtype=J.MMDIT_BF16,
+             scale=0.125, o=4 << 20, lse=5 << 20, d_o=6 << 20, dq=7 << 20, dk=8 << 20, dv=9 << 20,
+             ws=1 << 30, ws_bytes=1 << 28)
+    a.update(over)
+    return J.lib().mmdit_joint_attn_bwd(a["q"], a["n_q"], a["k"], a["v"], a["n_kv"], a["heads"], a["hd"],
+                                        a["dtype"], a["scale"], a["o"], a["lse"], a["d_o"], a["dq"], a["dk"],
+                                        a["dv"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hd=96), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(n_kv=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dk=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dv=(9 << 20) + 8), L.MMDIT_ERR_INVALID_ARG),          # misaligned
+    (dict(lse=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(d_o=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dk=(7 << 20) + 2048), L.MMDIT_ERR_INVALID_ARG),      # dk overlaps dq
+    (dict(dv=(6 << 20) + 1024), L.MMDIT_ERR_INVALID_ARG),      # dv overlaps d_o
+    (dict(dq=(5 << 20) - 1024), L.MMDIT_ERR_INVALID_ARG),      # dq overlaps lse
+    (dict(n_q=1 << 24), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(ws_bytes=100), L.MMDIT_ERR_WORKSPACE),
+])
+def test_joint_attn_bwd_rejects_bad_arguments(over, status):
+    assert _call_bwd(**over) == status
+    assert J.mmdit_last_error() != ""
+
+
+def test_joint_attn_fwd_rejects_bad_lse():
+    lib = J.lib()
+    args = [1 << 20, 10, 2 << 20, 3 << 20, 10, 2, 64, J.MMDIT_BF16, 0.125, 4 << 20]
+    assert lib.mmdit_joint_attn_fwd(*args, 0, 1 << 30, 1 << 28, None) == L.MMDIT_ERR_INVALID_ARG
+    assert lib.mmdit_joint_attn_fwd(*args, (5 << 20) + 2, 1 << 30, 1 << 28, None) == L.MMDIT_ERR_INVALID_ARG
+    assert lib.mmdit_joint_attn_fwd(*args, (4 << 20) + 64, 1 << 30, 1 << 28, None) == L.MMDIT_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_plan():
+    ws = J.mmdit_workspace_bytes
+    n = 35050
+    pad = 35072
+    a256 = lambda x: (x + 255) // 256 * 256
+    want = 2 * a256(24 * pad * 4) + 3 * a256(24 * 128 * pad * 2)
+    assert ws(J.MMDIT_OP_JOINT_ATTN_BWD, n, n, 24, 128, J.MMDIT_BF16) == want
+    assert ws(J.MMDIT_OP_JOINT_ATTN_BWD, 88, 88, 2, 64, J.MMDIT_FP32) == a256(2 * 88 * 4)
+    assert ws(J.MMDIT_OP_JOINT_ATTN_BWD, 0, 64, 2, 64, J.MMDIT_BF16) == a256(2 * 64 * 64 * 2)
 
 
 def test_rope_rejects_bad_descriptors():

@@ -1,0 +1,139 @@
+"""GPU parity of the training calls: mmdit_joint_attn_fwd (output and
+log-sum-exp) and mmdit_joint_attn_bwd (dq, dk, dv) against the fp64 oracle
+(oracle.attention_bwd), which forms the gradients from q, k, v and dO alone.
+
+Tolerances: the stated floating-point bars, max-abs 2e-2 for bf16 inputs with
+fp32 outputs and 1e-4 for the fp32 path.  Because a gradient tensor can be
+small in magnitude, the bf16 cases also bound the error relative to the
+largest reference entry: P and dS are rounded to bf16 (relative 2^-9) before
+the products and the sums run in fp32, so 1e-2 of the largest entry leaves a
+margin of several times the rounding.  The log-sum-exp: the forward sums the
+fp16-rounded probabilities (relative 2^-11 each), so 2e-3 absolute."""
+import numpy as np
+import pytest
+import torch
+
+import joint_video_audio_rope_amd as J
+from oracle import attention_bwd as AB
+from synth import WORKLOADS, joint_inputs, normal_tensors, upstream_grad
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_BF16, REL_BF16, TOL_FP32, TOL_LSE = 2e-2, 1e-2, 1e-4, 2e-3
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def check(name, got, ref, tol, rel=None):
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    peak = float(np.max(np.abs(ref))) if ref.size else 0.0
+    print("%s: max-abs %.3e, max |ref| %.3e" % (name, err, peak), flush=True)
+    assert err <= tol, (name, err)
+    if rel is not None:
+        assert err <= rel * max(peak, 1e-30), (name, err, peak)
+
+
+def run(q, k, v, g, scale=None):
+    o, lse = J.mmdit_joint_attn_fwd(q, k, v, softmax_scale=scale)
+    dq, dk, dv = J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("nq,nk,h,d", [
+    (300, 333, 3, 128),    # several 64-query / 64-key tiles, ragged tails on both sides
+    (130, 70, 2, 64),      # head_dim 64
+    (64, 64, 1, 128),      # exactly one tile
+    (1, 5, 1, 128),        # one query, fewer keys than a tile
+    (257, 1000, 2, 128),   # one query past a 256-query dQ workgroup
+    (520, 129, 2, 128),    # keys one past a 128-key dK/dV workgroup
+])
+def test_bwd_bf16_matches_oracle(nq, nk, h, d):
+    q, k, v, g = normal_tensors([(nq, h, d), (nk, h, d), (nk, h, d), (nq, h, d)], seed=nq * 7 + nk, device=DEV)
+    o, lse, dq, dk, dv = run(q, k, v, g)
+    qq, kk, vv, gg = f64(q), f64(k), f64(v), f64(g)
+    o_ref, lse_ref = AB.attention_fwd_lse(qq, kk, vv)
+    check("o", f64(o), o_ref, TOL_BF16)
+    check("lse", f64(lse), lse_ref, TOL_LSE)
+    rq, rk, rv = AB.attention_bwd(qq, kk, vv, gg)
+    check("dq", f64(dq), rq, TOL_BF16, REL_BF16)
+    check("dk", f64(dk), rk, TOL_BF16, REL_BF16)
+    check("dv", f64(dv), rv, TOL_BF16, REL_BF16)
+
+
+def test_bwd_bf16_explicit_scale():
+    q, k, v, g = normal_tensors([(200, 2, 128), (150, 2, 128), (150, 2, 128), (200, 2, 128)], seed=11, device=DEV)
+    o, lse, dq, dk, dv = run(q, k, v, g, scale=0.05)
+    qq, kk, vv, gg = f64(q), f64(k), f64(v), f64(g)
+    check("lse", f64(lse), AB.attention_fwd_lse(qq, kk, vv, scale=0.05)[1], TOL_LSE)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), AB.attention_bwd(qq, kk, vv, gg, scale=0.05)):
+        check(name, f64(got), ref, TOL_BF16, REL_BF16)
+
+
+@pytest.mark.parametrize("shape", [(88, 88, 2, 64), (200, 150, 2, 128)])
+def test_bwd_fp32_matches_oracle(shape):
+    nq, nk, h, d = shape
+    q, k, v, g = normal_tensors([(nq, h, d), (nk, h, d), (nk, h, d), (nq, h, d)], seed=5, dtype="fp32", device=DEV)
+    o, lse, dq, dk, dv = run(q, k, v, g)
+    qq, kk, vv, gg = f64(q), f64(k), f64(v), f64(g)
+    o_ref, lse_ref = AB.attention_fwd_lse(qq, kk, vv)
+    check("o", f64(o), o_ref, TOL_FP32)
+    check("lse", f64(lse), lse_ref, TOL_FP32)
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), AB.attention_bwd(qq, kk, vv, gg)):
+        check(name, f64(got), ref, TOL_FP32)
+
+
+def test_bwd_tiny_workload_fp32():
+    w = WORKLOADS["tiny"]
+    x = joint_inputs(w, DEV)
+    g = upstream_grad(w, DEV)
+    o, lse, dq, dk, dv = run(x["q"], x["k"], x["v"], g)
+    ref = AB.attention_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g))
+    for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check(name, f64(got), r, TOL_FP32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_without_queries_gives_zero_key_gradients(dtype):
+    q, k, v, g = normal_tensors([(0, 2, 64), (70, 2, 64), (70, 2, 64), (0, 2, 64)], seed=3, dtype=dtype, device=DEV)
+    o = torch.empty((0, 2, 64), dtype=torch.float32, device=DEV)
+    lse = torch.empty((2, 0), dtype=torch.float32, device=DEV)
+    dk = torch.full((70, 2, 64), 7.0, device=DEV)
+    dv = torch.full((70, 2, 64), 7.0, device=DEV)
+    J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def test_bwd_repeat_is_bitwise_identical():
+    q, k, v, g = normal_tensors([(700, 3, 128), (650, 3, 128), (650, 3, 128), (700, 3, 128)], seed=9, device=DEV)
+    _, _, dq1, dk1, dv1 = run(q, k, v, g)
+    _, _, dq2, dk2, dv2 = run(q, k, v, g)
+    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+
+
+def test_bwd_joint_480p_sampled():
+    """The full 480p-latent joint sequence (35050 tokens, 24 x 128) in the
+    launch configuration the bench times: dq on sampled queries of every head,
+    dk and dv on sampled keys of two heads (their queries' log-sum-exp and D
+    formed over all keys by the oracle), and sum_j dv_j = sum_i dO_i over
+    every head."""
+    w = WORKLOADS["480p"]
+    x = joint_inputs(w, DEV)
+    g = upstream_grad(w, DEV)
+    o, lse, dq, dk, dv = run(x["q"], x["k"], x["v"], g)
+    n = x["q"].shape[0]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, n - 1, 34319, 34320], rng.choice(n, 8, replace=False)]))
+    qq, kk, vv, gg = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g)
+    rq, _, _ = AB.attention_bwd(qq[rows], kk, vv, gg[rows])
+    check("dq rows", f64(dq)[rows], rq, TOL_BF16, REL_BF16)
+    keys = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 6, replace=False)]))
+    heads = [0, 23]
+    rk, rv = AB.key_rows_grads(qq, kk, vv, gg, keys, heads)
+    check("dk rows", f64(dk)[keys][:, heads], rk, TOL_BF16, REL_BF16)
+    check("dv rows", f64(dv)[keys][:, heads], rv, TOL_BF16, REL_BF16)
+    sums = dv.double().sum(dim=0).cpu().numpy()
+    check("sum dv", sums, gg.sum(axis=0), 0.5, 1e-3)

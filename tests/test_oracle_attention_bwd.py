@@ -123,3 +123,12 @@ def test_lse_matches_scipy_and_brute_force():
         tot = sum(math.exp(0.3 * float(np.dot(q[i, hd], k[j, hd])) - lse[hd, i]) for j in range(37))
         assert abs(tot - 1.0) < 1e-12
     assert np.max(np.abs(o - A.attention(q, k, v, scale=0.3))) < 1e-12
+
+
+def test_key_rows_match_full_gradients():
+    q, k, v, g = _rand((300, 2, 16), 25), _rand((200, 2, 16), 26), _rand((200, 2, 16), 27), _rand((300, 2, 16), 28)
+    _, dk, dv = B.attention_bwd(q, k, v, g, scale=0.4)
+    keys = [0, 5, 199]
+    dk2, dv2 = B.key_rows_grads(q, k, v, g, keys, [1], scale=0.4, chunk=70)
+    assert np.max(np.abs(dk2[:, 0] - dk[keys, 1])) < 1e-13
+    assert np.max(np.abs(dv2[:, 0] - dv[keys, 1])) < 1e-13
