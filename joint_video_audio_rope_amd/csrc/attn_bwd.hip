@@ -17,20 +17,22 @@
 //   transpose    bf16 Q^T, dO^T [heads][hd][n_q_pad] and K^T [heads][hd][n_kv_pad]
 //                (zero padded), the k-contiguous operands of the products
 //                that contract over tokens;
-//   bwd_dkdv     a workgroup owns 128 keys (4 waves of 32, one wave per SIMD,
-//                each wave's K and V rows held in registers) and streams the
-//                queries in 64-query tiles: S = Q K^T and dP = dO V^T with the
-//                queries as MFMA rows, permuted within each 32-row half as in
-//                the forward so that every lane's P and dS registers come out
-//                as the 8 consecutive queries the next products take; then
-//                dV^T += dO^T P and dK^T += Q^T dS, whose accumulators store
-//                like the forward's O^T (one key per lane, d along registers);
+//   bwd_key      a workgroup owns 256 keys (8 waves of 32, each wave's K (and
+//                V) rows held in registers) and streams the queries in
+//                64-query tiles: S = Q K^T (and dP = dO V^T) with the queries
+//                as MFMA rows, permuted within each 32-row half as in the
+//                forward so that every lane's P (dS) registers come out as the
+//                8 consecutive queries the next product takes; then dV^T +=
+//                dO^T P in one pass and dK^T += Q^T dS in a second, whose
+//                accumulators store like the forward's O^T (one key per lane,
+//                d along registers);
 //   bwd_dq       a workgroup owns 256 queries (8 waves of 32, Q and dO rows in
 //                registers) and streams the keys in 64-key tiles: S^T = K Q^T,
 //                dP^T = V dO^T, dQ^T += K^T dS^T.
-// dQ is not summed inside bwd_dkdv: that takes fp32 atomics on dQ from every
-// key tile.  The query-owned pass recomputes S and dP instead (7 products per
-// (query, key) block instead of 5), and every result is deterministic.
+// dQ is not summed in the key-owned passes: that takes fp32 atomics on dQ
+// from every key tile.  The query-owned pass recomputes S and dP instead (8
+// products per (query, key) block against the 5 of the definition), and
+// every result is deterministic.
 #include "attn_core.hpp"
 
 namespace mmdit {
@@ -109,18 +111,28 @@ __device__ __forceinline__ int xcd_logical(int total) {
     return (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
 }
 
-template <int HD>
-__global__ __launch_bounds__(kBwdKvWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdArgs a) {
+// Key-owned pass.  DK = false: S = Q K^T -> P -> dV^T += dO^T P.  DK = true:
+// S = Q K^T and dP = dO V^T -> dS -> dK^T += Q^T dS.  Two passes at two waves
+// per SIMD (each wave holds one fp32 accumulator block set) instead of one
+// pass at one wave per SIMD: the fused pass needs K, V, dK^T and dV^T in
+// registers (~380), and with four waves a 64-query tile brought only half
+// the matrix-core work per copied byte of the forward, so the waves waited on
+// the copies; the split recomputes S once more.
+template <int HD, bool DK>
+__global__ __launch_bounds__(kBwdKvWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_key_kernel(BwdArgs a) {
     using L = TileLayout<HD>;
     constexpr int NW = kBwdKvWaves;
     constexpr int KS = HD / 16;
     constexpr int DB = HD / 32;
-    constexpr int CK = kTileN * L::kKChunks / (kWave * NW);   // copies per wave of a Q or dO tile
-    constexpr int CV = HD * 8 / (kWave * NW);                 // copies per wave of a Q^T or dO^T tile
+    constexpr int CK = kTileN * L::kKChunks / (kWave * NW);   // copies per wave of a row-major tile
+    constexpr int CV = HD * 8 / (kWave * NW);                 // copies per wave of a transposed tile
     static_assert(NW >= 2 && CK >= 1 && CV >= 1, "tile copies");
-    // one buffer: Q tile | dO tile | Q^T tile | dO^T tile | lse2[64] | D[64]
-    constexpr int kBuf = 2 * L::kKBytes + 2 * L::kVBytes + 2 * kTileN * 4;
+    // one buffer: Q | [dO] | (DK ? Q^T : dO^T) | lse2[64] | [D[64]]
+    constexpr int kRow = DK ? 2 : 1;                           // row-major tiles
+    constexpr int kOffT = kRow * L::kKBytes;                   // the transposed tile
+    constexpr int kOffL = kOffT + L::kVBytes;                  // lse2, then D
+    constexpr int kBuf = kOffL + (DK ? 2 : 1) * kTileN * 4;
     __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
 
     const int kv_tiles = (int)((a.n_kv + kBwdKvKeys - 1) / kBwdKvKeys);
@@ -141,11 +153,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // wave's 32-key block), and its 8 d values per k-step
     const int64_t key = (int64_t)kt * kBwdKvKeys + w * 32 + m;
     const bool kok = key < a.n_kv;
-    bf16x8 kr[KS], vr[KS];
+    bf16x8 kr[KS], vr[DK ? KS : 1];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         kr[ks] = load_bf16x8(a.k + key * rstride + head * HD + 16 * ks + 8 * hh, kok);
-        vr[ks] = load_bf16x8(a.v + key * rstride + head * HD + 16 * ks + 8 * hh, kok);
+        if (DK) vr[ks] = load_bf16x8(a.v + key * rstride + head * HD + 16 * ks + 8 * hh, kok);
     }
 
     auto q_slot = [&](int i, int& qrow, int& c) {
@@ -169,8 +181,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
     const char* qg = reinterpret_cast<const char*>(a.q + head * HD);
     const char* og = reinterpret_cast<const char*>(a.d_o + head * HD);
-    const char* qtg = reinterpret_cast<const char*>(a.qt + (int64_t)head * HD * a.n_q_pad);
-    const char* otg = reinterpret_cast<const char*>(a.dot + (int64_t)head * HD * a.n_q_pad);
+    const char* tg = reinterpret_cast<const char*>((DK ? a.qt : a.dot) + (int64_t)head * HD * a.n_q_pad);
     const float* lsg = a.ls2 + (int64_t)head * a.n_q_pad;
     const float* ddg = a.dd + (int64_t)head * a.n_q_pad;
 
@@ -181,7 +192,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < CK; ++i) {
                 dma16(qg + q0 * rb + roff[i], b + (w * CK + i) * 1024);
-                dma16(og + q0 * rb + roff[i], b + L::kKBytes + (w * CK + i) * 1024);
+                if (DK) dma16(og + q0 * rb + roff[i], b + L::kKBytes + (w * CK + i) * 1024);
             }
         } else {   // rows past n_q re-read the last real row; their P is 0 (lse2 = +inf)
             const int last = (int)(a.n_q - q0) - 1;
@@ -191,26 +202,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
                 q_slot(i, r, c);
                 const int64_t off = (q0 + min(r, last)) * rb + c * 16;
                 dma16(qg + off, b + (w * CK + i) * 1024);
-                dma16(og + off, b + L::kKBytes + (w * CK + i) * 1024);
+                if (DK) dma16(og + off, b + L::kKBytes + (w * CK + i) * 1024);
             }
         }
 #pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            dma16(qtg + q0 * 2 + toff[i], b + 2 * L::kKBytes + (w * CV + i) * 1024);
-            dma16(otg + q0 * 2 + toff[i], b + 2 * L::kKBytes + L::kVBytes + (w * CV + i) * 1024);
-        }
-        char* lb = b + 2 * L::kKBytes + 2 * L::kVBytes;
-        if (w == 0) dma4(lsg + q0 + lane, lb);
-        if (w == 1) dma4(ddg + q0 + lane, lb + kTileN * 4);
+        for (int i = 0; i < CV; ++i) dma16(tg + q0 * 2 + toff[i], b + kOffT + (w * CV + i) * 1024);
+        if (w == 0) dma4(lsg + q0 + lane, b + kOffL);
+        if (DK && w == 1) dma4(ddg + q0 + lane, b + kOffL + kTileN * 4);
     };
 
     FragAddr<HD> fa;
     fa.init();
-    f32x16 dvt[DB], dkt[DB];
+    f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dvt[db][r] = dkt[db][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
     const int q_tiles = (int)(a.n_q_pad / kTileN);
     if (q_tiles > 0) {
@@ -222,9 +229,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
         if (t + 1 < q_tiles) issue(t + 1, buf(t + 1));
         const char* lq = buf(t);
         const char* lo = lq + L::kKBytes;
-        const char* lqt = lq + 2 * L::kKBytes;
-        const char* lot = lqt + L::kVBytes;
-        const float* lls = reinterpret_cast<const float*>(lot + L::kVBytes);
+        const char* lt = lq + kOffT;
+        const float* lls = reinterpret_cast<const float*>(lq + kOffL);
         const float* ldd = lls + kTileN;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -234,44 +240,45 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lq, fa, 2 * ks + qb), kr[ks], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lo, fa, 2 * ks + qb), vr[ks], dp, 0, 0, 0);
+                if (DK)
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lo, fa, 2 * ks + qb), vr[ks], dp, 0, 0, 0);
             }
             // register r holds query 32 qb + 16 (r / 8) + 8 hh + r % 8 of the tile
-            float lsv[16], ddv[16];
+            bf16x8 xb[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int h4 = 0; h4 < 2; ++h4) {
                     const int qi = 32 * qb + 16 * j + 8 * hh + 4 * h4;
                     const float4 x = *reinterpret_cast<const float4*>(lls + qi);
-                    const float4 y = *reinterpret_cast<const float4*>(ldd + qi);
-                    const int r0 = 8 * j + 4 * h4;
-                    lsv[r0] = x.x, lsv[r0 + 1] = x.y, lsv[r0 + 2] = x.z, lsv[r0 + 3] = x.w;
-                    ddv[r0] = y.x, ddv[r0 + 1] = y.y, ddv[r0 + 2] = y.z, ddv[r0 + 3] = y.w;
-                }
-            bf16x8 pb[2], sb[2];
+                    const float lsv[4] = {x.x, x.y, x.z, x.w};
+                    float ddv[4] = {0.f, 0.f, 0.f, 0.f};
+                    if (DK) {
+                        const float4 y = *reinterpret_cast<const float4*>(ldd + qi);
+                        ddv[0] = y.x, ddv[1] = y.y, ddv[2] = y.z, ddv[3] = y.w;
+                    }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -lsv[r]));
-                pb[r >> 3][r & 7] = (__bf16)p;
-                sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - ddv[r]));
-            }
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 8 * j + 4 * h4 + e;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -lsv[e]));
+                        xb[j][4 * h4 + e] = (__bf16)(DK ? p * (dp[r] - ddv[e]) : p);
+                    }
+                }
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag<HD>(lot, fa, 4 * db + 2 * qb + g), pb[g],
-                                                                      dvt[db], 0, 0, 0);
-                    dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag<HD>(lqt, fa, 4 * db + 2 * qb + g), sb[g],
-                                                                      dkt[db], 0, 0, 0);
-                }
+                for (int g = 0; g < 2; ++g)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag<HD>(lt, fa, 4 * db + 2 * qb + g), xb[g],
+                                                                      acc[db], 0, 0, 0);
         }
         wait_dma();
         __syncthreads();
     }
     if (!kok) return;
-    store_o<HD>(a.dv + key * rstride + head * HD, dvt, 1.f);
-    store_o<HD>(a.dk + key * rstride + head * HD, dkt, a.scale);
+    if (DK)
+        store_o<HD>(a.dk + key * rstride + head * HD, acc, a.scale);
+    else
+        store_o<HD>(a.dv + key * rstride + head * HD, acc, 1.f);
 }
 
 template <int HD>
@@ -531,10 +538,14 @@ hipError_t launch_transpose(const __bf16* src, int64_t n, int64_t n_pad, int hea
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int hd, hipStream_t s) {
     const int64_t kv_tiles = (a.n_kv + kBwdKvKeys - 1) / kBwdKvKeys;
     const unsigned blocks = (unsigned)((kv_tiles * a.heads + 7) / 8 * 8);
-    if (hd == 128)
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(blocks), dim3(kBwdKvWaves * kWave), 0, s, a);
-    else
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(blocks), dim3(kBwdKvWaves * kWave), 0, s, a);
+    const dim3 grid(blocks), block(kBwdKvWaves * kWave);
+    if (hd == 128) {
+        hipLaunchKernelGGL((bwd_key_kernel<128, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((bwd_key_kernel<128, true>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_key_kernel<64, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((bwd_key_kernel<64, true>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

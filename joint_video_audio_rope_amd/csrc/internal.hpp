@@ -85,9 +85,8 @@ hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const f
                             hipStream_t s);
 
 // ---- dense attention backward --------------------------------------------------
-// dK/dV workgroup: kBwdKvWaves waves of 32 keys, one wave per SIMD (each holds
-// its keys' K and V rows and fp32 dK^T, dV^T accumulators: ~300 registers).
-constexpr int kBwdKvWaves = 4;
+// dK and dV workgroups: kBwdKvWaves waves of 32 keys, two waves per SIMD.
+constexpr int kBwdKvWaves = 8;
 constexpr int kBwdKvKeys = 32 * kBwdKvWaves;
 // dQ workgroup: kBwdDqWaves waves of 32 queries, two waves per SIMD.
 constexpr int kBwdDqWaves = 8;
