@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse leg")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the training leg (joint attention forward with lse + backward)")
     ap.add_argument("--sparse-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
@@ -278,6 +280,9 @@ def main():
     }
 
     del o_vt, o_va, o_av, ws_vt, ws_av
+    if not args.no_train:
+        out["train"] = train_leg(args, torch, J, w, q, k, v, dev)
+        print("[bench] training leg: %s" % out["train"], file=sys.stderr, flush=True)
     if not args.no_sparse:
         out["block_sparse"] = sparse_leg(args, torch, J, WORKLOADS["sparse2k"], sparse_inputs, dev)
         print("[bench] block sparse: %s" % out["block_sparse"], file=sys.stderr, flush=True)
@@ -286,6 +291,51 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, torch, q, k, v)
         print("[bench] cpu baseline: %s" % out["cpu_baseline"], file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
+
+
+def train_leg(args, torch, J, w, q, k, v, dev):
+    """Joint attention of a training step on the same 480p-latent tensors:
+    forward with the log-sum-exp, then the backward for a seeded dO."""
+    from synth import upstream_grad
+
+    n, h, d = q.shape
+    g = upstream_grad(w, dev)
+    o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws_f = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN_BWD, n, n, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        J.mmdit_joint_attn_fwd(q, k, v, o=o, lse=lse, ws=ws_f, stream=stream)
+
+    def bwd():
+        J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, dq=dq, dk=dk, dv=dv, ws=ws_b, stream=stream)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_f = timed(fwd, 5)
+    t_b = timed(bwd, 5)
+    fl_f = attn_flops(n, n, h, d)
+    fl_b = 2.5 * fl_f          # five products of 2*N^2*d per head
+    return {"workload": "joint self-attention of the 480p-latent layer (35050 tokens, 24 x 128), "
+                        "seeded N(0,1) dO",
+            "fwd_lse_ms": round(t_f, 3), "bwd_ms": round(t_b, 3),
+            "bwd_tflops": round(fl_b / t_b * 1e-9, 1),
+            "fwd_bwd_tflops": round((fl_f + fl_b) / (t_f + t_b) * 1e-9, 1),
+            "flop_convention": "fwd 4*N^2*d*h, bwd 10*N^2*d*h"}
 
 
 def sparse_leg(args, torch, J, w, sparse_inputs, dev):
