@@ -12,7 +12,9 @@
  *                             selection, attention over the selected blocks;
  *   - mmdit_joint_attn_fwd    mmdit_joint_attn that also returns the per-query
  *                             log-sum-exp a training step keeps for the backward;
- *   - mmdit_joint_attn_bwd    gradients of that attention with respect to q, k, v.
+ *   - mmdit_joint_attn_bwd    gradients of that attention with respect to q, k, v;
+ *   - mmdit_block_sparse_attn_fwd / _bwd  the same pair for the block-sparse
+ *                             attention (selection held fixed in the backward).
  *
  * Conventions shared by every call
  *   Layout     Q, K, V and O are contiguous [tokens][heads][head_dim] (head_dim
@@ -65,7 +67,8 @@ typedef enum {
     MMDIT_OP_JOINT_ATTN = 0,
     MMDIT_OP_AV_CROSS_ATTN = 1,
     MMDIT_OP_BLOCK_SPARSE_ATTN = 2,
-    MMDIT_OP_JOINT_ATTN_BWD = 3
+    MMDIT_OP_JOINT_ATTN_BWD = 3,
+    MMDIT_OP_BLOCK_SPARSE_ATTN_BWD = 4
 } mmdit_op;
 
 /* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
@@ -132,7 +135,8 @@ mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* desc, float* host_t
 /* Workspace bytes `op` needs for these sizes (0 if none).  JOINT_ATTN: n_q, n_kv
  * as in mmdit_joint_attn (also for mmdit_joint_attn_fwd).  JOINT_ATTN_BWD: as
  * in mmdit_joint_attn_bwd.  AV_CROSS_ATTN: n_q = n_video, n_kv = n_audio.
- * BLOCK_SPARSE_ATTN: n_q = n_kv = T*H*W and `sp` gives the block geometry. */
+ * BLOCK_SPARSE_ATTN and BLOCK_SPARSE_ATTN_BWD: n_q = n_kv = T*H*W and `sp`
+ * gives the block geometry. */
 size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
                              int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp);
 
@@ -229,6 +233,38 @@ mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v
                                      const mmdit_sparse_desc* sp, double softmax_scale, float* o,
                                      uint32_t* sel_mask, int32_t* sel_count, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/* mmdit_block_sparse_attn for a training step: the same o and selection, plus
+ * lse [heads][T*H*W] fp32, the natural log of sum_j exp(softmax_scale *
+ * <q_i, k_j>) over the keys of the query's selected blocks.  Sources: Prism
+ * page, "Metodo" section 3 (attention over S_i only) and "Resultados"
+ * (training-step time of the sparse attention at 2K).  sel_mask is required
+ * here: mmdit_block_sparse_attn_bwd takes it.  Other arguments and workspace
+ * as in mmdit_block_sparse_attn; lse is 4-byte aligned and aliases nothing. */
+mmdit_status mmdit_block_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                         int32_t W, int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp,
+                                         double softmax_scale, float* o, float* lse, uint32_t* sel_mask,
+                                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of the block-sparse attention with its selection held fixed (the
+ * selection is piecewise constant in q and k): for every query i and key j of
+ * a selected block pair, P_ij = exp(softmax_scale * <q_i, k_j> - lse_i), and
+ * with D_i = <d_o_i, o_i>:
+ *   dv_j = sum_i P_ij d_o_i,   dS_ij = P_ij (<d_o_i, v_j> - D_i),
+ *   dq_i = softmax_scale * sum_j dS_ij k_j,  dk_j = softmax_scale * sum_i dS_ij q_i,
+ * sums over the selected pairs only.  Sources as for
+ * mmdit_block_sparse_attn_fwd.  q, k, v, T, H, W, heads, head_dim, sp (its
+ * zone and block geometry) and softmax_scale as passed to the forward; o,
+ * lse and sel_mask are its outputs; d_o [T*H*W][heads][head_dim] bf16.  dq,
+ * dk, dv [T*H*W][heads][head_dim] fp32, written (not accumulated), 16-byte
+ * aligned, must not overlap each other or any input.  bf16 products with
+ * fp32 accumulation; deterministic.  Workspace:
+ * mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, ...). */
+mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                         int32_t W, int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp,
+                                         double softmax_scale, const float* o, const float* lse, const void* d_o,
+                                         const uint32_t* sel_mask, float* dq, float* dk, float* dv, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmmdit.so")
 MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMDIT_ERR_HIP = range(5)
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
-MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD = 0, 1, 2, 3
+(MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,
+ MMDIT_OP_BLOCK_SPARSE_ATTN_BWD) = range(5)
 MMDIT_MAX_SEGMENTS = 16
 
 _STATUS = {1: "MMDIT_ERR_INVALID_ARG", 2: "MMDIT_ERR_UNSUPPORTED", 3: "MMDIT_ERR_WORKSPACE",
@@ -86,6 +87,12 @@ def lib():
         L.mmdit_block_sparse_attn.restype = i32
         L.mmdit_block_sparse_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32,
                                               ctypes.POINTER(SparseDesc), f64, vp, vp, vp, vp, sz, vp]
+        L.mmdit_block_sparse_attn_fwd.restype = i32
+        L.mmdit_block_sparse_attn_fwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(SparseDesc),
+                                                  f64, vp, vp, vp, vp, vp, sz, vp]
+        L.mmdit_block_sparse_attn_bwd.restype = i32
+        L.mmdit_block_sparse_attn_bwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(SparseDesc),
+                                                  f64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -327,3 +334,53 @@ def mmdit_block_sparse_attn(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4), t
                                          ctypes.byref(sd), scale, _ptr(o), _ptr(sel_mask),
                                          _ptr(sel_count), _ptr(ws), wsb, _stream(stream)))
     return o, sel_mask, sel_count
+
+
+def mmdit_block_sparse_attn_fwd(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9,
+                                softmax_scale=None, o=None, lse=None, sel_mask=None, sel_count=None, ws=None,
+                                stream=None):
+    """Block-sparse attention for a training step: (o fp32, lse fp32 [h, n],
+    sel_mask, sel_count); sel_mask feeds mmdit_block_sparse_attn_bwd."""
+    n, h, d = q.shape
+    assert n == T * H * W and q.dtype == torch.bfloat16
+    sd = sparse_desc(zone, block, top_k, top_p)
+    nb = n // (block[0] * block[1] * block[2])
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
+    if sel_mask is None:
+        sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+    if sel_count is None:
+        sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd), scale,
+                                             _ptr(o), _ptr(lse), _ptr(sel_mask), _ptr(sel_count), _ptr(ws), wsb,
+                                             _stream(stream)))
+    return o, lse, sel_mask, sel_count
+
+
+def mmdit_block_sparse_attn_bwd(q, k, v, o, lse, d_o, sel_mask, T, H, W, zone=(8, 8, 8), block=(4, 4, 4),
+                                softmax_scale=None, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Gradients (dq, dk, dv), fp32, of the block-sparse attention whose
+    forward returned (o, lse, sel_mask); the selection is held fixed."""
+    n, h, d = q.shape
+    assert n == T * H * W and q.dtype == k.dtype == v.dtype == d_o.dtype == torch.bfloat16
+    for t in (q, k, v, o, lse, d_o, sel_mask):
+        assert t.is_contiguous()
+    sd = sparse_desc(zone, block, 0, 1.0)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if dq is None:
+        dq = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, d, MMDIT_BF16, sd)
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd), scale,
+                                             _ptr(o), _ptr(lse), _ptr(d_o), _ptr(sel_mask), _ptr(dq), _ptr(dk),
+                                             _ptr(dv), _ptr(ws), wsb, _stream(stream)))
+    return dq, dk, dv

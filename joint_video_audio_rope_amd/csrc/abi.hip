@@ -342,6 +342,83 @@ mmdit_status check_ws(const void* ws, size_t ws_bytes, size_t need, const char* 
     return MMDIT_OK;
 }
 
+mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, int32_t H, int32_t W,
+                        int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp, double softmax_scale,
+                        float* o, float* lse, uint32_t* sel_mask, int32_t* sel_count, void* ws, size_t ws_bytes,
+                        void* stream, const char* who) {
+    SparsePlan p{};
+    mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
+    if (st != MMDIT_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "%s: null q, k, v or o", who);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", who);
+    if ((sel_mask && !aligned16(sel_mask)) || (sel_count && (reinterpret_cast<uintptr_t>(sel_count) & 3u)))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: misaligned sel_mask or sel_count", who);
+    const size_t n = (size_t)T * H * W;
+    const size_t ib = n * heads * head_dim * 2, ob = n * heads * head_dim * 4;
+    if (overlaps(o, ob, q, ib) || overlaps(o, ob, k, ib) || overlaps(o, ob, v, ib))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: output aliases an input", who);
+    if (lse) {
+        const size_t lb = n * heads * 4;
+        if (overlaps(lse, lb, o, ob) || overlaps(lse, lb, q, ib) || overlaps(lse, lb, k, ib) ||
+            overlaps(lse, lb, v, ib))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: lse aliases o or an input", who);
+    }
+    if ((st = check_ws(ws, ws_bytes, p.total, who)) != MMDIT_OK) return st;
+    char* w = (char*)ws;
+    SparseWs sw{};
+    sw.qbar = (double*)(w + p.off_qbar);
+    sw.kbar = (double*)(w + p.off_kbar);
+    sw.scores = (double*)(w + p.off_scores);
+    sw.mask = (uint32_t*)(w + p.off_mask);
+    sw.count = (int32_t*)(w + p.off_count);
+    sw.base = (int32_t*)(w + p.off_base);
+    sw.vt = (_Float16*)(w + p.off_vt);
+    sw.kimg = (__bf16*)(w + p.off_kimg);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse pool");
+    if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse vt");
+    if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse scores");
+    if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, sel_mask, sel_count, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse select");
+    if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
+                                (float)(softmax_scale * 1.4426950408889634), sw, o, lse, s)) !=
+        hipSuccess)
+        return hip_fail(e, "block_sparse attention");
+    return MMDIT_OK;
+}
+
+// Workspace of a block-sparse backward: D and lse2 [heads][n] fp32, the
+// transposed block images Q^T, dO^T, K^T [heads][nb][hd * 64] bf16, and the
+// transposed selection bitmask [heads][nb][ceil(nb/32)].
+struct SparseBwdPlan {
+    size_t off_dd, off_ls2, off_qt, off_dot, off_kt, off_maskt, total;
+};
+
+SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) {
+    SparseBwdPlan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    p.off_dd = take((size_t)heads * n * 4);
+    p.off_ls2 = take((size_t)heads * n * 4);
+    p.off_qt = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_dot = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_kt = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_maskt = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
+    p.total = off;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -399,6 +476,10 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
     if (op == MMDIT_OP_JOINT_ATTN_BWD) {
         if (n_kv < 1) return 0;
         return plan_bwd(n_q, n_kv, heads, head_dim, dtype).total;
+    }
+    if (op == MMDIT_OP_BLOCK_SPARSE_ATTN_BWD) {
+        if (!sp) return 0;
+        return plan_sparse_bwd(n_q, n_q / kTileN, heads, head_dim).total;
     }
     if (op == MMDIT_OP_BLOCK_SPARSE_ATTN) {
         if (!sp) return 0;
@@ -578,45 +659,87 @@ mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v
                                      const mmdit_sparse_desc* sp, double softmax_scale, float* o,
                                      uint32_t* sel_mask, int32_t* sel_count, void* ws,
                                      size_t ws_bytes, void* stream) {
+    return run_sparse(q, k, v, T, H, W, heads, head_dim, sp, softmax_scale, o, nullptr, sel_mask, sel_count, ws,
+                      ws_bytes, stream, "block_sparse");
+}
+
+mmdit_status mmdit_block_sparse_attn_fwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                         int32_t W, int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp,
+                                         double softmax_scale, float* o, float* lse, uint32_t* sel_mask,
+                                         int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+    if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse_fwd: lse must be a 4-byte aligned pointer");
+    if (!sel_mask)
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse_fwd: sel_mask is required (the backward takes it)");
+    return run_sparse(q, k, v, T, H, W, heads, head_dim, sp, softmax_scale, o, lse, sel_mask, sel_count, ws,
+                      ws_bytes, stream, "block_sparse_fwd");
+}
+
+mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                         int32_t W, int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp,
+                                         double softmax_scale, const float* o, const float* lse, const void* d_o,
+                                         const uint32_t* sel_mask, float* dq, float* dk, float* dv, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    const char* who = "block_sparse_bwd";
     SparsePlan p{};
     mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
     if (st != MMDIT_OK) return st;
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
-        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: softmax_scale must be positive and finite");
-    if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: null q, k, v or o");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: q, k, v, o must be 16-byte aligned");
-    if ((sel_mask && !aligned16(sel_mask)) || (sel_count && (reinterpret_cast<uintptr_t>(sel_count) & 3u)))
-        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: misaligned sel_mask or sel_count");
-    const size_t n = (size_t)T * H * W;
-    const size_t ib = n * heads * head_dim * 2, ob = n * heads * head_dim * 4;
-    if (overlaps(o, ob, q, ib) || overlaps(o, ob, k, ib) || overlaps(o, ob, v, ib))
-        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: output aliases an input");
-    if ((st = check_ws(ws, ws_bytes, p.total, "block_sparse")) != MMDIT_OK) return st;
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    const void* al16[8] = {q, k, v, o, d_o, dq, dk, dv};
+    for (const void* ptr : al16)
+        if (!ptr || !aligned16(ptr))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: q, k, v, o, d_o, dq, dk, dv must be non-null and 16-byte aligned",
+                        who);
+    if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u) || !sel_mask ||
+        (reinterpret_cast<uintptr_t>(sel_mask) & 3u))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: lse and sel_mask must be non-null and 4-byte aligned", who);
+    const int64_t n = (int64_t)T * H * W;
+    const int64_t nb = p.g.nb, nw = (nb + 31) / 32;
+    const size_t ib = (size_t)n * heads * head_dim * 2, fb = (size_t)n * heads * head_dim * 4;
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[6] = {q, k, v, o, lse, d_o};
+    const size_t isz[6] = {ib, ib, ib, fb, (size_t)n * heads * 4, ib};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], fb, outs[j], fb))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: dq, dk and dv must not overlap", who);
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], fb, ins[j], isz[j]))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: a gradient aliases an input", who);
+        if (overlaps(outs[i], fb, sel_mask, (size_t)heads * nb * nw * 4))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: a gradient aliases sel_mask", who);
+    }
+    const SparseBwdPlan bp = plan_sparse_bwd(n, nb, heads, head_dim);
+    if ((st = check_ws(ws, ws_bytes, bp.total, who)) != MMDIT_OK) return st;
     char* w = (char*)ws;
-    SparseWs sw{};
-    sw.qbar = (double*)(w + p.off_qbar);
-    sw.kbar = (double*)(w + p.off_kbar);
-    sw.scores = (double*)(w + p.off_scores);
-    sw.mask = (uint32_t*)(w + p.off_mask);
-    sw.count = (int32_t*)(w + p.off_count);
-    sw.base = (int32_t*)(w + p.off_base);
-    sw.vt = (_Float16*)(w + p.off_vt);
-    sw.kimg = (__bf16*)(w + p.off_kimg);
+    SparseBwdArgs a{};
+    a.q = (const __bf16*)q;
+    a.k = (const __bf16*)k;
+    a.v = (const __bf16*)v;
+    a.d_o = (const __bf16*)d_o;
+    a.qt_img = (const __bf16*)(w + bp.off_qt);
+    a.dot_img = (const __bf16*)(w + bp.off_dot);
+    a.kt_img = (const __bf16*)(w + bp.off_kt);
+    a.mask = sel_mask;
+    a.maskt = (const uint32_t*)(w + bp.off_maskt);
+    a.ls2 = (const float*)(w + bp.off_ls2);
+    a.dd = (const float*)(w + bp.off_dd);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = (float)softmax_scale;
+    a.scale_log2 = (float)(softmax_scale * 1.4426950408889634);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse pool");
-    if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse vt");
-    if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse scores");
-    if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, sel_mask, sel_count, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse select");
-    if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
-                                (float)(softmax_scale * 1.4426950408889634), sw, o, s)) !=
-        hipSuccess)
-        return hip_fail(e, "block_sparse attention");
+    if ((e = launch_bwd_rowterm(o, d_o, MMDIT_BF16, lse, n, n, heads, head_dim, (float*)a.dd, (float*)a.ls2, s)) !=
+            hipSuccess ||
+        (e = launch_block_timg(p.g, a.q, (__bf16*)a.qt_img, s)) != hipSuccess ||
+        (e = launch_block_timg(p.g, a.d_o, (__bf16*)a.dot_img, s)) != hipSuccess ||
+        (e = launch_block_timg(p.g, a.k, (__bf16*)a.kt_img, s)) != hipSuccess ||
+        (e = launch_mask_transpose(p.g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
+        (e = launch_sparse_bwd(p.g, a, s)) != hipSuccess)
+        return hip_fail(e, who);
     return MMDIT_OK;
 }
 

@@ -155,7 +155,34 @@ hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const 
 hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s);
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
-                              float scale_log2, const SparseWs& w, float* o, hipStream_t s);
+                              float scale_log2, const SparseWs& w, float* o, float* lse, hipStream_t s);
+
+// Largest number of blocks per head (selection rows staged in LDS).
+constexpr int kSelMax = 4096;
+
+// ---- block-sparse backward ------------------------------------------------------
+struct SparseBwdArgs {
+    const __bf16* q;         // [n][heads][hd] raster tokens
+    const __bf16* k;
+    const __bf16* v;
+    const __bf16* d_o;
+    const __bf16* qt_img;    // [heads][nb][hd * 64] transposed block images
+    const __bf16* dot_img;
+    const __bf16* kt_img;
+    const uint32_t* mask;    // [heads][nb][ceil(nb/32)] query block -> selected key blocks
+    const uint32_t* maskt;   // [heads][nb][ceil(nb/32)] key block -> query blocks that selected it
+    const float* ls2;        // [heads][n] lse * log2(e)
+    const float* dd;         // [heads][n] <dO_i, O_i>
+    float* dq;               // [n][heads][hd]
+    float* dk;
+    float* dv;
+    float scale;
+    float scale_log2;
+};
+
+hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, hipStream_t s);
+hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint32_t* maskt, hipStream_t s);
+hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s);
 
 // Token index (raster t, h, w) of local token r (0..63, raster inside the
 // 4x4x4 block) of block j.

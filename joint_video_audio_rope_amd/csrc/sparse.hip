@@ -173,7 +173,6 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
 }
 
 constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup
-constexpr int kSelMax = 4096;   // largest row (blocks per head)
 // Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
 // Measured on the 24 x 64 x 112 grid (density 27.6 %): a group stages on
 // average 0.73 (pairs), 0.62 (triples), 0.50 (4 blocks) of the tiles its
@@ -433,7 +432,7 @@ __device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken) {
 template <int HD, int G, int R>
 __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_kernel(
         SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-        SparseWs w, float* __restrict__ o) {
+        SparseWs w, float* __restrict__ o, float* __restrict__ lse) {
     using L = TileLayout<HD>;
     constexpr int NC = 2 * G;                          // consumer waves; wave NC produces
     constexpr int KS = HD / 16;
@@ -586,6 +585,10 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     if (b0 + side >= g.nb) return;
     const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
     store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
+    // log-sum-exp over the selected keys, natural log (reference maximum and
+    // running sum are in the exp2 domain)
+    if (lse && hh == 0)
+        lse[(int64_t)head * ((int64_t)g.T * g.H * g.W) + qtok] = (st.m_run[0] + log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -634,12 +637,12 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 }
 
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
-                              float scale_log2, const SparseWs& w, float* o, hipStream_t s) {
+                              float scale_log2, const SparseWs& w, float* o, float* lse, hipStream_t s) {
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
     const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
     hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 1) * kWave), 0, s, g,
-                       q, k, scale_log2, w, o);
+                       q, k, scale_log2, w, o, lse);
     return hipGetLastError();
 }
 

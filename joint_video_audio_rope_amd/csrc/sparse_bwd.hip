@@ -1,0 +1,467 @@
+// Backward pass of the block-sparse video self-attention (training).
+//
+// The Prism page ("Resultados", efficiency gains) measures the block-sparse
+// attention by the time of a training step at 2K; its "Metodo" section 3
+// defines the attention as softmax attention of each query block over the
+// key blocks of S_i only.  The selection is a piecewise-constant function of
+// Q and K, so the backward holds it fixed: the gradients are those of masked
+// softmax attention, with P_ij = exp(s <q_i, k_j> - lse_i) on the selected
+// pairs (lse_i from the sparse forward, over S_i) and 0 elsewhere.
+//
+// Passes (bf16 products, fp32 accumulation), mirroring the dense backward:
+//   block_timg   per-block transposed images Q^T, dO^T, K^T [heads][nb][hd x 64]
+//                in the LDS order of a transposed tile (the operands that
+//                contract over tokens; a block's 64 tokens are not contiguous
+//                in the raster layout, so these are staged once);
+//   mask_transpose  the selection bitmask transposed: for each key block, the
+//                query blocks that selected it;
+//   dq           a workgroup owns 4 query blocks (8 waves of 32 queries) and
+//                walks the union of their selections: S^T = K Q^T, dP^T =
+//                V dO^T, dQ^T += K^T dS^T for each selected key block;
+//   key (dV, dK) a workgroup owns 4 key blocks (8 waves of 32 keys) and walks
+//                the union of the query blocks that selected them: S = Q K^T
+//                -> P -> dV^T += dO^T P, and S, dP = dO V^T -> dS -> dK^T +=
+//                Q^T dS.
+// Row-major tiles (Q, dO, K, V rows) are gathered straight from the raster
+// layout by the copies: each lane's copy fetches the 16-byte chunk of the
+// token that belongs at its LDS position.  Walks are synchronous (one
+// workgroup barrier per tile, double-buffered copies); a wave whose block did
+// not select the tile skips its products.
+#include "attn_core.hpp"
+
+namespace mmdit {
+
+namespace {
+
+// Token offset of block-local token r (raster inside the block) from the
+// block's first token.
+__device__ __forceinline__ int block_off(const SparseGeom& g, int r) {
+    const int a = r / (g.BH * g.BW);
+    const int rr = r - a * (g.BH * g.BW);
+    const int b = rr / g.BW;
+    const int c = rr - b * g.BW;
+    return (a * g.H + b) * g.W + c;
+}
+
+// One workgroup per (block, head): the block's 64 tokens of src, transposed
+// to [HD][64] bf16 and laid out as the LDS image of a transposed tile (chunk
+// u of the image holds (d, c) = v_at(u): tokens 8c .. 8c + 7 of row d).  The
+// 16-bit values move as halves of 32-bit words.
+template <int HD>
+__global__ __launch_bounds__(256) void block_timg_kernel(SparseGeom g, const __bf16* __restrict__ src,
+                                                         __bf16* __restrict__ dst) {
+    using L = TileLayout<HD>;
+    __shared__ uint16_t tile[kTileN][HD + 2];
+    const int j = blockIdx.x, head = blockIdx.y;
+    const int64_t base = block_token(g, j, 0);
+    const int64_t rs = (int64_t)g.heads * HD;
+    constexpr int CPR = HD / 8;
+    for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
+        const int r = u / CPR, c = u % CPR;
+        const int64_t tok = base + block_off(g, r);
+        const uint4 x = *reinterpret_cast<const uint4*>(src + tok * rs + head * HD + c * 8);
+        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+    }
+    __syncthreads();
+    __bf16* out = dst + ((int64_t)head * g.nb + j) * (HD * kTileN);
+    for (int u = threadIdx.x; u < HD * (kTileN / 8); u += 256) {
+        int d, c;
+        L::v_at(u, d, c);
+        auto pair = [&](int i) { return (uint32_t)tile[c * 8 + i][d] | ((uint32_t)tile[c * 8 + i + 1][d] << 16); };
+        *reinterpret_cast<uint4*>(out + u * 8) = make_uint4(pair(0), pair(2), pair(4), pair(6));
+    }
+}
+
+// maskT[head][j][w] bit b = mask[head][32 w + b][j / 32] bit j % 32 (0 past nb).
+__global__ __launch_bounds__(256) void mask_transpose_kernel(const uint32_t* __restrict__ mask, int nb, int heads,
+                                                             uint32_t* __restrict__ maskt) {
+    const int nw = (nb + 31) >> 5;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= (int64_t)heads * nb * nw) return;
+    const int wi = (int)(id % nw);
+    const int64_t hj = id / nw;
+    const int j = (int)(hj % nb);
+    const int head = (int)(hj / nb);
+    const uint32_t* col = mask + (int64_t)head * nb * nw + (j >> 5);
+    uint32_t word = 0u;
+    for (int b = 0; b < 32; ++b) {
+        const int i = 32 * wi + b;
+        if (i >= nb) break;
+        word |= ((col[(int64_t)i * nw] >> (j & 31)) & 1u) << b;
+    }
+    maskt[id] = word;
+}
+
+constexpr int kSG = 4;   // blocks per workgroup (2 waves of 32 tokens each)
+
+// Cursor over the union of kSG bitmask rows staged in LDS (the same walk in
+// every wave; values are wave-uniform).
+struct UnionWalk {
+    const uint32_t (*rows)[kSelMax / 32];
+    int nw, word;
+    uint32_t bits;
+    __device__ uint32_t union_word(int wd) const {
+        uint32_t u = 0u;
+#pragma unroll
+        for (int sd = 0; sd < kSG; ++sd) u |= rows[sd][wd];
+        return __builtin_amdgcn_readfirstlane(u);
+    }
+    __device__ void init(const uint32_t (*r)[kSelMax / 32], int n_words) {
+        rows = r;
+        nw = n_words;
+        word = 0;
+        bits = nw > 0 ? union_word(0) : 0u;
+    }
+    __device__ int next() {
+        while (bits == 0u) {
+            if (++word >= nw) return -1;
+            bits = union_word(word);
+        }
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        return word * 32 + b;
+    }
+};
+
+__device__ __forceinline__ void dma4(const void* gp, char* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gp, MMDIT_LDS(lds_wave_base), 4, 0, 0);
+}
+
+// Copy one block's 64 rows of a [tokens][heads][HD] bf16 tensor into a
+// row-major tile (MFMA row m of each 32-row half holds block-local token
+// perm(m)); roff holds this lane's per-copy offsets from the block's first
+// token row.
+template <int CK>
+__device__ __forceinline__ void gather_rows(const char* g0, const uint32_t (&roff)[CK], char* tile, int w) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) dma16(g0 + roff[i], tile + (w * CK + i) * 1024);
+}
+
+template <int HD>
+__global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, SparseBwdArgs a) {
+    using L = TileLayout<HD>;
+    constexpr int NW = 8;
+    constexpr int KS = HD / 16;
+    constexpr int DB = HD / 32;
+    constexpr int CK = kTileN * L::kKChunks / (kWave * NW);
+    constexpr int CV = HD * 8 / (kWave * NW);
+    static_assert(CK >= 1 && CV >= 1, "tile copies");
+    constexpr int kBuf = 2 * L::kKBytes + L::kVBytes;   // K rows | V rows | K^T
+    __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+    __shared__ uint32_t msk[kSG][kSelMax / 32];
+
+    const int groups = (g.nb + kSG - 1) / kSG;
+    const int total = groups * g.heads;
+    const int per_xcd = (total + 7) >> 3;
+    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (logical >= total) return;
+    const int grp = logical % groups;
+    const int head = logical / groups;
+    const int b0 = kSG * grp;
+    const int nw = (g.nb + 31) >> 5;
+    const int64_t n = (int64_t)g.T * g.H * g.W;
+
+    const uint32_t* mrow = a.mask + ((int64_t)head * g.nb + b0) * nw;
+    for (int i = threadIdx.x; i < kSG * nw; i += NW * kWave) {
+        const int sd = i / nw, wd = i - (i / nw) * nw;
+        msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
+    }
+    __syncthreads();
+
+    const int w = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5;
+    const int m = lane & 31;
+    const int side = w >> 1;
+    const int64_t rstride = (int64_t)g.heads * HD;
+    const int64_t rb = rstride * 2;
+    const bool own_ok = b0 + side < g.nb;
+    const int qb = min(b0 + side, g.nb - 1);
+    const int64_t qtok = block_token(g, qb, 0) + block_off(g, (w & 1) * 32 + m);
+    bf16x8 qr[KS], gr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qr[ks] = load_bf16x8(a.q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
+        gr[ks] = load_bf16x8(a.d_o + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
+    }
+    const float lq2 = a.ls2[(int64_t)head * n + qtok];
+    const float dq_d = a.dd[(int64_t)head * n + qtok];
+
+    // this lane's row-tile copies: offset of the token (and chunk) it fetches
+    uint32_t roff[CK];
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+        int row, c;
+        L::k_at((w * CK + i) * kWave + lane, row, c);
+        roff[i] = (uint32_t)(block_off(g, (row & ~31) | perm_row(row & 31)) * rb + c * 16);
+    }
+    const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
+    const char* vg = reinterpret_cast<const char*>(a.v + head * HD);
+    const char* ktg = reinterpret_cast<const char*>(a.kt_img + (int64_t)head * g.nb * (HD * kTileN)) + 16 * lane;
+
+    auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
+    auto issue = [&](int j, char* b) {
+        const int64_t t0 = block_token(g, j, 0) * rb;
+        gather_rows<CK>(kg + t0, roff, b, w);
+        gather_rows<CK>(vg + t0, roff, b + L::kKBytes, w);
+        const char* src = ktg + (int64_t)j * (HD * kTileN * 2);
+#pragma unroll
+        for (int i = 0; i < CV; ++i)
+            dma16(src + (w * CV + i) * 1024, b + 2 * L::kKBytes + (w * CV + i) * 1024);
+    };
+
+    FragAddr<HD> fa;
+    fa.init();
+    f32x16 dqt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
+
+    UnionWalk walk;
+    walk.init(msk, nw);
+    int cur = walk.next();
+    if (cur >= 0) issue(cur, buf(0));
+    wait_dma();
+    __syncthreads();
+    int own_word = -1;
+    uint32_t own = 0u;
+    for (int t = 0; cur >= 0; ++t) {
+        const int nxt = walk.next();
+        if (nxt >= 0) issue(nxt, buf(t + 1));
+        if ((cur >> 5) != own_word) {
+            own_word = cur >> 5;
+            own = __builtin_amdgcn_readfirstlane(msk[side][own_word]);
+        }
+        if ((own >> (cur & 31)) & 1u) {
+            const char* lk = buf(t);
+            const char* lv = lk + L::kKBytes;
+            const char* lkt = lk + 2 * L::kKBytes;
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lk, fa, 2 * ks + kb), qr[ks], s[kb],
+                                                                    0, 0, 0);
+                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lv, fa, 2 * ks + kb), gr[ks],
+                                                                     dp[kb], 0, 0, 0);
+                }
+            }
+            bf16x8 sb[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], a.scale_log2, -lq2));
+                    sb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dq_d));
+                }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg)
+                    dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        *reinterpret_cast<const bf16x8*>(lkt + fa.v[gg] + db * 32 * L::kVRowBytes), sb[gg], dqt[db],
+                        0, 0, 0);
+        }
+        wait_dma();
+        __syncthreads();
+        cur = nxt;
+    }
+    if (!own_ok) return;
+    store_o<HD>(a.dq + qtok * rstride + head * HD, dqt, a.scale);
+}
+
+// Key-owned pass.  DK = false: S = Q K^T -> P -> dV^T += dO^T P.  DK = true:
+// S and dP = dO V^T -> dS -> dK^T += Q^T dS.
+template <int HD, bool DK>
+__global__ __launch_bounds__(8 * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
+    using L = TileLayout<HD>;
+    constexpr int NW = 8;
+    constexpr int KS = HD / 16;
+    constexpr int DB = HD / 32;
+    constexpr int CK = kTileN * L::kKChunks / (kWave * NW);
+    constexpr int CV = HD * 8 / (kWave * NW);
+    static_assert(CK >= 1 && CV >= 1, "tile copies");
+    // one buffer: Q rows | [dO rows] | (DK ? Q^T : dO^T) | lse2[64] | [D[64]]
+    constexpr int kRow = DK ? 2 : 1;
+    constexpr int kOffT = kRow * L::kKBytes;
+    constexpr int kOffL = kOffT + L::kVBytes;
+    constexpr int kBuf = kOffL + (DK ? 2 : 1) * kTileN * 4;
+    __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+    __shared__ uint32_t msk[kSG][kSelMax / 32];
+
+    const int groups = (g.nb + kSG - 1) / kSG;
+    const int total = groups * g.heads;
+    const int per_xcd = (total + 7) >> 3;
+    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (logical >= total) return;
+    const int grp = logical % groups;
+    const int head = logical / groups;
+    const int c0 = kSG * grp;
+    const int nw = (g.nb + 31) >> 5;
+    const int64_t n = (int64_t)g.T * g.H * g.W;
+
+    const uint32_t* mrow = a.maskt + ((int64_t)head * g.nb + c0) * nw;
+    for (int i = threadIdx.x; i < kSG * nw; i += NW * kWave) {
+        const int sd = i / nw, wd = i - (i / nw) * nw;
+        msk[sd][wd] = (c0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
+    }
+    __syncthreads();
+
+    const int w = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5;
+    const int m = lane & 31;
+    const int side = w >> 1;
+    const int64_t rstride = (int64_t)g.heads * HD;
+    const int64_t rb = rstride * 2;
+    const bool own_ok = c0 + side < g.nb;
+    const int kb_own = min(c0 + side, g.nb - 1);
+    const int64_t ktok = block_token(g, kb_own, 0) + block_off(g, (w & 1) * 32 + m);
+    bf16x8 kr[KS], vr[DK ? KS : 1];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kr[ks] = load_bf16x8(a.k + ktok * rstride + head * HD + 16 * ks + 8 * hh, true);
+        if (DK) vr[ks] = load_bf16x8(a.v + ktok * rstride + head * HD + 16 * ks + 8 * hh, true);
+    }
+
+    uint32_t roff[CK];
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+        int row, c;
+        L::k_at((w * CK + i) * kWave + lane, row, c);
+        roff[i] = (uint32_t)(block_off(g, (row & ~31) | perm_row(row & 31)) * rb + c * 16);
+    }
+    const int loff = block_off(g, lane);   // this lane's query of the lse / D copies
+    const char* qg = reinterpret_cast<const char*>(a.q + head * HD);
+    const char* og = reinterpret_cast<const char*>(a.d_o + head * HD);
+    const char* tg = reinterpret_cast<const char*>((DK ? a.qt_img : a.dot_img) + (int64_t)head * g.nb * (HD * kTileN)) +
+                     16 * lane;
+    const float* lsg = a.ls2 + (int64_t)head * n;
+    const float* ddg = a.dd + (int64_t)head * n;
+
+    auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
+    auto issue = [&](int i, char* b) {
+        const int64_t tok0 = block_token(g, i, 0);
+        gather_rows<CK>(qg + tok0 * rb, roff, b, w);
+        if (DK) gather_rows<CK>(og + tok0 * rb, roff, b + L::kKBytes, w);
+        const char* src = tg + (int64_t)i * (HD * kTileN * 2);
+#pragma unroll
+        for (int c = 0; c < CV; ++c) dma16(src + (w * CV + c) * 1024, b + kOffT + (w * CV + c) * 1024);
+        if (w == 0) dma4(lsg + tok0 + loff, b + kOffL);
+        if (DK && w == 1) dma4(ddg + tok0 + loff, b + kOffL + kTileN * 4);
+    };
+
+    FragAddr<HD> fa;
+    fa.init();
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    UnionWalk walk;
+    walk.init(msk, nw);
+    int cur = walk.next();
+    if (cur >= 0) issue(cur, buf(0));
+    wait_dma();
+    __syncthreads();
+    int own_word = -1;
+    uint32_t own = 0u;
+    for (int t = 0; cur >= 0; ++t) {
+        const int nxt = walk.next();
+        if (nxt >= 0) issue(nxt, buf(t + 1));
+        if ((cur >> 5) != own_word) {
+            own_word = cur >> 5;
+            own = __builtin_amdgcn_readfirstlane(msk[side][own_word]);
+        }
+        if ((own >> (cur & 31)) & 1u) {
+            const char* lq = buf(t);
+            const char* lo = lq + L::kKBytes;
+            const char* lt = lq + kOffT;
+            const float* lls = reinterpret_cast<const float*>(lq + kOffL);
+            const float* ldd = lls + kTileN;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16 s, dp;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lq, fa, 2 * ks + qb), kr[ks], s, 0, 0, 0);
+                    if (DK)
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lo, fa, 2 * ks + qb), vr[ks], dp, 0,
+                                                                     0, 0);
+                }
+                // register r holds block-local query 32 qb + 16 (r / 8) + 8 hh + r % 8
+                bf16x8 xb[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int h4 = 0; h4 < 2; ++h4) {
+                        const int qi = 32 * qb + 16 * j + 8 * hh + 4 * h4;
+                        const float4 x = *reinterpret_cast<const float4*>(lls + qi);
+                        const float lsv[4] = {x.x, x.y, x.z, x.w};
+                        float ddv[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (DK) {
+                            const float4 y = *reinterpret_cast<const float4*>(ldd + qi);
+                            ddv[0] = y.x, ddv[1] = y.y, ddv[2] = y.z, ddv[3] = y.w;
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 8 * j + 4 * h4 + e;
+                            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -lsv[e]));
+                            xb[j][4 * h4 + e] = (__bf16)(DK ? p * (dp[r] - ddv[e]) : p);
+                        }
+                    }
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            *reinterpret_cast<const bf16x8*>(lt + fa.v[2 * qb + gg] + db * 32 * L::kVRowBytes),
+                            xb[gg], acc[db], 0, 0, 0);
+            }
+        }
+        wait_dma();
+        __syncthreads();
+        cur = nxt;
+    }
+    if (!own_ok) return;
+    if (DK)
+        store_o<HD>(a.dk + ktok * rstride + head * HD, acc, a.scale);
+    else
+        store_o<HD>(a.dv + ktok * rstride + head * HD, acc, 1.f);
+}
+
+}  // namespace
+
+hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, hipStream_t s) {
+    hipLaunchKernelGGL(block_timg_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, src, dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint32_t* maskt, hipStream_t s) {
+    const int64_t words = (int64_t)g.heads * g.nb * ((g.nb + 31) / 32);
+    hipLaunchKernelGGL(mask_transpose_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s, mask, g.nb,
+                       g.heads, maskt);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s) {
+    const int groups = (g.nb + kSG - 1) / kSG;
+    const unsigned blocks = (unsigned)((groups * g.heads + 7) / 8 * 8);
+    const dim3 block(8 * kWave);
+    hipLaunchKernelGGL(sparse_bwd_dq_kernel<128>, dim3(blocks), block, 0, s, g, a);
+    hipLaunchKernelGGL((sparse_bwd_key_kernel<128, false>), dim3(blocks), block, 0, s, g, a);
+    hipLaunchKernelGGL((sparse_bwd_key_kernel<128, true>), dim3(blocks), block, 0, s, g, a);
+    return hipGetLastError();
+}
+
+}  // namespace mmdit

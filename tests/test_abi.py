@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
-              "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd",
+              "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd", "mmdit_block_sparse_attn_fwd",
+              "mmdit_block_sparse_attn_bwd",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
               "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
         assert n in names
