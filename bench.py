@@ -380,12 +380,49 @@ def sparse_leg(args, torch, J, w, sparse_inputs, dev):
     density = float(counts.mean().item() / nb)
     fl_dense = attn_flops(n, n, h, d)
     fl_sparse = 4.0 * 64 * 64 * d * float(counts.sum().item())
-    return {"workload": "video 24x64x112 (172032 tokens), 24 heads x 128, zones 8x8x8, blocks 4x4x4, "
-                        "top-k 32 + top-p 0.9, smooth-field Q/K/V",
-            "dense_ms": round(t_dense, 3), "sparse_ms": round(t_sparse, 3),
-            "speedup": round(t_dense / t_sparse, 3), "density": round(density, 4),
-            "dense_tflops": round(fl_dense / t_dense * 1e-9, 1),
-            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_sparse * 1e-9, 1)}
+    out = {"workload": "video 24x64x112 (172032 tokens), 24 heads x 128, zones 8x8x8, blocks 4x4x4, "
+                       "top-k 32 + top-p 0.9, smooth-field Q/K/V",
+           "dense_ms": round(t_dense, 3), "sparse_ms": round(t_sparse, 3),
+           "speedup": round(t_dense / t_sparse, 3), "density": round(density, 4),
+           "dense_tflops": round(fl_dense / t_dense * 1e-9, 1),
+           "sparse_attn_tflops_incl_selection": round(fl_sparse / t_sparse * 1e-9, 1)}
+    if not args.no_train:
+        out.update(sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream))
+    return out
+
+
+def sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream):
+    """Attention of a training step at the same shape: forward with the
+    log-sum-exp plus backward, dense against block-sparse."""
+    from synth import normal_tensors
+
+    T, H, W = w["T"], w["H"], w["W"]
+    n, h, d = q.shape
+    dev = q.device
+    g = normal_tensors([(n, h, d)], seed=int(w["seed"]) + 7919, device=dev)[0]
+    lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws_db = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN_BWD, n, n, h, d, J.MMDIT_BF16),
+                        dtype=torch.uint8, device=dev)
+    sd = J.sparse_desc(w["zone"], w["block"], w["top_k"], w["top_p"])
+    ws_sb = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, d, J.MMDIT_BF16, sd),
+                        dtype=torch.uint8, device=dev)
+
+    def dense_step():
+        J.mmdit_joint_attn_fwd(q, k, v, o=o, lse=lse, ws=ws_d, stream=stream)
+        J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, dq=dq, dk=dk, dv=dv, ws=ws_db, stream=stream)
+
+    def sparse_step():
+        J.mmdit_block_sparse_attn_fwd(q, k, v, T, H, W, w["zone"], w["block"], w["top_k"], w["top_p"], o=o,
+                                      lse=lse, sel_mask=mask, sel_count=cnt, ws=ws_s, stream=stream)
+        J.mmdit_block_sparse_attn_bwd(q, k, v, o, lse, g, mask, T, H, W, w["zone"], w["block"], dq=dq, dk=dk,
+                                      dv=dv, ws=ws_sb, stream=stream)
+
+    t_dense = timed(dense_step)
+    t_sparse = timed(sparse_step)
+    del ws_db, ws_sb, dq, dk, dv, g
+    return {"train_dense_ms": round(t_dense, 3), "train_sparse_ms": round(t_sparse, 3),
+            "train_speedup": round(t_dense / t_sparse, 3)}
 
 
 def cpu_baseline(args, torch, q, k, v):
