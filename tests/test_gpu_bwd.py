@@ -137,3 +137,40 @@ def test_bwd_joint_480p_sampled():
     check("dv rows", f64(dv)[keys][:, heads], rv, TOL_BF16, REL_BF16)
     sums = dv.double().sum(dim=0).cpu().numpy()
     check("sum dv", sums, gg.sum(axis=0), 0.5, 1e-3)
+
+
+def test_bwd_audio_video_480p_shapes():
+    """The cross-attention shapes of the 480p-latent layer: 218 audio queries
+    against the 34320 video-stream keys (the forward splits the key range and
+    merges the partials, so the log-sum-exp comes from the merge) and the
+    reverse direction, forward with lse and backward."""
+    w = WORKLOADS["480p"]
+    x = joint_inputs(w, DEV)
+    g = upstream_grad(w, DEV)
+    n_vs = (w["n_cond_frames"] + w["T"]) * w["H"] * w["W"]
+    a0, a1 = n_vs, n_vs + w["n_audio"]
+    q, k, v = x["q"], x["k"], x["v"]
+    # audio -> video
+    qa, ga = q[a0:a1].contiguous(), g[a0:a1].contiguous()
+    kv, vv = k[:n_vs].contiguous(), v[:n_vs].contiguous()
+    o, lse, dq, dk, dv = run(qa, kv, vv, ga)
+    qq, kk, vv64, gg = f64(qa), f64(kv), f64(vv), f64(ga)
+    o_ref, lse_ref = AB.attention_fwd_lse(qq, kk, vv64)
+    check("a->v o", f64(o), o_ref, TOL_BF16)
+    check("a->v lse", f64(lse), lse_ref, TOL_LSE)
+    rq, _, _ = AB.attention_bwd(qq, kk, vv64, gg)
+    check("a->v dq", f64(dq), rq, TOL_BF16, REL_BF16)
+    keys = np.array([0, 1, 1559, 1560, 17000, n_vs - 1])
+    rk, rv = AB.key_rows_grads(qq, kk, vv64, gg, keys, list(range(w["heads"])))
+    check("a->v dk rows", f64(dk)[keys], rk, TOL_BF16, REL_BF16)
+    check("a->v dv rows", f64(dv)[keys], rv, TOL_BF16, REL_BF16)
+    # video -> audio: sampled video queries, every audio key
+    ka, va = k[a0:a1].contiguous(), v[a0:a1].contiguous()
+    qv, gv = q[:n_vs].contiguous(), g[:n_vs].contiguous()
+    o, lse, dq, dk, dv = run(qv, ka, va, gv)
+    rows = np.array([0, 1, 777, 1560, 20000, n_vs - 1])
+    rq, _, _ = AB.attention_bwd(f64(qv)[rows], f64(ka), f64(va), f64(gv)[rows])
+    check("v->a dq rows", f64(dq)[rows], rq, TOL_BF16, REL_BF16)
+    rk, rv = AB.key_rows_grads(f64(qv), f64(ka), f64(va), f64(gv), np.arange(w["n_audio"]), [0, 11])
+    check("v->a dk", f64(dk)[:, [0, 11]], rk, TOL_BF16, REL_BF16)
+    check("v->a dv", f64(dv)[:, [0, 11]], rv, TOL_BF16, REL_BF16)
