@@ -611,7 +611,7 @@ mmdit_status mmdit_joint_attn_bwd(const void* q, int64_t n_q, const void* k, con
         (e = launch_transpose(a.q, n_q, p.n_q_pad, heads, head_dim, (__bf16*)a.qt, s)) != hipSuccess ||
         (e = launch_transpose(a.d_o, n_q, p.n_q_pad, heads, head_dim, (__bf16*)a.dot, s)) != hipSuccess ||
         (e = launch_transpose(a.k, n_kv, p.n_kv_pad, heads, head_dim, (__bf16*)a.kt, s)) != hipSuccess ||
-        (e = launch_bwd_dkdv(a, head_dim, s)) != hipSuccess || (e = launch_bwd_dq(a, head_dim, s)) != hipSuccess)
+        (e = launch_bwd_keys(a, head_dim, s)) != hipSuccess || (e = launch_bwd_dq(a, head_dim, s)) != hipSuccess)
         return hip_fail(e, who);
     return MMDIT_OK;
 }

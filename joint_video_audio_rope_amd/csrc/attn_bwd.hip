@@ -535,7 +535,7 @@ hipError_t launch_transpose(const __bf16* src, int64_t n, int64_t n_pad, int hea
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int hd, hipStream_t s) {
+hipError_t launch_bwd_keys(const BwdArgs& a, int hd, hipStream_t s) {
     const int64_t kv_tiles = (a.n_kv + kBwdKvKeys - 1) / kBwdKvKeys;
     const unsigned blocks = (unsigned)((kv_tiles * a.heads + 7) / 8 * 8);
     const dim3 grid(blocks), block(kBwdKvWaves * kWave);

@@ -118,7 +118,8 @@ hipError_t launch_bwd_rowterm(const float* o, const void* d_o, int dtype, const 
 // [n][heads][hd] bf16 -> [heads][hd][n_pad] bf16, zero past n.
 hipError_t launch_transpose(const __bf16* src, int64_t n, int64_t n_pad, int heads, int hd, __bf16* dst,
                             hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, int hd, hipStream_t s);
+// The two key-owned passes: dV, then dK.
+hipError_t launch_bwd_keys(const BwdArgs& a, int hd, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, int hd, hipStream_t s);
 hipError_t launch_bwd_fp32(const float* q, const float* k, const float* v, const float* d_o, const float* lse,
                            const float* dd, int64_t n_q, int64_t n_kv, int heads, int hd, float scale, float* dq,
