@@ -211,6 +211,55 @@ def test_block_sparse_rejects_bad_arguments(over, status):
     assert st == status
 
 
+def _sparse_bwd_call(**over):
+    # 24 x 64 x 112 grid, 24 heads: bf16 tensors 1.06 GB, fp32 tensors 2.1 GB each
+    a = dict(q=1 << 32, k=2 << 32, v=3 << 32, o=4 << 32, lse=5 << 32, d_o=6 << 32, mask=7 << 32,
+             dq=8 << 32, dk=9 << 32, dv=10 << 32, T=24, H=64, W=112, heads=24, hd=128, scale=0.088,
+             ws=1 << 40, ws_bytes=1 << 38)
+    a.update(over)
+    sd = J.sparse_desc()
+    return J.lib().mmdit_block_sparse_attn_bwd(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["heads"],
+                                               a["hd"], ctypes.byref(sd), a["scale"], a["o"], a["lse"],
+                                               a["d_o"], a["mask"], a["dq"], a["dk"], a["dv"], a["ws"],
+                                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
+    (dict(scale=-1.0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(mask=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(lse=(5 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dv=(10 << 32) + 8), L.MMDIT_ERR_INVALID_ARG),     # misaligned
+    (dict(dk=(8 << 32) + 4096), L.MMDIT_ERR_INVALID_ARG),   # dk overlaps dq
+    (dict(dq=(6 << 32) + 4096), L.MMDIT_ERR_INVALID_ARG),   # dq overlaps d_o
+    (dict(dv=(7 << 32) - 4096), L.MMDIT_ERR_INVALID_ARG),   # dv runs into the mask
+    (dict(ws_bytes=1000), L.MMDIT_ERR_WORKSPACE),
+])
+def test_block_sparse_bwd_rejects_bad_arguments(over, status):
+    assert _sparse_bwd_call(**over) == status
+    assert J.mmdit_last_error() != ""
+
+
+def test_block_sparse_fwd_requires_lse_and_mask():
+    lib = J.lib()
+    sd = J.sparse_desc()
+    args = [1 << 32, 2 << 32, 3 << 32, 24, 64, 112, 24, 128, ctypes.byref(sd), 0.088, 4 << 32]
+    assert lib.mmdit_block_sparse_attn_fwd(*args, 0, 7 << 32, None, 1 << 40, 1 << 38, None) == L.MMDIT_ERR_INVALID_ARG
+    assert lib.mmdit_block_sparse_attn_fwd(*args, 5 << 32, 0, None, 1 << 40, 1 << 38, None) == L.MMDIT_ERR_INVALID_ARG
+    # lse inside o
+    assert lib.mmdit_block_sparse_attn_fwd(*args, (4 << 32) + 256, 7 << 32, None, 1 << 40, 1 << 38,
+                                           None) == L.MMDIT_ERR_INVALID_ARG
+
+
+def test_sparse_bwd_workspace_plan():
+    a256 = lambda x: (x + 255) // 256 * 256
+    n, nb, h = 172032, 2688, 24
+    want = 2 * a256(h * n * 4) + 3 * a256(h * nb * 128 * 64 * 2) + a256(h * nb * 84 * 4)
+    sd = J.sparse_desc()
+    assert J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, 128, J.MMDIT_BF16, sd) == want
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
