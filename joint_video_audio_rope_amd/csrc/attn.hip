@@ -161,28 +161,27 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
         tile_max<false, QB>(sa, a.scale_log2, kTileN, mx);
 
     // Top of step t: K(t+1) and V(t) are published; every wave is done with
-    // K(t) and V(t-1), whose buffers receive K(t+2) and V(t+1).
-    auto top = [&](int t) {
-        const int b = (t - tile0) & 1;
+    // K(t) and V(t-1), whose buffers (b = (t - tile0) & 1) receive K(t+2) and V(t+1).
+    auto top = [&](int t, int b) {
         wait_dma();
         __syncthreads();
         if (t + 2 < tile1) issue_k(t + 2, kbuf(b));
         if (t + 1 < tile1) issue_v(t + 1, vbuf(b ^ 1));
         maybe_rescale<HD, QB>(st, mx);
     };
-    // steps whose next tile is full
+    // Steps whose next tile is full, two per iteration: t - tile0 is even at
+    // the first, so the buffer indices are constants (their LDS offsets fold
+    // into the fragment reads' immediates).
     const int main_end = tile1 - 1 - (last_partial ? 1 : 0);
     int t = tile0;
     for (; t + 1 < main_end; t += 2) {
-        top(t);
-        tile_step<HD, QB, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
-                                       st, a.scale_log2, kTileN, mx);
-        top(t + 1);
-        tile_step<HD, QB, true, false>(kbuf((t + 2 - tile0) & 1), vbuf((t + 1 - tile0) & 1), fa, qf, sb,
-                                       sa, st, a.scale_log2, kTileN, mx);
+        top(t, 0);
+        tile_step<HD, QB, true, false>(kbuf(1), vbuf(0), fa, qf, sa, sb, st, a.scale_log2, kTileN, mx);
+        top(t + 1, 1);
+        tile_step<HD, QB, true, false>(kbuf(0), vbuf(1), fa, qf, sb, sa, st, a.scale_log2, kTileN, mx);
     }
     if (t < main_end) {
-        top(t);
+        top(t, (t - tile0) & 1);
         tile_step<HD, QB, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
                                        st, a.scale_log2, kTileN, mx);
 #pragma unroll
@@ -192,7 +191,7 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
         ++t;
     }
     if (t + 1 < tile1) {   // the next tile is the partial last one
-        top(t);
+        top(t, (t - tile0) & 1);
         tile_step<HD, QB, true, true>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
                                       st, a.scale_log2, last_valid, mx);
 #pragma unroll
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
             for (int kb = 0; kb < 2; ++kb) sa[qb][kb] = sb[qb][kb];
         ++t;
     }
-    top(t);
+    top(t, (t - tile0) & 1);
     tile_step<HD, QB, false, false>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN,
                                     mx);
 
