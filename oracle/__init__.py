@@ -10,6 +10,7 @@ numpy so that a reader can check each step against the pages by eye:
   attention.py     dense softmax attention: joint, A<->V and video->text
   attention_bwd.py log-sum-exp and gradients of (masked) softmax attention
   block_sparse.py  Prism block pooling, hybrid top-k/top-p, sparse attention
+  adaptive_blocks.py  Prism variation indicator and content-adaptive block shapes
   brute.py         pure-Python loop versions used to cross-check the above
 """
-from . import rope, attention, attention_bwd, block_sparse, brute  # noqa: F401
+from . import rope, attention, attention_bwd, block_sparse, adaptive_blocks, brute  # noqa: F401

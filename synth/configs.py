@@ -1,4 +1,4 @@
-"""The five synthetic workloads, as plain numbers.
+"""The synthetic workloads, as plain numbers.
 
 Each entry is raw workload data: token grid sizes, modality counts, head
 geometry, dtype, seed and the input distribution.  Nothing here computes any
@@ -41,6 +41,14 @@ WORKLOADS = {
         T=24, H=64, W=112, heads=24, head_dim=128,
         zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9,
         field_length=4.0, noise_std=0.1,
+    ),
+    "adaptive2k": dict(
+        id=6, dtype="bf16", seed=5,
+        T=24, H=64, W=112, heads=24, head_dim=128,
+        top_k=32, top_p=0.9,
+        field_length=4.0, noise_std=0.1,
+        bg_length=16.0, bg_amp=1.0, fg_lengths=(2.0, 4.0, 8.0), fg_radius=20.0,
+        audio_radius=10.0, audio_gain=4.0, audio_period=6.0,
     ),
 }
 

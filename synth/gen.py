@@ -67,12 +67,12 @@ def _smooth_fields(n_ch, T, H, W, length, g, device, chunk=256):
     White N(0,1) noise per channel on the periodic T x H x W grid, blurred by
     a Gaussian of std length/sqrt(2) per axis (so the field's covariance is
     exp(-r^2 / (2 length^2))), then shifted and scaled per channel to mean 0,
-    variance 1.
+    variance 1.  `length` is one number or a (t, h, w) triple.
     """
-    sigma = length / math.sqrt(2.0)
-    ht = _gaussian_transfer(T, sigma, device)[:, None, None]
-    hh = _gaussian_transfer(H, sigma, device)[None, :, None]
-    hw = _gaussian_transfer(W, sigma, device)[: W // 2 + 1][None, None, :]
+    lt, lh, lw = (length,) * 3 if isinstance(length, (int, float)) else tuple(length)
+    ht = _gaussian_transfer(T, lt / math.sqrt(2.0), device)[:, None, None]
+    hh = _gaussian_transfer(H, lh / math.sqrt(2.0), device)[None, :, None]
+    hw = _gaussian_transfer(W, lw / math.sqrt(2.0), device)[: W // 2 + 1][None, None, :]
     tf = ht * hh * hw
     out = torch.empty((T * H * W, n_ch), dtype=torch.float32, device=device)
     for c0 in range(0, n_ch, chunk):
@@ -110,6 +110,57 @@ def sparse_inputs(w, device="cpu"):
         out[name] = x.reshape(n, h, d).to(dt).contiguous()
         del x
     del F, G
+    return out
+
+
+def _blob(T, H, W, hc, wc, radius, device):
+    """exp(-((h - hc)^2 + (w - wc)^2) / (2 radius^2)) on the grid, [T, H, W] fp32,
+    the same in every frame."""
+    hh = torch.arange(H, device=device, dtype=torch.float32)[:, None]
+    ww = torch.arange(W, device=device, dtype=torch.float32)[None, :]
+    b = torch.exp(-((hh - hc) ** 2 + (ww - wc) ** 2) / (2.0 * radius * radius))
+    return b[None].expand(T, H, W)
+
+
+def adaptive_inputs(w, device="cpu"):
+    """Q, K, V [T*H*W, heads, head_dim] bf16 in raster order and per-token
+    audio norms a [T*H*W] fp32 >= 0 for the content-adaptive block shapes.
+
+    Q and K are as in sparse_inputs (one shared smooth field F of length
+    `field_length`, own noise).  V is a quiet background plus a compact
+    foreground: `bg_amp` times a smooth field of length `bg_length`, plus a
+    Gaussian blob (radius `fg_radius` tokens in h, w, the same in every frame)
+    times a field with per-axis lengths `fg_lengths` (t, h, w), plus noise.
+    The audio norms are a second blob (radius `audio_radius`, peak
+    `audio_gain`) pulsing along t with period `audio_period`:
+    a = gain * blob * (1 + cos(2 pi t / period)) / 2, a sound source inside
+    the frame.  Draw order: the two blob centres (uniform in h, w), F, the
+    background field, the foreground field, then the noise of Q, K and V.
+    """
+    T, H, W = w["T"], w["H"], w["W"]
+    h, d = w["heads"], w["head_dim"]
+    n = T * H * W
+    g = _gen(w["seed"], device)
+    ctr = torch.rand(4, generator=g, device=device, dtype=torch.float64).tolist()
+    F = _smooth_fields(h * d, T, H, W, w["field_length"], g, device)
+    bg = _smooth_fields(h * d, T, H, W, w["bg_length"], g, device)
+    fg = _smooth_fields(h * d, T, H, W, w["fg_lengths"], g, device)
+    env = _blob(T, H, W, ctr[0] * H, ctr[1] * W, w["fg_radius"], device).reshape(n, 1)
+    V = bg.mul_(float(w["bg_amp"])).add_(fg.mul_(env))
+    del fg
+    s = float(w["noise_std"])
+    dt = _DTYPES[w["dtype"]]
+    out = {}
+    for name, base in (("q", F), ("k", F), ("v", V)):
+        x = torch.randn((n, h * d), generator=g, device=device, dtype=torch.float32)
+        x.mul_(s).add_(base)
+        out[name] = x.reshape(n, h, d).to(dt).contiguous()
+        del x
+    del F, V
+    tt = torch.arange(T, device=device, dtype=torch.float32)[:, None, None]
+    pulse = 0.5 * (1.0 + torch.cos(2.0 * math.pi * tt / float(w["audio_period"])))
+    a = _blob(T, H, W, ctr[2] * H, ctr[3] * W, w["audio_radius"], device) * pulse * float(w["audio_gain"])
+    out["a"] = a.reshape(n).contiguous()
     return out
 
 

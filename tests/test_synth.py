@@ -65,3 +65,26 @@ def test_sparse_fields():
     lag = np.mean(q * np.roll(q, 4, axis=2)) / np.mean(q * q)
     assert abs(lag - np.exp(-0.5) / 1.01) < 0.08
     assert torch.equal(sparse_inputs(w)["v"], x["v"])
+
+
+def test_adaptive_inputs():
+    from synth import adaptive_inputs
+    w = shrink("adaptive2k", T=8, H=32, W=32, heads=2, head_dim=16, fg_radius=6.0, audio_radius=4.0)
+    x = adaptive_inputs(w)
+    n = 8 * 32 * 32
+    assert x["q"].shape == (n, 2, 16) and x["q"].dtype == torch.bfloat16
+    assert x["a"].shape == (n,) and x["a"].dtype == torch.float32
+    a = x["a"].numpy().reshape(8, 32, 32)
+    assert a.min() >= 0.0 and abs(a.max() - 4.0) < 0.3
+    # the audio pulse has period 6 frames: frames 0 and 6 peak, frame 3 is silent
+    assert a[3].max() < 1e-6 and abs(a[0].max() - a[6].max()) < 1e-5
+    # Q and K share their field as in the uniform workload
+    q, k = x["q"].float().numpy(), x["k"].float().numpy()
+    assert np.corrcoef(q.ravel(), k.ravel())[0, 1] > 0.98
+    # V: the foreground blob carries more local variation than the background
+    v = x["v"].float().numpy().reshape(8, 32, 32, 32)
+    dv = np.abs(np.diff(v, axis=0)).mean(axis=(0, 3))
+    assert dv.max() > 3 * dv.min()
+    again = adaptive_inputs(w)
+    for t in "qkva":
+        assert torch.equal(again[t], x[t])
