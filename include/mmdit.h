@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 2
+#define MMDIT_ABI_VERSION 3
 #define MMDIT_MAX_SEGMENTS 16
 
 typedef enum {
@@ -68,7 +68,8 @@ typedef enum {
     MMDIT_OP_AV_CROSS_ATTN = 1,
     MMDIT_OP_BLOCK_SPARSE_ATTN = 2,
     MMDIT_OP_JOINT_ATTN_BWD = 3,
-    MMDIT_OP_BLOCK_SPARSE_ATTN_BWD = 4
+    MMDIT_OP_BLOCK_SPARSE_ATTN_BWD = 4,
+    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE = 5
 } mmdit_op;
 
 /* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
@@ -245,6 +246,58 @@ mmdit_status mmdit_block_sparse_attn_fwd(const void* q, const void* k, const voi
                                          int32_t W, int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp,
                                          double softmax_scale, float* o, float* lse, uint32_t* sel_mask,
                                          int32_t* sel_count, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-token Euclidean norms: out[t] = sqrt(sum_c x[t][c]^2) for t < n, x fp32
+ * [n][width] (width a multiple of 4, x 16-byte aligned), out fp32 [n], fp32
+ * sums.  Source: Prism page, "Metodo" section 1 (a = ||h_hat||_2 of the
+ * audio->video cross-attention output, cached for the next layer's block
+ * shapes); with x = the o_video of mmdit_av_cross_attn ([n_video][heads *
+ * head_dim]) it gives that layer's a_norm for mmdit_block_sparse_attn_adaptive.
+ * n == 0 does nothing; out must not overlap x. */
+mmdit_status mmdit_token_norms(const float* x, int64_t n, int64_t width, float* out, void* stream);
+
+/* Block-sparse video self-attention with content-adaptive 3D block shapes.
+ * Sources: Prism page (xyznot.com 2610.05416), "Ideas clave" (8x8x8
+ * macro-zones, dual-guidance variation indicator, 16 candidate shapes of 64,
+ * 128 or 256 tokens) and "Metodo" sections 1-3.
+ * Per zone m, in fp64: sigma2_d = mean over the heads*head_dim channels of the
+ * variance, over the 8 positions along axis d, of the mean of v over the
+ * other two axes; E = sum_d sigma2_d; rho = E / max_m E; the volume B is 64 if
+ * rho >= 0.5, 128 if rho >= 0.25, else 256; abar = (zone mean of a_norm) / (its
+ * largest zone mean); r_d and vhat_d are the shares of sigma2_d and of the same
+ * directional variance of a_norm (0 for a zero total); g_d = r_d + abar vhat_d +
+ * 1e-6; l*_d = -log2(g_d)/2 + (log2 B + sum log2(g)/2) / 3; the shape is the
+ * candidate of volume B nearest to l* (log2 edges, Euclidean, ties to the first
+ * in candidate order).  Candidates: the boxes with edges in {2, 4, 8}; code
+ * 0..6 volume 64: (2,4,8) (2,8,4) (4,2,8) (4,4,4) (4,8,2) (8,2,4) (8,4,2); 7..12
+ * volume 128: (2,8,8) (4,4,8) (4,8,4) (8,2,8) (8,4,4) (8,8,2); 13..15 volume 256:
+ * (4,8,8) (8,4,8) (8,8,4), as (b_T, b_H, b_W).
+ * Blocks are numbered zone by zone (zones in raster order), in raster order of
+ * their position inside the zone; the block means of q and k, the fp64 block
+ * probabilities and the top-k / top-p selection over blocks are those of
+ * mmdit_block_sparse_attn with these blocks; every query attends to the
+ * tokens of its block's selected blocks.
+ * Tiles: each zone is 8 tiles of 64 tokens; a block of B tokens is B/64
+ * consecutive tiles (the block's longest edge halved, first of t, h, w among
+ * equals, once per factor 2; tiles in raster order inside the block).
+ * a_norm [T*H*W] fp32: per-token norms of the previous layer's audio->video
+ * cross-attention output (mmdit_token_norms), or NULL for no audio guidance.
+ * q, k, v [T*H*W][heads][head_dim] bf16; o fp32, lse [heads][T*H*W] fp32 or
+ * NULL (as for mmdit_block_sparse_attn_fwd).  Optional outputs (NULL if not
+ * wanted): zone_shape [nz] uint8 candidate codes (nz = T*H*W / 512);
+ * tile_block [nt] int32 block id of each tile (nt = T*H*W / 64); n_blocks [1]
+ * int32 number of blocks; sel_mask [heads][nt][ceil(nt/32)] uint32, row i
+ * (tile i) has bit j set iff tile j's block is selected by tile i's block;
+ * sel_count [heads][nt] int32 selected blocks of tile i's block.  T, H, W must
+ * be multiples of 8, nz <= 512, head_dim 128.  Workspace:
+ * mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, T*H*W, 0, heads,
+ * head_dim, MMDIT_BF16, NULL). */
+mmdit_status mmdit_block_sparse_attn_adaptive(const void* q, const void* k, const void* v, const float* a_norm,
+                                              int32_t T, int32_t H, int32_t W, int32_t heads, int32_t head_dim,
+                                              int32_t top_k, double top_p, double softmax_scale, float* o,
+                                              float* lse, uint8_t* zone_shape, int32_t* tile_block,
+                                              int32_t* n_blocks, uint32_t* sel_mask, int32_t* sel_count, void* ws,
+                                              size_t ws_bytes, void* stream);
 
 /* Gradients of the block-sparse attention with its selection held fixed (the
  * selection is piecewise constant in q and k): for every query i and key j of

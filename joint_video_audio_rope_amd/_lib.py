@@ -18,7 +18,12 @@ MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMD
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
 (MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,
- MMDIT_OP_BLOCK_SPARSE_ATTN_BWD) = range(5)
+ MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE) = range(6)
+
+# (b_T, b_H, b_W) of the content-adaptive shape codes, in code order
+ADAPTIVE_SHAPES = ((2, 4, 8), (2, 8, 4), (4, 2, 8), (4, 4, 4), (4, 8, 2), (8, 2, 4), (8, 4, 2),
+                   (2, 8, 8), (4, 4, 8), (4, 8, 4), (8, 2, 8), (8, 4, 4), (8, 8, 2),
+                   (4, 8, 8), (8, 4, 8), (8, 8, 4))
 MMDIT_MAX_SEGMENTS = 16
 
 _STATUS = {1: "MMDIT_ERR_INVALID_ARG", 2: "MMDIT_ERR_UNSUPPORTED", 3: "MMDIT_ERR_WORKSPACE",
@@ -93,6 +98,11 @@ def lib():
         L.mmdit_block_sparse_attn_bwd.restype = i32
         L.mmdit_block_sparse_attn_bwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(SparseDesc),
                                                   f64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mmdit_token_norms.argtypes = [vp, i64, i64, vp, vp]
+        L.mmdit_token_norms.restype = i32
+        L.mmdit_block_sparse_attn_adaptive.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f64,
+                                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mmdit_block_sparse_attn_adaptive.restype = i32
         _lib = L
     return _lib
 
@@ -360,6 +370,52 @@ def mmdit_block_sparse_attn_fwd(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4
                                              _ptr(o), _ptr(lse), _ptr(sel_mask), _ptr(sel_count), _ptr(ws), wsb,
                                              _stream(stream)))
     return o, lse, sel_mask, sel_count
+
+
+def mmdit_token_norms(x, out=None, stream=None):
+    """out[t] = ||x[t]||_2 over all other dimensions of an fp32 tensor
+    [n, ...] (e.g. the video output of mmdit_av_cross_attn)."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    n = x.shape[0]
+    width = x.numel() // max(n, 1)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _check(lib().mmdit_token_norms(_ptr(x), n, width, _ptr(out), _stream(stream)))
+    return out
+
+
+def mmdit_block_sparse_attn_adaptive(q, k, v, T, H, W, a_norm=None, top_k=32, top_p=0.9, softmax_scale=None,
+                                     o=None, lse=None, want_lse=False, ws=None, stream=None):
+    """Block-sparse attention with content-adaptive block shapes.  Returns a
+    dict: o fp32 [n, h, d], lse ([h, n] or None), zone_shape uint8 [nz] codes
+    into ADAPTIVE_SHAPES, tile_block int32 [nt], n_blocks int32 [1], sel_mask
+    int32 [h, nt, ceil(nt/32)] (tile level), sel_count int32 [h, nt]."""
+    n, h, d = q.shape
+    assert n == T * H * W and q.dtype == k.dtype == v.dtype == torch.bfloat16
+    for t in (q, k, v):
+        assert t.is_contiguous()
+    if a_norm is not None:
+        assert a_norm.dtype == torch.float32 and a_norm.numel() == n and a_norm.is_contiguous()
+    nt, nz = n // 64, n // 512
+    dev = q.device
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+    out = dict(o=o, lse=lse,
+               zone_shape=torch.empty(nz, dtype=torch.uint8, device=dev),
+               tile_block=torch.empty(nt, dtype=torch.int32, device=dev),
+               n_blocks=torch.empty(1, dtype=torch.int32, device=dev),
+               sel_mask=torch.empty((h, nt, (nt + 31) // 32), dtype=torch.int32, device=dev),
+               sel_count=torch.empty((h, nt), dtype=torch.int32, device=dev))
+    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, n, 0, h, d, MMDIT_BF16, None)
+    ws, wsb = _ws(need, dev, ws)
+    _check(lib().mmdit_block_sparse_attn_adaptive(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(a_norm), T, H, W, h, d, top_k, top_p, scale, _ptr(o), _ptr(lse),
+        _ptr(out["zone_shape"]), _ptr(out["tile_block"]), _ptr(out["n_blocks"]), _ptr(out["sel_mask"]),
+        _ptr(out["sel_count"]), _ptr(ws), wsb, _stream(stream)))
+    return out
 
 
 def mmdit_block_sparse_attn_bwd(q, k, v, o, lse, d_o, sel_mask, T, H, W, zone=(8, 8, 8), block=(4, 4, 4),

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmmdit.so")
-SOURCES = ["abi.hip", "rope.hip", "attn.hip", "attn_bwd.hip", "sparse.hip", "sparse_bwd.hip"]
+SOURCES = ["abi.hip", "rope.hip", "attn.hip", "attn_bwd.hip", "sparse.hip", "sparse_bwd.hip", "adaptive.hip"]
 
 # Packed fp32 VALU ops stay off: hipcc must not form v_pk_{add,mul,fma}_f32.
 HIPFLAGS = [

@@ -342,13 +342,54 @@ mmdit_status check_ws(const void* ws, size_t ws_bytes, size_t need, const char* 
     return MMDIT_OK;
 }
 
+// Content-adaptive blocks: the extra workspace after the uniform layout of
+// the nt = T*H*W / 64 tiles (zone statistics, shape codes, tile tables).
+struct AdaptivePlan {
+    size_t off_part, off_audio, off_code, off_tdim, off_lead, off_tblock, off_nblocks, total;
+};
+
+AdaptivePlan adaptive_layout(size_t start, int64_t nt, int32_t heads, int32_t hd) {
+    AdaptivePlan p{};
+    size_t off = start;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const int64_t nz = nt / kZoneTiles;
+    p.off_part = take((size_t)nz * zone_stat_chunks(heads, hd) * 3 * 8);
+    p.off_audio = take((size_t)nz * 4 * 8);
+    p.off_code = take((size_t)nz);
+    p.off_tdim = take((size_t)nt);
+    p.off_lead = take((size_t)nt * 4);
+    p.off_tblock = take((size_t)nt * 4);
+    p.off_nblocks = take(4);
+    p.total = off;
+    return p;
+}
+
+// Outputs and the audio input of an adaptive call (all optional).
+struct AdaptiveCall {
+    const float* a;
+    uint8_t* zone_shape;
+    int32_t* tile_block;
+    int32_t* n_blocks;
+};
+
 mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, int32_t H, int32_t W,
                         int32_t heads, int32_t head_dim, const mmdit_sparse_desc* sp, double softmax_scale,
                         float* o, float* lse, uint32_t* sel_mask, int32_t* sel_count, void* ws, size_t ws_bytes,
-                        void* stream, const char* who) {
+                        void* stream, const char* who, const AdaptiveCall* ad = nullptr) {
     SparsePlan p{};
     mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
     if (st != MMDIT_OK) return st;
+    AdaptivePlan ap{};
+    if (ad) {
+        if ((int64_t)p.g.nb / kZoneTiles > kMaxZones)
+            return fail(MMDIT_ERR_UNSUPPORTED, "%s: %d zones (max %d)", who, p.g.nb / kZoneTiles, kMaxZones);
+        ap = adaptive_layout(p.total, p.g.nb, heads, head_dim);
+        p.total = ap.total;
+    }
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
         return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
     if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "%s: null q, k, v or o", who);
@@ -366,6 +407,22 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
             overlaps(lse, lb, v, ib))
             return fail(MMDIT_ERR_INVALID_ARG, "%s: lse aliases o or an input", who);
     }
+    if (ad) {
+        const size_t n4 = n * 4, nt = (size_t)p.g.nb;
+        if ((ad->a && (reinterpret_cast<uintptr_t>(ad->a) & 3u)) ||
+            (ad->tile_block && (reinterpret_cast<uintptr_t>(ad->tile_block) & 3u)) ||
+            (ad->n_blocks && (reinterpret_cast<uintptr_t>(ad->n_blocks) & 3u)))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: a_norm, tile_block and n_blocks must be 4-byte aligned", who);
+        if (ad->a && (overlaps(o, ob, ad->a, n4) || (lse && overlaps(lse, n * heads * 4, ad->a, n4))))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: an output aliases a_norm", who);
+        const void* outs[3] = {ad->zone_shape, ad->tile_block, ad->n_blocks};
+        const size_t sizes[3] = {nt / kZoneTiles, nt * 4, 4};
+        for (int i = 0; i < 3; ++i)
+            if (outs[i] && (overlaps(outs[i], sizes[i], o, ob) || overlaps(outs[i], sizes[i], q, ib) ||
+                            overlaps(outs[i], sizes[i], k, ib) || overlaps(outs[i], sizes[i], v, ib) ||
+                            (ad->a && overlaps(outs[i], sizes[i], ad->a, n4))))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: zone_shape, tile_block or n_blocks aliases a tensor", who);
+    }
     if ((st = check_ws(ws, ws_bytes, p.total, who)) != MMDIT_OK) return st;
     char* w = (char*)ws;
     SparseWs sw{};
@@ -379,6 +436,23 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
     sw.kimg = (__bf16*)(w + p.off_kimg);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (ad) {
+        AdaptiveWs aw{};
+        aw.part = (double*)(w + ap.off_part);
+        aw.audio = (double*)(w + ap.off_audio);
+        aw.code = ad->zone_shape ? ad->zone_shape : (uint8_t*)(w + ap.off_code);
+        aw.base = sw.base;
+        aw.tdim = (uint8_t*)(w + ap.off_tdim);
+        aw.lead = (int32_t*)(w + ap.off_lead);
+        aw.tblock = ad->tile_block ? ad->tile_block : (int32_t*)(w + ap.off_tblock);
+        aw.nblocks = ad->n_blocks ? ad->n_blocks : (int32_t*)(w + ap.off_nblocks);
+        sw.tdim = aw.tdim;
+        sw.lead = aw.lead;
+        if ((e = launch_zone_stats(p.g, (const __bf16*)v, ad->a, head_dim, aw, s)) != hipSuccess)
+            return hip_fail(e, "block_sparse_adaptive zone statistics");
+        if ((e = launch_zone_shapes(p.g, head_dim, aw, s)) != hipSuccess)
+            return hip_fail(e, "block_sparse_adaptive shapes");
+    }
     if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse pool");
     if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
@@ -487,6 +561,11 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
         SparsePlan p;
         sparse_layout(n_q / kTileN, heads, head_dim, &p);
         return p.total;
+    }
+    if (op == MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE) {
+        SparsePlan p;
+        sparse_layout(n_q / kTileN, heads, head_dim, &p);
+        return adaptive_layout(p.total, n_q / kTileN, heads, head_dim).total;
     }
     return 0;
 }
@@ -673,6 +752,39 @@ mmdit_status mmdit_block_sparse_attn_fwd(const void* q, const void* k, const voi
         return fail(MMDIT_ERR_INVALID_ARG, "block_sparse_fwd: sel_mask is required (the backward takes it)");
     return run_sparse(q, k, v, T, H, W, heads, head_dim, sp, softmax_scale, o, lse, sel_mask, sel_count, ws,
                       ws_bytes, stream, "block_sparse_fwd");
+}
+
+mmdit_status mmdit_token_norms(const float* x, int64_t n, int64_t width, float* out, void* stream) {
+    if (n < 0 || width < 4 || width % 4)
+        return fail(MMDIT_ERR_INVALID_ARG, "token_norms: n >= 0 and width a positive multiple of 4 required");
+    if (n >= ((int64_t)1 << 31)) return fail(MMDIT_ERR_UNSUPPORTED, "token_norms: n must stay below 2^31");
+    if (n == 0) return MMDIT_OK;
+    if (!x || !out || !aligned16(x) || (reinterpret_cast<uintptr_t>(out) & 3u))
+        return fail(MMDIT_ERR_INVALID_ARG, "token_norms: x must be 16-byte and out 4-byte aligned, non-null");
+    if (overlaps(out, (size_t)n * 4, x, (size_t)n * width * 4))
+        return fail(MMDIT_ERR_INVALID_ARG, "token_norms: out aliases x");
+    const hipError_t e = launch_token_norms(x, n, width, out, (hipStream_t)stream);
+    return e == hipSuccess ? MMDIT_OK : hip_fail(e, "token_norms");
+}
+
+mmdit_status mmdit_block_sparse_attn_adaptive(const void* q, const void* k, const void* v, const float* a_norm,
+                                              int32_t T, int32_t H, int32_t W, int32_t heads, int32_t head_dim,
+                                              int32_t top_k, double top_p, double softmax_scale, float* o,
+                                              float* lse, uint8_t* zone_shape, int32_t* tile_block,
+                                              int32_t* n_blocks, uint32_t* sel_mask, int32_t* sel_count, void* ws,
+                                              size_t ws_bytes, void* stream) {
+    const char* who = "block_sparse_adaptive";
+    if (T % kZoneEdge || H % kZoneEdge || W % kZoneEdge || T < 1 || H < 1 || W < 1)
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: T, H, W must be positive multiples of %d", who, kZoneEdge);
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", who);
+    mmdit_sparse_desc sp{};
+    for (int i = 0; i < 3; ++i) sp.zone[i] = kZoneEdge, sp.block[i] = 4;
+    sp.top_k = top_k;
+    sp.top_p = top_p;
+    const AdaptiveCall ad{a_norm, zone_shape, tile_block, n_blocks};
+    return run_sparse(q, k, v, T, H, W, heads, head_dim, &sp, softmax_scale, o, lse, sel_mask, sel_count, ws,
+                      ws_bytes, stream, who, &ad);
 }
 
 mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,

@@ -145,6 +145,11 @@ struct SparseWs {
     int32_t* base;      // [nb] raster token index of each block's first token
     _Float16* vt;       // [heads][nb][hd * 64]: each key block's V^T in LDS tile order
     __bf16* kimg;       // [heads][nb][64 * hd]: each key block's K rows in LDS tile order
+    // Content-adaptive blocks (null for uniform blocks).  "Blocks" above are
+    // then 64-token tiles; a block of 128 or 256 tokens is 2 or 4 consecutive
+    // tiles, and base[] is filled by the shape pass.
+    const uint8_t* tdim;  // [nb] log2 edges of each tile: t | h << 2 | w << 4
+    const int32_t* lead;  // [nb] first tile of the tile's block
 };
 
 hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
@@ -160,6 +165,32 @@ hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16
 
 // Largest number of blocks per head (selection rows staged in LDS).
 constexpr int kSelMax = 4096;
+
+// ---- content-adaptive block shapes ----------------------------------------------
+constexpr int kZoneEdge = 8;       // macro-zone edge in tokens along t, h and w
+constexpr int kZoneTiles = 8;      // 64-token tiles per zone
+constexpr int kStatPairs = 256;    // channel pairs per zone-statistics workgroup
+constexpr int kMaxZones = kSelMax / kZoneTiles;
+
+struct AdaptiveWs {
+    double* part;      // [nz][nchunk][3] per-chunk sums over channels of the directional variances
+    double* audio;     // [nz][4] zone mean of the audio norms, then their three directional variances
+    uint8_t* code;     // [nz] candidate shape of each zone
+    int32_t* base;     // [nt] first raster token of each tile (SparseWs::base)
+    uint8_t* tdim;     // [nt] log2 edges of each tile
+    int32_t* lead;     // [nt] first tile of the tile's block
+    int32_t* tblock;   // [nt] block id of each tile
+    int32_t* nblocks;  // [1] number of blocks
+};
+
+// Per zone channel statistics of V and the audio norms a (may be null), then
+// the one-workgroup pass that turns them into volumes, shapes and tile tables.
+hipError_t launch_zone_stats(const SparseGeom& g, const __bf16* v, const float* a, int hd, const AdaptiveWs& w,
+                             hipStream_t s);
+hipError_t launch_zone_shapes(const SparseGeom& g, int hd, const AdaptiveWs& w, hipStream_t s);
+int zone_stat_chunks(int heads, int hd);
+// out[t] = ||x[t][0 .. width)||_2 for t < n; width a multiple of 4.
+hipError_t launch_token_norms(const float* x, int64_t n, int64_t width, float* out, hipStream_t s);
 
 // ---- block-sparse backward ------------------------------------------------------
 struct SparseBwdArgs {
@@ -184,6 +215,16 @@ struct SparseBwdArgs {
 hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, hipStream_t s);
 hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint32_t* maskt, hipStream_t s);
 hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s);
+
+// Offset from a tile's first token of its local token r (raster inside the
+// tile) for a tile with log2 edges code = lt | lh << 2 | lw << 4.
+__device__ __forceinline__ int64_t tile_local(const SparseGeom& g, uint32_t code, int r) {
+    const int lh = (code >> 2) & 3, lw = (code >> 4) & 3;
+    const int a = r >> (lh + lw);
+    const int b = (r >> lw) & ((1 << lh) - 1);
+    const int c = r & ((1 << lw) - 1);
+    return ((int64_t)a * g.H + b) * g.W + c;
+}
 
 // Token index (raster t, h, w) of local token r (0..63, raster inside the
 // 4x4x4 block) of block j.

@@ -37,41 +37,59 @@ __device__ __forceinline__ int64_t block_local(const SparseGeom& g, int r) {
 // One workgroup per block: thread -> 8 consecutive channels of heads*hd.
 // Sums of 64 bf16 values in fp64 are exact for any realistic spread of
 // exponents, so the means do not depend on the summation order.
+// With adaptive blocks the workgroup of a block's first tile pools all of the
+// block's tiles (up to 256 rows, still exact) and writes the block mean to
+// every tile of the block; the other tiles' workgroups exit.
 template <int HD>
 __global__ __launch_bounds__(512) void block_pool_kernel(SparseGeom g, const __bf16* __restrict__ q,
                                                          const __bf16* __restrict__ k,
                                                          SparseWs w) {
     const int j = blockIdx.x;
-    const int64_t base = block_token(g, j, 0);
-    if (threadIdx.x == 0) w.base[j] = (int32_t)base;
+    int ntile = 1;
+    if (w.tdim) {
+        if (w.lead[j] != j) return;
+        while (ntile < 4 && j + ntile < g.nb && w.lead[j + ntile] == j) ++ntile;
+    } else if (threadIdx.x == 0) {
+        w.base[j] = (int32_t)block_token(g, j, 0);
+    }
     const int ncg = g.heads * HD / 8;
     const int64_t rs = (int64_t)g.heads * HD;
-    const int vol = g.BT * g.BH * g.BW;
     for (int cg = threadIdx.x; cg < ncg; cg += blockDim.x) {
         double sq[8], sk[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) sq[i] = sk[i] = 0.0;
-        for (int a = 0; a < g.BT; ++a)
-            for (int b = 0; b < g.BH; ++b) {
-                const int64_t row = base + ((int64_t)a * g.H + b) * g.W;
-                for (int c = 0; c < g.BW; ++c) {
-                    const int64_t tok = row + c;
-                    const bf16x8 x = load_bf16x8(q + tok * rs + cg * 8, true);
-                    const bf16x8 y = load_bf16x8(k + tok * rs + cg * 8, true);
+        auto add = [&](int64_t tok) {
+            const bf16x8 x = load_bf16x8(q + tok * rs + cg * 8, true);
+            const bf16x8 y = load_bf16x8(k + tok * rs + cg * 8, true);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        sq[i] += (double)(float)x[i];
-                        sk[i] += (double)(float)y[i];
-                    }
-                }
+            for (int i = 0; i < 8; ++i) {
+                sq[i] += (double)(float)x[i];
+                sk[i] += (double)(float)y[i];
             }
+        };
+        if (w.tdim) {
+            for (int u = 0; u < ntile; ++u) {
+                const int64_t base = w.base[j + u];
+                const uint32_t code = w.tdim[j + u];
+                for (int r = 0; r < kTileN; ++r) add(base + tile_local(g, code, r));
+            }
+        } else {
+            const int64_t base = block_token(g, j, 0);
+            for (int a = 0; a < g.BT; ++a)
+                for (int b = 0; b < g.BH; ++b) {
+                    const int64_t row = base + ((int64_t)a * g.H + b) * g.W;
+                    for (int c = 0; c < g.BW; ++c) add(row + c);
+                }
+        }
         const int head = cg * 8 / HD, d = cg * 8 % HD;
-        const int64_t o = ((int64_t)head * g.nb + j) * HD + d;
-        const double inv = 1.0 / vol;
+        const double inv = 1.0 / (kTileN * ntile);
+        for (int u = 0; u < ntile; ++u) {
+            const int64_t o = ((int64_t)head * g.nb + j + u) * HD + d;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            w.qbar[o + i] = sq[i] * inv;
-            w.kbar[o + i] = sk[i] * inv;
+            for (int i = 0; i < 8; ++i) {
+                w.qbar[o + i] = sq[i] * inv;
+                w.kbar[o + i] = sk[i] * inv;
+            }
         }
     }
 }
@@ -87,12 +105,14 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
     using L = TileLayout<HD>;
     __shared__ _Float16 tile[kTileN][HD + 2];
     const int j = blockIdx.x, head = blockIdx.y;
-    const int64_t base = block_token(g, j, 0);
+    const int64_t base = w.tdim ? (int64_t)w.base[j] : block_token(g, j, 0);
+    const uint32_t code = w.tdim ? w.tdim[j] : 0u;
+    auto local = [&](int r) { return w.tdim ? tile_local(g, code, r) : block_local(g, r); };
     const int64_t rs = (int64_t)g.heads * HD;
     constexpr int CPR = HD / 8;
     for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
         const int r = u / CPR, c = u % CPR;
-        const int64_t tok = base + block_local(g, r);
+        const int64_t tok = base + local(r);
         const bf16x8 x = load_bf16x8(v + tok * rs + head * HD + c * 8, true);
 #pragma unroll
         for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)(float)x[i];
@@ -103,7 +123,7 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
     for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
         int row, c;
         L::k_at(u, row, c);
-        const int64_t tok = base + block_local(g, (row & ~31) | perm_row(row & 31));
+        const int64_t tok = base + local((row & ~31) | perm_row(row & 31));
         *reinterpret_cast<bf16x8*>(kdst + u * 8) = load_bf16x8(k + tok * rs + head * HD + c * 8, true);
     }
     __syncthreads();
@@ -210,7 +230,7 @@ __device__ __forceinline__ uint64_t value_key(double x) { return (uint64_t)__dou
 //   top-k: the k-th element is the largest key x with count(P >= x) >= k.
 // The selection is the longer of the two prefixes.  Slots past the row hold
 // P = -1, which no threshold >= 0 admits.
-template <int EM>   // elements per lane: nb <= 64 EM
+template <int EM, bool AD>   // elements per lane: nb <= 64 EM; AD: adaptive blocks (w.lead set)
 __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom g, int top_k,
                                                                       double top_p, SparseWs w,
                                                                       uint32_t* __restrict__ sel_mask,
@@ -221,21 +241,37 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     const int lane = threadIdx.x & 63;
     const double* L = w.scores + (int64_t)row * nb;
 
-    // softmax over the row, fp64
+    // Columns that are blocks: every column with uniform blocks; with adaptive
+    // blocks only each block's first tile (the other tiles of the block repeat
+    // its logit and take its decision at the end).
+    uint64_t okm = 0;
+    int nv = nb;   // blocks in the row
+    if constexpr (AD) {
+#pragma unroll
+        for (int r = 0; r < EM; ++r) {
+            const int j = lane + 64 * r;
+            if (j < nb && w.lead[j] == j) okm |= 1ull << r;
+        }
+        nv = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r) nv += __popcll(__ballot((okm >> r) & 1ull));
+    }
+    auto col_ok = [&](int r) { return AD ? ((okm >> r) & 1ull) != 0 : lane + 64 * r < nb; };
+
+    // softmax over the row's blocks, fp64
     double P[EM];
     double mx = -__builtin_inf();
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
         const int j = lane + 64 * r;
-        P[r] = j < nb ? L[j] : -__builtin_inf();
+        P[r] = col_ok(r) ? L[j] : -__builtin_inf();
         mx = fmax(mx, P[r]);
     }
     mx = wave_max(mx);
     double se = 0.0;
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
-        const int j = lane + 64 * r;
-        if (j < nb) {
+        if (col_ok(r)) {
             P[r] = exp(P[r] - mx);
             se += P[r];
         }
@@ -244,8 +280,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     double tot = 0.0;
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
-        const int j = lane + 64 * r;
-        if (j < nb) {
+        if (col_ok(r)) {
             P[r] = P[r] / se;
             tot += P[r];
         } else {
@@ -293,7 +328,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     const uint64_t kInf = 0x7FF0000000000000ull;   // +inf: above every probability
 
     // top-p prefix: n_p elements, the last one of value vp, the mp-th of its run
-    int n_p = nb;
+    int n_p = nv;
     double vp = -1.0;
     int mp = 0;
     if (top_p < 1.0 && tot >= top_p) {
@@ -330,10 +365,10 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     }
 
     // top-k prefix
-    const int kk = top_k < nb ? top_k : nb;
+    const int kk = top_k < nv ? top_k : nv;
     double vk = -1.0;
     int mk = 0;
-    if (kk > 0 && kk < nb) {
+    if (kk > 0 && kk < nv) {
         uint64_t lo = 0, hi = kInf;   // count(P >= lo) >= k > count(P >= hi)
         while (hi - lo > 1 && count_in(key_value(lo), key_value(hi)) > 1) {
             const uint64_t mid = lo + ((hi - lo) >> 1);
@@ -349,13 +384,14 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     // the longer prefix: every element above the last value, plus the first
     // m of that value's run in id order (all elements when it covers the row)
     const int K = kk > n_p ? kk : n_p;
-    const bool all = K >= nb;
+    const bool all = K >= nv;
     const double v = kk > n_p ? vk : vp;
     const int mrun = kk > n_p ? mk : mp;
     const int nw = (nb + 31) >> 5;
     uint32_t* mrow = w.mask + (int64_t)row * nw;
     uint32_t* srow = sel_mask ? sel_mask + (int64_t)row * nw : nullptr;
-    int before = 0;   // run elements with a lower id
+    int before = 0;        // run elements with a lower id
+    uint64_t prev = 0, prev_starts = 0;   // block-start decisions and positions of the previous 64 columns
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
         const bool valid = P[r] >= 0.0;
@@ -363,7 +399,19 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
         const int rank = before + __popcll(eq & ((1ull << lane) - 1ull));
         before += __popcll(eq);
         const bool sel = valid && (all || P[r] > v || (P[r] == v && rank < mrun));
-        const uint64_t b = __ballot(sel);
+        uint64_t b = __ballot(sel);
+        if constexpr (AD) {
+            // A block's later tiles copy the bit of its first tile: the
+            // nearest block start at or below the column, in this word of 64
+            // columns or, if none, the last one of the previous word.
+            const uint64_t starts = __ballot(((okm >> r) & 1ull) != 0);
+            const uint64_t upto = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+            const bool inh = upto ? ((b >> (63 - __clzll(upto))) & 1ull)
+                                  : (prev_starts && ((prev >> (63 - __clzll(prev_starts))) & 1ull));
+            prev = b;
+            prev_starts = starts;
+            b = __ballot(sel || (inh && lane + 64 * r < nb));
+        }
         const int wd = 2 * r + lane;
         if (lane < 2 && wd < nw) {   // words past the row hold no bits
             const uint32_t word = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
@@ -543,7 +591,8 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     const int hh = lane >> 5;
     const int m = lane & 31;
     const int qb = min(b0 + side, g.nb - 1);
-    const int64_t qtok = (int64_t)w.base[qb] + block_local(g, (wv & 1) * 32 + m);
+    const int qr = (wv & 1) * 32 + m;
+    const int64_t qtok = (int64_t)w.base[qb] + (w.tdim ? tile_local(g, w.tdim[qb], qr) : block_local(g, qr));
     bf16x8 qf[1][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -623,16 +672,20 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
     const unsigned blocks = (unsigned)((g.heads * g.nb + kSelWaves - 1) / kSelWaves);
     const dim3 grid(blocks), block(64 * kSelWaves);
     const int em = (g.nb + 63) / 64;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+    };
+    const bool ad = w.lead != nullptr;
     if (em <= 8)
-        hipLaunchKernelGGL(block_select_kernel<8>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+        ad ? go(block_select_kernel<8, true>) : go(block_select_kernel<8, false>);
     else if (em <= 16)
-        hipLaunchKernelGGL(block_select_kernel<16>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+        ad ? go(block_select_kernel<16, true>) : go(block_select_kernel<16, false>);
     else if (em <= 32)
-        hipLaunchKernelGGL(block_select_kernel<32>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+        ad ? go(block_select_kernel<32, true>) : go(block_select_kernel<32, false>);
     else if (em <= 48)
-        hipLaunchKernelGGL(block_select_kernel<48>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+        ad ? go(block_select_kernel<48, true>) : go(block_select_kernel<48, false>);
     else
-        hipLaunchKernelGGL(block_select_kernel<64>, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
+        ad ? go(block_select_kernel<64, true>) : go(block_select_kernel<64, false>);
     return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
               "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd", "mmdit_block_sparse_attn_fwd",
-              "mmdit_block_sparse_attn_bwd",
+              "mmdit_block_sparse_attn_bwd", "mmdit_block_sparse_attn_adaptive", "mmdit_token_norms",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
               "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
         assert n in names
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert J.mmdit_abi_version() == 2
+    assert J.mmdit_abi_version() == 3
     assert isinstance(J.mmdit_last_error(), str)
 
 
@@ -277,3 +277,63 @@ def test_block_sparse_workspace_query_matches_the_call():
                                      1 << 36, None, None, 1 << 40, need - 1, None)
     assert st == L.MMDIT_ERR_WORKSPACE
     assert int(re.search(r"required (\d+)", J.mmdit_last_error()).group(1)) == need
+
+
+def _adaptive_call(**over):
+    # 24 x 64 x 112 grid, 24 heads: bf16 tensors 1.06 GB, fp32 o 2.1 GB
+    a = dict(q=1 << 32, k=2 << 32, v=3 << 32, a=4 << 32, T=24, H=64, W=112, heads=24, hd=128, top_k=32,
+             top_p=0.9, scale=0.088, o=5 << 32, lse=None, shape=6 << 32, tblock=7 << 32, nblocks=8 << 32,
+             mask=None, count=None, ws=1 << 40, ws_bytes=1 << 38)
+    a.update(over)
+    return J.lib().mmdit_block_sparse_attn_adaptive(
+        a["q"], a["k"], a["v"], a["a"], a["T"], a["H"], a["W"], a["heads"], a["hd"], a["top_k"], a["top_p"],
+        a["scale"], a["o"], a["lse"], a["shape"], a["tblock"], a["nblocks"], a["mask"], a["count"], a["ws"],
+        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=20), L.MMDIT_ERR_INVALID_ARG),                  # not whole 8 x 8 x 8 zones
+    (dict(W=100), L.MMDIT_ERR_INVALID_ARG),
+    (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(T=48), L.MMDIT_ERR_UNSUPPORTED),                  # 672 zones, 5376 tiles
+    (dict(top_k=-1), L.MMDIT_ERR_INVALID_ARG),
+    (dict(top_p=1.5), L.MMDIT_ERR_INVALID_ARG),
+    (dict(scale=0.0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(a=(4 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),       # misaligned norms
+    (dict(lse=(9 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),
+    (dict(tblock=(5 << 32) + 1024), L.MMDIT_ERR_INVALID_ARG),   # tile_block inside o
+    (dict(shape=(1 << 32) + 64), L.MMDIT_ERR_INVALID_ARG),      # zone_shape inside q
+    (dict(a=(5 << 32) + 4096), L.MMDIT_ERR_INVALID_ARG),         # o overwrites the norms
+    (dict(nblocks=(7 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),
+    (dict(o=(2 << 32) + 1024), L.MMDIT_ERR_INVALID_ARG),         # o aliases k
+    (dict(ws_bytes=1000), L.MMDIT_ERR_WORKSPACE),
+])
+def test_block_sparse_adaptive_rejects_bad_arguments(over, status):
+    assert _adaptive_call(**over) == status
+    assert J.mmdit_last_error() != ""
+
+
+def test_adaptive_workspace_plan_and_query():
+    a256 = lambda x: (x + 255) // 256 * 256
+    n, h = 172032, 24
+    nt, nz = n // 64, n // 512
+    sd = J.sparse_desc()
+    uniform = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, 128, J.MMDIT_BF16, sd)
+    extra = a256(nz * 6 * 3 * 8) + a256(nz * 4 * 8) + a256(nz) + a256(nt) + 2 * a256(nt * 4) + 256
+    need = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, n, 0, h, 128, J.MMDIT_BF16, None)
+    assert need == uniform + extra
+    assert _adaptive_call(ws_bytes=need - 1) == L.MMDIT_ERR_WORKSPACE
+    assert int(re.search(r"required (\d+)", J.mmdit_last_error()).group(1)) == need
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1 << 32, 10, 6, 2 << 32), L.MMDIT_ERR_INVALID_ARG),          # width not a multiple of 4
+    ((1 << 32, 10, 0, 2 << 32), L.MMDIT_ERR_INVALID_ARG),
+    ((1 << 32, -1, 8, 2 << 32), L.MMDIT_ERR_INVALID_ARG),
+    (((1 << 32) + 8, 10, 8, 2 << 32), L.MMDIT_ERR_INVALID_ARG),    # x not 16-byte aligned
+    ((1 << 32, 10, 8, (1 << 32) + 64), L.MMDIT_ERR_INVALID_ARG),   # out inside x
+    ((None, 10, 8, 2 << 32), L.MMDIT_ERR_INVALID_ARG),
+    ((None, 0, 8, None), L.MMDIT_OK),                               # nothing to do
+])
+def test_token_norms_checks(args, status):
+    assert J.lib().mmdit_token_norms(*args, None) == status
