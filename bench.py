@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--no-train", action="store_true",
                     help="skip the training leg (joint attention forward with lse + backward)")
     ap.add_argument("--sparse-reps", type=int, default=3)
+    ap.add_argument("--no-adaptive", action="store_true", help="skip the content-adaptive block-shape leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the oracle sample (all heads, all keys)")
@@ -287,6 +288,10 @@ def main():
         out["block_sparse"] = sparse_leg(args, torch, J, WORKLOADS["sparse2k"], sparse_inputs, dev)
         print("[bench] block sparse: %s" % out["block_sparse"], file=sys.stderr, flush=True)
 
+    if not args.no_adaptive:
+        out["adaptive_sparse"] = adaptive_leg(args, torch, J, WORKLOADS["adaptive2k"], dev)
+        print("[bench] adaptive block shapes: %s" % out["adaptive_sparse"], file=sys.stderr, flush=True)
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, torch, q, k, v)
         print("[bench] cpu baseline: %s" % out["cpu_baseline"], file=sys.stderr, flush=True)
@@ -389,6 +394,60 @@ def sparse_leg(args, torch, J, w, sparse_inputs, dev):
     if not args.no_train:
         out.update(sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream))
     return out
+
+
+def adaptive_leg(args, torch, J, w, dev):
+    """Dense vs block-sparse self-attention with content-adaptive block shapes
+    on the 24 x 64 x 112 grid (foreground blob in V, pulsing audio norms)."""
+    from synth import adaptive_inputs
+
+    T, H, W = w["T"], w["H"], w["W"]
+    h, d = w["heads"], w["head_dim"]
+    n = T * H * W
+    x = adaptive_inputs(w, dev)
+    q, k, v, a = x["q"], x["k"], x["v"], x["a"]
+    o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, n, 0, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+
+    def dense():
+        J.mmdit_joint_attn(q, k, v, o=o, ws=ws_d, stream=stream)
+
+    def adaptive():
+        res.update(J.mmdit_block_sparse_attn_adaptive(q, k, v, T, H, W, a_norm=a, top_k=w["top_k"],
+                                                      top_p=w["top_p"], o=o, ws=ws_a, stream=stream))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.sparse_reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.sparse_reps
+
+    t_dense = timed(dense)
+    t_ad = timed(adaptive)
+    nt = n // 64
+    words = res["sel_mask"].view(torch.uint8).cpu()
+    pairs = int(torch.bitwise_and(words[..., None] >> torch.arange(8, dtype=torch.uint8), 1).sum().item())
+    vols = torch.bincount(res["zone_shape"].long().cpu(), minlength=16)
+    by_vol = {64: int(vols[:7].sum()), 128: int(vols[7:13].sum()), 256: int(vols[13:].sum())}
+    fl_sparse = 4.0 * 64 * 64 * d * pairs
+    return {"workload": "video 24x64x112 (172032 tokens), 24 heads x 128, zones 8x8x8, content-adaptive "
+                        "blocks (16 shapes, 64/128/256 tokens), top-k 32 + top-p 0.9, foreground blob in V, "
+                        "pulsing audio norms",
+            "zones_by_volume": by_vol, "shapes_used": int((vols > 0).sum()),
+            "blocks": int(res["n_blocks"].item()),
+            "dense_ms": round(t_dense, 3), "adaptive_ms": round(t_ad, 3),
+            "speedup": round(t_dense / t_ad, 3), "density": round(pairs / (h * nt * nt), 4),
+            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_ad * 1e-9, 1)}
 
 
 def sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream):
