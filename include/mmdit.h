@@ -69,7 +69,8 @@ typedef enum {
     MMDIT_OP_BLOCK_SPARSE_ATTN = 2,
     MMDIT_OP_JOINT_ATTN_BWD = 3,
     MMDIT_OP_BLOCK_SPARSE_ATTN_BWD = 4,
-    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE = 5
+    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE = 5,
+    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD = 6
 } mmdit_op;
 
 /* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
@@ -298,6 +299,26 @@ mmdit_status mmdit_block_sparse_attn_adaptive(const void* q, const void* k, cons
                                               float* lse, uint8_t* zone_shape, int32_t* tile_block,
                                               int32_t* n_blocks, uint32_t* sel_mask, int32_t* sel_count, void* ws,
                                               size_t ws_bytes, void* stream);
+
+/* Gradients of mmdit_block_sparse_attn_adaptive with its shapes and selection
+ * held fixed (both are piecewise constant in the inputs): the gradients of
+ * masked softmax attention over the selected tile pairs, as
+ * mmdit_block_sparse_attn_bwd states them.  Sources: Prism page, "Metodo"
+ * sections 1-3 and "Resultados" (training-step time of the sparse attention).
+ * q, k, v, T, H, W, heads, head_dim and softmax_scale as passed to the
+ * forward; o and lse (required) are its outputs, zone_shape [T*H*W/512] and
+ * sel_mask (tile level) likewise.  d_o [T*H*W][heads][head_dim] bf16; dq, dk,
+ * dv fp32, written, 16-byte aligned, overlapping nothing.  The inputs are
+ * permuted to the tile order of the forward's blocks, the uniform sparse
+ * backward runs on them, and the gradients are permuted back (about 25 GB of
+ * extra traffic at 172032 tokens x 24 x 128).  Deterministic.  Workspace:
+ * mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, T*H*W, 0,
+ * heads, head_dim, MMDIT_BF16, NULL). */
+mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                                  int32_t W, int32_t heads, int32_t head_dim, double softmax_scale,
+                                                  const float* o, const float* lse, const void* d_o,
+                                                  const uint8_t* zone_shape, const uint32_t* sel_mask, float* dq,
+                                                  float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* Gradients of the block-sparse attention with its selection held fixed (the
  * selection is piecewise constant in q and k): for every query i and key j of

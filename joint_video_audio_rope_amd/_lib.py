@@ -18,7 +18,7 @@ MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMD
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
 (MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,
- MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE) = range(6)
+ MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD) = range(7)
 
 # (b_T, b_H, b_W) of the content-adaptive shape codes, in code order
 ADAPTIVE_SHAPES = ((2, 4, 8), (2, 8, 4), (4, 2, 8), (4, 4, 4), (4, 8, 2), (8, 2, 4), (8, 4, 2),
@@ -103,6 +103,9 @@ def lib():
         L.mmdit_block_sparse_attn_adaptive.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f64,
                                                        vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mmdit_block_sparse_attn_adaptive.restype = i32
+        L.mmdit_block_sparse_attn_adaptive_bwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f64, vp, vp, vp, vp,
+                                                           vp, vp, vp, vp, vp, sz, vp]
+        L.mmdit_block_sparse_attn_adaptive_bwd.restype = i32
         _lib = L
     return _lib
 
@@ -416,6 +419,28 @@ def mmdit_block_sparse_attn_adaptive(q, k, v, T, H, W, a_norm=None, top_k=32, to
         _ptr(out["zone_shape"]), _ptr(out["tile_block"]), _ptr(out["n_blocks"]), _ptr(out["sel_mask"]),
         _ptr(out["sel_count"]), _ptr(ws), wsb, _stream(stream)))
     return out
+
+
+def mmdit_block_sparse_attn_adaptive_bwd(q, k, v, fwd, d_o, T, H, W, softmax_scale=None, dq=None, dk=None,
+                                         dv=None, ws=None, stream=None):
+    """Gradients (dq, dk, dv), fp32, of the adaptive block-sparse attention
+    whose forward returned `fwd` (the dict of mmdit_block_sparse_attn_adaptive,
+    called with want_lse=True); shapes and selection are held fixed."""
+    n, h, d = q.shape
+    assert n == T * H * W and q.dtype == k.dtype == v.dtype == d_o.dtype == torch.bfloat16
+    assert fwd["lse"] is not None, "the forward must keep the log-sum-exp (want_lse=True)"
+    for t in (q, k, v, d_o, fwd["o"], fwd["lse"], fwd["zone_shape"], fwd["sel_mask"]):
+        assert t.is_contiguous()
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=q.device) if t is None else t
+                  for t in (dq, dk, dv))
+    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, d, MMDIT_BF16, None)
+    ws, wsb = _ws(need, q.device, ws)
+    _check(lib().mmdit_block_sparse_attn_adaptive_bwd(
+        _ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, scale, _ptr(fwd["o"]), _ptr(fwd["lse"]), _ptr(d_o),
+        _ptr(fwd["zone_shape"]), _ptr(fwd["sel_mask"]), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
+        _stream(stream)))
+    return dq, dk, dv
 
 
 def mmdit_block_sparse_attn_bwd(q, k, v, o, lse, d_o, sel_mask, T, H, W, zone=(8, 8, 8), block=(4, 4, 4),

@@ -493,6 +493,75 @@ SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) 
     return p;
 }
 
+// Adaptive-shape backward: the token map of the tile order, the inputs and
+// gradients permuted to it, then the uniform backward's workspace.
+struct AdaptiveBwdPlan {
+    size_t off_map, off_q, off_k, off_v, off_do, off_o, off_lse, off_dq, off_dk, off_dv, off_bwd, total;
+    SparseBwdPlan bwd;
+};
+
+AdaptiveBwdPlan plan_adaptive_bwd(int64_t n, int32_t heads, int32_t hd) {
+    AdaptiveBwdPlan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align256(bytes);
+        return o;
+    };
+    const size_t hb = (size_t)n * heads * hd * 2, fb = hb * 2;
+    p.off_map = take((size_t)n * 4);
+    p.off_q = take(hb);
+    p.off_k = take(hb);
+    p.off_v = take(hb);
+    p.off_do = take(hb);
+    p.off_o = take(fb);
+    p.off_lse = take((size_t)n * heads * 4);
+    p.off_dq = take(fb);
+    p.off_dk = take(fb);
+    p.off_dv = take(fb);
+    p.bwd = plan_sparse_bwd(n, n / kTileN, heads, hd);
+    p.off_bwd = take(p.bwd.total);
+    p.total = off;
+    return p;
+}
+
+// The kernels of a block-sparse backward over the plan's geometry.
+mmdit_status run_sparse_bwd(const SparsePlan& p, const SparseBwdPlan& bp, const void* q, const void* k,
+                            const void* v, const float* o, const float* lse, const void* d_o,
+                            const uint32_t* sel_mask, float* dq, float* dk, float* dv, double softmax_scale, char* w,
+                            hipStream_t s, const char* who) {
+    const int64_t n = (int64_t)p.g.T * p.g.H * p.g.W;
+    const int heads = p.g.heads;
+    const int head_dim = 128;
+    SparseBwdArgs a{};
+    a.q = (const __bf16*)q;
+    a.k = (const __bf16*)k;
+    a.v = (const __bf16*)v;
+    a.d_o = (const __bf16*)d_o;
+    a.qt_img = (const __bf16*)(w + bp.off_qt);
+    a.dot_img = (const __bf16*)(w + bp.off_dot);
+    a.kt_img = (const __bf16*)(w + bp.off_kt);
+    a.mask = sel_mask;
+    a.maskt = (const uint32_t*)(w + bp.off_maskt);
+    a.ls2 = (const float*)(w + bp.off_ls2);
+    a.dd = (const float*)(w + bp.off_dd);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = (float)softmax_scale;
+    a.scale_log2 = (float)(softmax_scale * 1.4426950408889634);
+    hipError_t e;
+    if ((e = launch_bwd_rowterm(o, d_o, MMDIT_BF16, lse, n, n, heads, head_dim, (float*)a.dd, (float*)a.ls2, s)) !=
+            hipSuccess ||
+        (e = launch_block_timg(p.g, a.q, (__bf16*)a.qt_img, s)) != hipSuccess ||
+        (e = launch_block_timg(p.g, a.d_o, (__bf16*)a.dot_img, s)) != hipSuccess ||
+        (e = launch_block_timg(p.g, a.k, (__bf16*)a.kt_img, s)) != hipSuccess ||
+        (e = launch_mask_transpose(p.g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
+        (e = launch_sparse_bwd(p.g, a, s)) != hipSuccess)
+        return hip_fail(e, who);
+    return MMDIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -562,6 +631,7 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
         sparse_layout(n_q / kTileN, heads, head_dim, &p);
         return p.total;
     }
+    if (op == MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD) return plan_adaptive_bwd(n_q, heads, head_dim).total;
     if (op == MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE) {
         SparsePlan p;
         sparse_layout(n_q / kTileN, heads, head_dim, &p);
@@ -824,33 +894,90 @@ mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const voi
     }
     const SparseBwdPlan bp = plan_sparse_bwd(n, nb, heads, head_dim);
     if ((st = check_ws(ws, ws_bytes, bp.total, who)) != MMDIT_OK) return st;
+    return run_sparse_bwd(p, bp, q, k, v, o, lse, d_o, sel_mask, dq, dk, dv, softmax_scale, (char*)ws,
+                          (hipStream_t)stream, who);
+}
+
+mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
+                                                  int32_t W, int32_t heads, int32_t head_dim, double softmax_scale,
+                                                  const float* o, const float* lse, const void* d_o,
+                                                  const uint8_t* zone_shape, const uint32_t* sel_mask, float* dq,
+                                                  float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+    const char* who = "block_sparse_adaptive_bwd";
+    if (T < 1 || H < 1 || W < 1 || T % kZoneEdge || H % kZoneEdge || W % kZoneEdge)
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: T, H, W must be positive multiples of %d", who, kZoneEdge);
+    const int64_t n = (int64_t)T * H * W;
+    if (n / kTileN / kZoneTiles > kMaxZones)
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: %lld zones (max %d)", who, (long long)(n / 512), kMaxZones);
+    // the grid in tile order: one row of tokens, a block per 64 of them
+    mmdit_sparse_desc flat{};
+    flat.zone[0] = flat.zone[1] = flat.block[0] = flat.block[1] = 1;
+    flat.zone[2] = flat.block[2] = kTileN;
+    flat.top_k = 0;
+    flat.top_p = 1.0;
+    SparsePlan p{};
+    mmdit_status st = plan_sparse(1, 1, (int)std::min<int64_t>(n, INT32_MAX), heads, head_dim, &flat, &p);
+    if (st != MMDIT_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    const void* al16[8] = {q, k, v, o, d_o, dq, dk, dv};
+    for (const void* ptr : al16)
+        if (!ptr || !aligned16(ptr))
+            return fail(MMDIT_ERR_INVALID_ARG, "%s: q, k, v, o, d_o, dq, dk, dv must be non-null and 16-byte aligned",
+                        who);
+    if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u) || !sel_mask ||
+        (reinterpret_cast<uintptr_t>(sel_mask) & 3u) || !zone_shape)
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: lse, sel_mask (4-byte aligned) and zone_shape are required", who);
+    const int64_t nb = p.g.nb, nw = (nb + 31) / 32;
+    const size_t ib = (size_t)n * heads * head_dim * 2, fb = (size_t)n * heads * head_dim * 4;
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[8] = {q, k, v, o, lse, d_o, sel_mask, zone_shape};
+    const size_t isz[8] = {ib, ib, ib, fb, (size_t)n * heads * 4, ib, (size_t)heads * nb * nw * 4,
+                           (size_t)(n / 512)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], fb, outs[j], fb))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: dq, dk and dv must not overlap", who);
+        for (int j = 0; j < 8; ++j)
+            if (overlaps(outs[i], fb, ins[j], isz[j]))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: a gradient aliases an input", who);
+    }
+    const AdaptiveBwdPlan ap = plan_adaptive_bwd(n, heads, head_dim);
+    if ((st = check_ws(ws, ws_bytes, ap.total, who)) != MMDIT_OK) return st;
     char* w = (char*)ws;
-    SparseBwdArgs a{};
-    a.q = (const __bf16*)q;
-    a.k = (const __bf16*)k;
-    a.v = (const __bf16*)v;
-    a.d_o = (const __bf16*)d_o;
-    a.qt_img = (const __bf16*)(w + bp.off_qt);
-    a.dot_img = (const __bf16*)(w + bp.off_dot);
-    a.kt_img = (const __bf16*)(w + bp.off_kt);
-    a.mask = sel_mask;
-    a.maskt = (const uint32_t*)(w + bp.off_maskt);
-    a.ls2 = (const float*)(w + bp.off_ls2);
-    a.dd = (const float*)(w + bp.off_dd);
-    a.dq = dq;
-    a.dk = dk;
-    a.dv = dv;
-    a.scale = (float)softmax_scale;
-    a.scale_log2 = (float)(softmax_scale * 1.4426950408889634);
     hipStream_t s = (hipStream_t)stream;
+    // tile order of the grid the forward chose, then the inputs in that order
+    SparseGeom grid{};
+    grid.T = T, grid.H = H, grid.W = W;
+    grid.nzh = H / kZoneEdge, grid.nzw = W / kZoneEdge;
+    grid.nb = (int32_t)nb;
+    grid.heads = heads;
+    int32_t* tokmap = (int32_t*)(w + ap.off_map);
+    char* qp = w + ap.off_q;
+    char* kp = w + ap.off_k;
+    char* vp = w + ap.off_v;
+    char* gp = w + ap.off_do;
+    char* op = w + ap.off_o;
+    float* lp = (float*)(w + ap.off_lse);
+    float* gq = (float*)(w + ap.off_dq);
+    float* gk = (float*)(w + ap.off_dk);
+    float* gv = (float*)(w + ap.off_dv);
+    const int64_t rbh = (int64_t)heads * head_dim * 2, rbf = rbh * 2;
     hipError_t e;
-    if ((e = launch_bwd_rowterm(o, d_o, MMDIT_BF16, lse, n, n, heads, head_dim, (float*)a.dd, (float*)a.ls2, s)) !=
-            hipSuccess ||
-        (e = launch_block_timg(p.g, a.q, (__bf16*)a.qt_img, s)) != hipSuccess ||
-        (e = launch_block_timg(p.g, a.d_o, (__bf16*)a.dot_img, s)) != hipSuccess ||
-        (e = launch_block_timg(p.g, a.k, (__bf16*)a.kt_img, s)) != hipSuccess ||
-        (e = launch_mask_transpose(p.g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
-        (e = launch_sparse_bwd(p.g, a, s)) != hipSuccess)
+    if ((e = launch_tile_token_map(grid, zone_shape, tokmap, s)) != hipSuccess ||
+        (e = launch_permute_rows(q, qp, tokmap, n, rbh, true, s)) != hipSuccess ||
+        (e = launch_permute_rows(k, kp, tokmap, n, rbh, true, s)) != hipSuccess ||
+        (e = launch_permute_rows(v, vp, tokmap, n, rbh, true, s)) != hipSuccess ||
+        (e = launch_permute_rows(d_o, gp, tokmap, n, rbh, true, s)) != hipSuccess ||
+        (e = launch_permute_rows(o, op, tokmap, n, rbf, true, s)) != hipSuccess ||
+        (e = launch_permute_cols(lse, lp, tokmap, n, heads, s)) != hipSuccess)
+        return hip_fail(e, who);
+    st = run_sparse_bwd(p, ap.bwd, qp, kp, vp, (const float*)op, lp, gp, sel_mask, gq, gk, gv, softmax_scale,
+                        w + ap.off_bwd, s, who);
+    if (st != MMDIT_OK) return st;
+    if ((e = launch_permute_rows(gq, dq, tokmap, n, rbf, false, s)) != hipSuccess ||
+        (e = launch_permute_rows(gk, dk, tokmap, n, rbf, false, s)) != hipSuccess ||
+        (e = launch_permute_rows(gv, dv, tokmap, n, rbf, false, s)) != hipSuccess)
         return hip_fail(e, who);
     return MMDIT_OK;
 }

@@ -55,6 +55,43 @@ __device__ __forceinline__ int64_t zone_origin(const SparseGeom& g, int m) {
     return ((int64_t)(zt * kZoneEdge) * g.H + zh * kZoneEdge) * g.W + zw * kZoneEdge;
 }
 
+// Geometry of tile s (zone s / 8, tile s % 8 of the zone) for zone shape
+// code `code`: the raster index of its first token, its log2 edges
+// (t | h << 2 | w << 4), its index inside its block and its block's index
+// inside the zone.
+struct TileGeom {
+    int64_t base;
+    uint32_t dims;
+    int sub, blk;
+};
+
+__device__ __forceinline__ TileGeom tile_geom(const SparseGeom& g, int s, int code) {
+    const int zm = s / kZoneTiles, u = s - zm * kZoneTiles;
+    const uint8_t* c = kCand[code];
+    const int lbt = c[0], lbh = c[1], lbw = c[2];
+    const int split = lbt + lbh + lbw - 6;   // tiles per block = 2^split
+    const int blk = u >> split, sub = u & ((1 << split) - 1);
+    // position of the block inside the zone, raster over (8 >> lbt, 8 >> lbh, 8 >> lbw)
+    const int nbh = 8 >> lbh, nbw = 8 >> lbw;
+    const int pt = blk / (nbh * nbw), ph = (blk / nbw) % nbh, pw = blk % nbw;
+    // tile edges: halve the longest edge (first of t, h, w) split times
+    int lt = lbt, lh = lbh, lw = lbw;
+    for (int i = 0; i < split; ++i) {
+        if (lt >= lh && lt >= lw) --lt;
+        else if (lh >= lw) --lh;
+        else --lw;
+    }
+    const int qh_n = 1 << (lbh - lh), qw_n = 1 << (lbw - lw);
+    const int qt = sub / (qh_n * qw_n), qh = (sub / qw_n) % qh_n, qw = sub % qw_n;
+    const int t = (pt << lbt) + (qt << lt), h = (ph << lbh) + (qh << lh), w = (pw << lbw) + (qw << lw);
+    TileGeom r;
+    r.base = zone_origin(g, zm) + ((int64_t)t * g.H + h) * g.W + w;
+    r.dims = (uint32_t)(lt | (lh << 2) | (lw << 4));
+    r.sub = sub;
+    r.blk = blk;
+    return r;
+}
+
 // Sum over 8 positions of (mean at the position - zone mean)^2, / 8.
 __device__ __forceinline__ double axis_var(const double (&s)[8], double mu) {
     double acc = 0.0;
@@ -233,31 +270,50 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
     }
     __syncthreads();
     for (int s = tid; s < nz * kZoneTiles; s += 1024) {
-        const int zm = s / kZoneTiles, u = s - zm * kZoneTiles;
-        const uint8_t* c = kCand[zcode[zm]];
-        const int lbt = c[0], lbh = c[1], lbw = c[2];
-        const int split = lbt + lbh + lbw - 6;   // tiles per block = 2^split
-        const int per = 1 << split;
-        const int blk = u >> split, sub = u & (per - 1);
-        // position of the block inside the zone, raster over (8 >> lbt, 8 >> lbh, 8 >> lbw)
-        const int nbh = 8 >> lbh, nbw = 8 >> lbw;
-        const int pt = blk / (nbh * nbw), ph = (blk / nbw) % nbh, pw = blk % nbw;
-        // tile edges: halve the longest edge (first of t, h, w) split times
-        int lt = lbt, lh = lbh, lw = lbw;
-        for (int i = 0; i < split; ++i) {
-            if (lt >= lh && lt >= lw) --lt;
-            else if (lh >= lw) --lh;
-            else --lw;
-        }
-        const int qh_n = 1 << (lbh - lh), qw_n = 1 << (lbw - lw);
-        const int qt = sub / (qh_n * qw_n), qh = (sub / qw_n) % qh_n, qw = sub % qw_n;
-        const int64_t org = zone_origin(g, zm);
-        const int t = (pt << lbt) + (qt << lt), h = (ph << lbh) + (qh << lh), ww = (pw << lbw) + (qw << lw);
-        w.base[s] = (int32_t)(org + ((int64_t)t * g.H + h) * g.W + ww);
-        w.tdim[s] = (uint8_t)(lt | (lh << 2) | (lw << 4));
-        w.lead[s] = s - sub;
-        w.tblock[s] = zbase[zm] + blk;
+        const int zm = s / kZoneTiles;
+        const TileGeom tg = tile_geom(g, s, zcode[zm]);
+        w.base[s] = (int32_t)tg.base;
+        w.tdim[s] = (uint8_t)tg.dims;
+        w.lead[s] = s - tg.sub;
+        w.tblock[s] = zbase[zm] + tg.blk;
     }
+}
+
+// Raster token of every position of the tile order: tokmap[64 s + r] is
+// local token r of tile s.  One workgroup of 64 threads per tile.  Codes
+// outside 0..15 are clamped (they come from a forward call of this library).
+__global__ __launch_bounds__(64) void tile_token_map_kernel(SparseGeom g, const uint8_t* __restrict__ codes,
+                                                            int32_t* __restrict__ tokmap) {
+    const int s = blockIdx.x, r = threadIdx.x;
+    const int code = min((int)codes[s / kZoneTiles], 15);
+    const TileGeom tg = tile_geom(g, s, code);
+    tokmap[(int64_t)s * kTileN + r] = (int32_t)(tg.base + tile_local(g, tg.dims, r));
+}
+
+// Rows of row_bytes bytes (a multiple of 16): gather (dst[p] = src[tokmap[p]])
+// or scatter (dst[tokmap[p]] = src[p]).  One workgroup per 8 rows.
+__global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restrict__ src, char* __restrict__ dst,
+                                                           const int32_t* __restrict__ tokmap, int64_t n,
+                                                           int64_t row_bytes, int gather) {
+    const int64_t chunks = row_bytes / 16;
+    for (int64_t i = threadIdx.x; i < 8 * chunks; i += 256) {
+        const int64_t p = (int64_t)blockIdx.x * 8 + i / chunks;
+        if (p >= n) break;
+        const int64_t c = i - (i / chunks) * chunks;
+        const int64_t t = tokmap[p];
+        const int64_t from = gather ? t : p, to = gather ? p : t;
+        *reinterpret_cast<uint4*>(dst + to * row_bytes + c * 16) =
+            *reinterpret_cast<const uint4*>(src + from * row_bytes + c * 16);
+    }
+}
+
+// dst[h][p] = src[h][tokmap[p]] for [heads][n] fp32.
+__global__ __launch_bounds__(256) void permute_cols_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                           const int32_t* __restrict__ tokmap, int64_t n) {
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (p >= n) return;
+    const int64_t h = blockIdx.y;
+    dst[h * n + p] = src[h * n + tokmap[p]];
 }
 
 // out[t] = sqrt(sum_c x[t][c]^2), one workgroup of 256 threads per token,
@@ -283,6 +339,26 @@ __global__ __launch_bounds__(256) void token_norms_kernel(const float* __restric
 }
 
 }  // namespace
+
+hipError_t launch_tile_token_map(const SparseGeom& g, const uint8_t* codes, int32_t* tokmap, hipStream_t s) {
+    hipLaunchKernelGGL(tile_token_map_kernel, dim3(g.nb), dim3(kTileN), 0, s, g, codes, tokmap);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* tokmap, int64_t n, int64_t row_bytes,
+                               bool gather, hipStream_t s) {
+    if (row_bytes % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(permute_rows_kernel, dim3((uint32_t)((n + 7) / 8)), dim3(256), 0, s, (const char*)src,
+                       (char*)dst, tokmap, n, row_bytes, gather ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_cols(const float* src, float* dst, const int32_t* tokmap, int64_t n, int heads,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(permute_cols_kernel, dim3((uint32_t)((n + 255) / 256), heads), dim3(256), 0, s, src, dst,
+                       tokmap, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_token_norms(const float* x, int64_t n, int64_t width, float* out, hipStream_t s) {
     if (n == 0) return hipSuccess;

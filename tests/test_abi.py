@@ -30,6 +30,7 @@ def test_header_declares_the_calls():
     for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
               "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd", "mmdit_block_sparse_attn_fwd",
               "mmdit_block_sparse_attn_bwd", "mmdit_block_sparse_attn_adaptive", "mmdit_token_norms",
+              "mmdit_block_sparse_attn_adaptive_bwd",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
               "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
         assert n in names
@@ -337,3 +338,43 @@ def test_adaptive_workspace_plan_and_query():
 ])
 def test_token_norms_checks(args, status):
     assert J.lib().mmdit_token_norms(*args, None) == status
+
+
+def _adaptive_bwd_call(**over):
+    a = dict(q=1 << 32, k=2 << 32, v=3 << 32, o=4 << 32, lse=5 << 32, d_o=6 << 32, shape=7 << 32,
+             mask=(7 << 32) + (1 << 20), dq=8 << 32, dk=9 << 32, dv=10 << 32, T=24, H=64, W=112, heads=24, hd=128,
+             scale=0.088, ws=1 << 40, ws_bytes=1 << 39)
+    a.update(over)
+    return J.lib().mmdit_block_sparse_attn_adaptive_bwd(
+        a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["heads"], a["hd"], a["scale"], a["o"], a["lse"],
+        a["d_o"], a["shape"], a["mask"], a["dq"], a["dk"], a["dv"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
+    (dict(T=48), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), L.MMDIT_ERR_INVALID_ARG),
+    (dict(shape=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(lse=0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(mask=(7 << 32) + (1 << 20) + 2), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dq=(8 << 32) + 8), L.MMDIT_ERR_INVALID_ARG),
+    (dict(dk=(8 << 32) + 4096), L.MMDIT_ERR_INVALID_ARG),          # dk overlaps dq
+    (dict(dv=(7 << 32) - 1024), L.MMDIT_ERR_INVALID_ARG),          # dv runs into zone_shape
+    (dict(ws_bytes=1000), L.MMDIT_ERR_WORKSPACE),
+])
+def test_block_sparse_adaptive_bwd_rejects_bad_arguments(over, status):
+    assert _adaptive_bwd_call(**over) == status
+    assert J.mmdit_last_error() != ""
+
+
+def test_adaptive_bwd_workspace_plan():
+    a256 = lambda x: (x + 255) // 256 * 256
+    n, nb, h = 172032, 2688, 24
+    hb = n * h * 128 * 2
+    uniform_bwd = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, 128, J.MMDIT_BF16,
+                                          J.sparse_desc())
+    want = a256(n * 4) + 4 * a256(hb) + a256(2 * hb) + a256(n * h * 4) + 3 * a256(2 * hb) + a256(uniform_bwd)
+    need = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, 128, J.MMDIT_BF16, None)
+    assert need == want
+    assert _adaptive_bwd_call(ws_bytes=need - 1) == L.MMDIT_ERR_WORKSPACE

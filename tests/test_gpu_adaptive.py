@@ -161,3 +161,84 @@ def test_token_norms_match_oracle():
     ref = A.token_norms(f64(x))
     np.testing.assert_allclose(f64(got), ref, rtol=1e-5)
     assert float(got[17]) == 0.0
+
+
+REL_GRAD = 1e-2   # bf16 gradients: max-abs within 1e-2 of the largest reference entry (as the uniform backward)
+
+
+def check_rel(name, got, ref, rel):
+    err = float(np.max(np.abs(got - ref)))
+    peak = float(np.max(np.abs(ref)))
+    print("%s: max-abs %.3e, max |ref| %.3e" % (name, err, peak), flush=True)
+    assert err <= rel * max(peak, 1e-30), (name, err, peak)
+
+
+@pytest.mark.parametrize("k_sel,p_sel,use_a", [(4, 0.8, True), (2, 0.5, False)])
+def test_adaptive_bwd_small_grid(k_sel, p_sel, use_a):
+    w = shrink("adaptive2k", T=8, H=32, W=32, heads=2, fg_radius=8.0, audio_radius=5.0, seed=21)
+    T, H, W = w["T"], w["H"], w["W"]
+    n = T * H * W
+    x = adaptive_inputs(w, DEV)
+    r = run(x, T, H, W, k_sel, p_sel, use_a)
+    g = normal_tensors([(n, 2, 128)], seed=5, device=DEV)[0]
+    dq, dk, dv = J.mmdit_block_sparse_attn_adaptive_bwd(x["q"], x["k"], x["v"], r, g, T, H, W)
+    torch.cuda.synchronize()
+    q64, k64, v64, g64 = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g)
+    codes, ind = A.zone_shapes(v64, f64(x["a"]) if use_a else None, T, H, W)
+    np.testing.assert_array_equal(r["zone_shape"].cpu().numpy().astype(np.int64), codes)
+    assert len(set(ind["volume"].tolist())) >= 2
+    blocks, _ = A.adaptive_block_tokens(T, H, W, codes)
+    P = B.block_probs(A.ragged_means(q64, blocks), A.ragged_means(k64, blocks))
+    m_ref, _, _ = B.select_blocks(P, k_sel, p_sel)
+    blk = np.empty(n, dtype=np.int64)
+    for j, b in enumerate(blocks):
+        blk[b] = j
+    allowed = m_ref[:, blk][:, :, blk]
+    rq, rk, rv = AB.attention_bwd(q64, k64, v64, g64, allowed=allowed)
+    check_rel("dq", f64(dq), rq, REL_GRAD)
+    check_rel("dk", f64(dk), rk, REL_GRAD)
+    check_rel("dv", f64(dv), rv, REL_GRAD)
+
+
+def test_adaptive_bwd_repeat_is_bitwise_identical():
+    w = shrink("adaptive2k", T=8, H=16, W=32, heads=2, fg_radius=5.0, seed=22)
+    T, H, W = w["T"], w["H"], w["W"]
+    x = adaptive_inputs(w, DEV)
+    g = normal_tensors([(T * H * W, 2, 128)], seed=6, device=DEV)[0]
+    r = run(x, T, H, W, 3, 0.7)
+    a = J.mmdit_block_sparse_attn_adaptive_bwd(x["q"], x["k"], x["v"], r, g, T, H, W)
+    b = J.mmdit_block_sparse_attn_adaptive_bwd(x["q"], x["k"], x["v"], r, g, T, H, W)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_adaptive_bwd_full_size_sampled():
+    """The full 24 x 64 x 112 grid: dq of sampled query blocks of two heads
+    against the oracle over their selected keys, and sum_j dv_j = sum_i dO_i
+    for every head (every query's probabilities sum to one)."""
+    w = WORKLOADS["adaptive2k"]
+    T, H, W = w["T"], w["H"], w["W"]
+    n, h = T * H * W, w["heads"]
+    x = adaptive_inputs(w, DEV)
+    r = run(x, T, H, W, w["top_k"], w["top_p"])
+    g = normal_tensors([(n, h, 128)], seed=17, device=DEV)[0]
+    dq, dk, dv = J.mmdit_block_sparse_attn_adaptive_bwd(x["q"], x["k"], x["v"], r, g, T, H, W)
+    torch.cuda.synchronize()
+    codes = r["zone_shape"].cpu().numpy().astype(np.int64)
+    blocks, _ = A.adaptive_block_tokens(T, H, W, codes)
+    heads = [0, 23]
+    q64, k64, v64, g64 = (f64(t[:, heads]) for t in (x["q"], x["k"], x["v"], g))
+    P = B.block_probs(A.ragged_means(q64, blocks), A.ragged_means(k64, blocks))
+    m_ref, _, _ = B.select_blocks(P, w["top_k"], w["top_p"])
+    dq64 = f64(dq[:, heads])
+    rng = np.random.default_rng(2)
+    nb = len(blocks)
+    for hi in range(2):
+        for i in np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, 3, replace=False)])):
+            keys = np.concatenate([blocks[j] for j in np.nonzero(m_ref[hi, i])[0]])
+            qt = blocks[i]
+            sl = np.s_[hi:hi + 1]
+            rq, _, _ = AB.attention_bwd(q64[qt][:, sl], k64[keys][:, sl], v64[keys][:, sl], g64[qt][:, sl])
+            check_rel("dq h%d b%d" % (heads[hi], i), dq64[qt, hi], rq[:, 0], REL_GRAD)
+    sums = dv.double().sum(dim=0).cpu().numpy()
+    check_rel("sum dv", sums, f64(g).sum(axis=0), 1e-3)
