@@ -434,6 +434,33 @@ def adaptive_leg(args, torch, J, w, dev):
 
     t_dense = timed(dense)
     t_ad = timed(adaptive)
+    train = {}
+    if not args.no_train:
+        from synth import normal_tensors
+
+        g = normal_tensors([(n, h, d)], seed=int(w["seed"]) + 7919, device=dev)[0]
+        lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+        dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=dev) for _ in range(3))
+        ws_db = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN_BWD, n, n, h, d, J.MMDIT_BF16),
+                            dtype=torch.uint8, device=dev)
+        ws_ab = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, d,
+                                                    J.MMDIT_BF16), dtype=torch.uint8, device=dev)
+        fwd = {}
+
+        def dense_step():
+            J.mmdit_joint_attn_fwd(q, k, v, o=o, lse=lse, ws=ws_d, stream=stream)
+            J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, dq=dq, dk=dk, dv=dv, ws=ws_db, stream=stream)
+
+        def adaptive_step():
+            fwd.update(J.mmdit_block_sparse_attn_adaptive(q, k, v, T, H, W, a_norm=a, top_k=w["top_k"],
+                                                          top_p=w["top_p"], o=o, lse=lse, ws=ws_a, stream=stream))
+            J.mmdit_block_sparse_attn_adaptive_bwd(q, k, v, fwd, g, T, H, W, dq=dq, dk=dk, dv=dv, ws=ws_ab,
+                                                   stream=stream)
+
+        t_dt, t_at = timed(dense_step), timed(adaptive_step)
+        train = {"train_dense_ms": round(t_dt, 3), "train_adaptive_ms": round(t_at, 3),
+                 "train_speedup": round(t_dt / t_at, 3)}
+        del ws_db, ws_ab, dq, dk, dv
     nt = n // 64
     words = res["sel_mask"].view(torch.uint8).cpu()
     pairs = int(torch.bitwise_and(words[..., None] >> torch.arange(8, dtype=torch.uint8), 1).sum().item())
@@ -447,7 +474,7 @@ def adaptive_leg(args, torch, J, w, dev):
             "blocks": int(res["n_blocks"].item()),
             "dense_ms": round(t_dense, 3), "adaptive_ms": round(t_ad, 3),
             "speedup": round(t_dense / t_ad, 3), "density": round(pairs / (h * nt * nt), 4),
-            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_ad * 1e-9, 1)}
+            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_ad * 1e-9, 1), **train}
 
 
 def sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream):

@@ -47,7 +47,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---- dense attention plan ----------------------------------------------------
 struct AttnPlan {
     int64_t n_pad, n_q_pad;
-    int32_t q_tiles, kv_tiles, splits, tiles_per_split;
+    int32_t q_tile, q_tiles, kv_tiles, splits, tiles_per_split;
     size_t vt_bytes, part_o_bytes, part_ml_bytes;
     size_t total() const { return vt_bytes + part_o_bytes + part_ml_bytes; }
 };
@@ -56,8 +56,9 @@ AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
     AttnPlan p{};
     if (dtype != MMDIT_BF16) return p;   // the fp32 kernel needs no workspace
     p.n_pad = round_up(n_kv, kTileN);
-    p.q_tiles = (int32_t)((n_q + kDenseQ - 1) / kDenseQ);
-    p.n_q_pad = (int64_t)p.q_tiles * kDenseQ;
+    p.q_tile = n_kv <= kShortKv ? kShortQ : kDenseQ;
+    p.q_tiles = (int32_t)((n_q + p.q_tile - 1) / p.q_tile);
+    p.n_q_pad = (int64_t)p.q_tiles * p.q_tile;
     p.kv_tiles = (int32_t)(p.n_pad / kTileN);
     const int64_t base = (int64_t)p.q_tiles * heads;
     int splits = 1;
@@ -136,6 +137,7 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
     a.n_pad = p.n_pad;
     a.n_q_pad = p.n_q_pad;
     a.heads = heads;
+    a.q_tile = p.q_tile;
     a.q_tiles = p.q_tiles;
     a.splits = p.splits;
     a.tiles_per_split = p.tiles_per_split;

@@ -50,10 +50,12 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
     }
 }
 
-template <int HD, int QB>
-__global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArgs a) {
+// NW waves of QB blocks of 32 queries: a workgroup serves 32 NW QB queries.
+// Four-wave workgroups run two per CU, so they must fit two waves per SIMD.
+template <int HD, int QB, int NW>
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs a) {
     using L = TileLayout<HD>;
-    constexpr int NW = dense_threads(QB) / kWave;
+    constexpr int QT = 32 * NW * QB;
     constexpr int KS = HD / 16;
     constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);   // K copies per wave per tile
     constexpr int VCH = HD * 8 / (kWave * NW);                 // V^T copies per wave per tile
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
     const int64_t krb = rstride * 2;                            // bytes per key row
 
     // query row of this lane in query block qb: qrow0 + 32 qb
-    const int64_t qrow0 = (int64_t)qt * kDenseQ + w * 32 * QB + m;
+    const int64_t qrow0 = (int64_t)qt * QT + w * 32 * QB + m;
     bf16x8 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -97,19 +99,25 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
         L::k_at((w * KCH + i) * kWave + lane, row, c);
         krow = (row & ~31) | perm_row(row & 31);
     };
-    uint32_t koff[KCH];
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    // Eight waves keep the offsets in registers; four waves (twice the copies
+    // per wave) recompute them per tile rather than spill.
+    constexpr bool kKeep = NW >= 8;
+    auto k_off = [&](int i) {
         int krow, c;
         k_slot(i, krow, c);
-        koff[i] = (uint32_t)(krow * krb + c * 16);
-    }
-    uint32_t voff[VCH];
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
+        return (uint32_t)(krow * krb + c * 16);
+    };
+    auto v_off = [&](int i) {
         int d, c;
         L::v_at((w * VCH + i) * kWave + lane, d, c);
-        voff[i] = (uint32_t)((d * a.n_pad + c * 8) * 2);
+        return (uint32_t)((d * a.n_pad + c * 8) * 2);
+    };
+    uint32_t koff[kKeep ? KCH : 1], voff[kKeep ? VCH : 1];
+    if constexpr (kKeep) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) koff[i] = k_off(i);
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) voff[i] = v_off(i);
     }
     const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
     const char* vg = reinterpret_cast<const char*>(a.vt + (int64_t)head * HD * a.n_pad);
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
         const char* kt = kg + kv0 * krb;
         if (kv0 + kTileN <= a.n_kv) {
 #pragma unroll
-            for (int i = 0; i < KCH; ++i) dma16(kt + koff[i], lb + (w * KCH + i) * 1024);
+            for (int i = 0; i < KCH; ++i) dma16(kt + (kKeep ? koff[i] : k_off(i)), lb + (w * KCH + i) * 1024);
         } else {   // rows past n_kv re-read the last real row; their scores are masked
             const int last = (int)(a.n_kv - kv0) - 1;
 #pragma unroll
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(dense_threads(QB), 1) void attn_bf16_kernel(AttnArg
     auto issue_v = [&](int t, char* lb) {
         const char* vt = vg + (int64_t)t * kTileN * 2;
 #pragma unroll
-        for (int i = 0; i < VCH; ++i) dma16(vt + voff[i], lb + (w * VCH + i) * 1024);
+        for (int i = 0; i < VCH; ++i) dma16(vt + (kKeep ? voff[i] : v_off(i)), lb + (w * VCH + i) * 1024);
     };
 
     FragAddr<HD> fa;
@@ -307,11 +315,18 @@ hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int hea
 hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s) {
     const int total = a.q_tiles * a.heads * a.splits;
     const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
-    constexpr int QB = kDenseQB;
-    if (hd == 128)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, QB>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
-    else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, QB>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
+    constexpr int QB = kDenseQB, NW = dense_threads(QB) / kWave, NS = kShortQ / 32;
+    if (a.q_tile == kShortQ) {
+        // two workgroups per CU: kShortQ queries each
+        if (hd == 128)
+            hipLaunchKernelGGL((attn_bf16_kernel<128, 1, NS>), dim3(blocks), dim3(NS * kWave), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_bf16_kernel<64, 1, NS>), dim3(blocks), dim3(NS * kWave), 0, s, a);
+    } else if (hd == 128) {
+        hipLaunchKernelGGL((attn_bf16_kernel<128, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((attn_bf16_kernel<64, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
+    }
     return hipGetLastError();
 }
 

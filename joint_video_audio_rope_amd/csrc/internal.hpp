@@ -33,6 +33,12 @@ constexpr int kTileN = 64;
 constexpr int kDenseQ = 256;
 constexpr int kDenseQB = 1;
 constexpr int dense_threads(int qb) { return kDenseQ / (32 * qb) * kWave; }
+// Calls with at most kShortKv keys (video -> text, video -> audio) use
+// workgroups of kShortQ queries (4 waves), two per CU at the same two waves
+// per SIMD: with only a few key tiles per workgroup, one workgroup's Q loads
+// and O stores then overlap the other's products.
+constexpr int kShortQ = 128;
+constexpr int kShortKv = 1024;
 
 // ---- RoPE ------------------------------------------------------------------
 struct RopeSeg {
@@ -70,11 +76,12 @@ struct AttnArgs {
     float* lse;            // [heads][n_q] natural-log log-sum-exp, or null
     int64_t n_q, n_kv, n_pad, n_q_pad;
     int32_t heads;
-    int32_t q_tiles;       // ceil(n_q / kDenseQ)
+    int32_t q_tiles;       // ceil(n_q / q_tile)
     int32_t splits;
     int32_t tiles_per_split;
     int32_t kv_tiles;
     float scale_log2;      // softmax scale * log2(e)
+    int32_t q_tile;        // queries per workgroup: kDenseQ or kShortQ
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s);
@@ -109,6 +116,7 @@ struct BwdArgs {
     int32_t heads;
     float scale;           // softmax scale
     float scale_log2;      // softmax scale * log2(e)
+    int32_t q_tile;        // queries per workgroup: kDenseQ or kShortQ
 };
 
 // D = <dO, O> (and, when ls2 is not null, lse * log2(e)) per (head, query),
