@@ -168,6 +168,19 @@ def test_ragged_and_split_shapes(nq, nkv, h, d):
     assert np.max(np.abs(f64(o) - ref)) <= TOL_BF16
 
 
+@pytest.mark.parametrize("nq,nkv,h", [(127, 1024, 2), (129, 1025, 2), (128, 1023, 3), (385, 512, 2), (10, 1024, 2)])
+def test_short_key_boundary_with_lse(nq, nkv, h):
+    """Key sets of at most 1024 keys run in 128-query workgroups, longer ones in
+    256-query workgroups; (10, 1024) also splits the keys across workgroups."""
+    from oracle import attention_bwd as AB
+    q, k, v = _rand((nq, h, 128), 20), _rand((nkv, h, 128), 21), _rand((nkv, h, 128), 22)
+    o, lse = J.mmdit_joint_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = AB.attention_fwd_lse(f64(q), f64(k), f64(v))
+    assert np.max(np.abs(f64(o) - o_ref)) <= TOL_BF16
+    assert np.max(np.abs(f64(lse) - lse_ref)) <= 2e-3
+
+
 def test_single_key_and_empty_queries():
     q, k, v = _rand((200, 2, 128), 13), _rand((1, 2, 128), 14), _rand((1, 2, 128), 15)
     o = J.mmdit_joint_attn(q, k, v)
