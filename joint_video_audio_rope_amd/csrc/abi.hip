@@ -56,7 +56,7 @@ AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
     AttnPlan p{};
     if (dtype != MMDIT_BF16) return p;   // the fp32 kernel needs no workspace
     p.n_pad = round_up(n_kv, kTileN);
-    p.q_tile = n_kv <= kShortKv ? kShortQ : kDenseQ;
+    p.q_tile = (n_kv <= kShortKv || n_q <= kDenseQ) ? kShortQ : kDenseQ;
     p.q_tiles = (int32_t)((n_q + p.q_tile - 1) / p.q_tile);
     p.n_q_pad = (int64_t)p.q_tiles * p.q_tile;
     p.kv_tiles = (int32_t)(p.n_pad / kTileN);

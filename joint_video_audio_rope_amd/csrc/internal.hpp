@@ -36,7 +36,8 @@ constexpr int dense_threads(int qb) { return kDenseQ / (32 * qb) * kWave; }
 // Calls with at most kShortKv keys (video -> text, video -> audio) use
 // workgroups of kShortQ queries (4 waves), two per CU at the same two waves
 // per SIMD: with only a few key tiles per workgroup, one workgroup's Q loads
-// and O stores then overlap the other's products.
+// and O stores then overlap the other's products.  So do calls with at most
+// kDenseQ queries (audio -> video), whose keys are split across workgroups.
 constexpr int kShortQ = 128;
 constexpr int kShortKv = 1024;
 
