@@ -138,7 +138,9 @@ mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* desc, float* host_t
  * as in mmdit_joint_attn (also for mmdit_joint_attn_fwd).  JOINT_ATTN_BWD: as
  * in mmdit_joint_attn_bwd.  AV_CROSS_ATTN: n_q = n_video, n_kv = n_audio.
  * BLOCK_SPARSE_ATTN and BLOCK_SPARSE_ATTN_BWD: n_q = n_kv = T*H*W and `sp`
- * gives the block geometry. */
+ * gives the block geometry.  BLOCK_SPARSE_ATTN_ADAPTIVE and
+ * BLOCK_SPARSE_ATTN_ADAPTIVE_BWD: n_q = T*H*W; n_kv, dtype and `sp` are not
+ * read. */
 size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
                              int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp);
 
