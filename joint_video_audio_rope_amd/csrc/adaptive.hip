@@ -30,7 +30,6 @@
 // so the discrete choices (volume, shape) are taken in the same precision as
 // the double-precision reference.
 #include "internal.hpp"
-#include "attn_core.hpp"
 
 namespace mmdit {
 
