@@ -274,6 +274,13 @@ def test_block_sparse_full_size():
     assert 0.05 < dens < 0.9
 
 
+def test_block_sparse_maximum_blocks():
+    """4096 blocks per head, the most a selection row may hold (64 per lane)."""
+    w = shrink("sparse2k", T=16, H=128, W=128, heads=1, seed=9)
+    c = _sparse_check(w, 32, 0.9, n_qblocks=8)
+    assert c.shape == (1, 4096)
+
+
 def _sparse_tie_case(w, k_sel, p_sel, twin):
     """Key blocks copied onto other key blocks give bitwise-equal block
     probabilities; the selection must take equal values in ascending block id
