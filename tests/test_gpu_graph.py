@@ -82,3 +82,31 @@ def test_graph_replays_match_eager():
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), (rep, i)
         assert torch.equal(ad["zone_shape"], want_shape) and torch.equal(ad["sel_mask"], want_mask), rep
+
+
+def test_two_streams_match_one():
+    """Independent calls on two streams at once (separate workspaces) give the
+    same bits as the same calls one after the other: the library keeps no
+    state between calls."""
+    w = WORKLOADS["block"]
+    x = joint_inputs(w, DEV)
+    q, k, v = x["q"], x["k"], x["v"]
+    n, h, d = q.shape
+    ws_s = shrink("sparse2k", T=8, H=32, W=32, heads=4, seed=33)
+    xs = sparse_inputs(ws_s, DEV)
+    seq_o = J.mmdit_joint_attn(q, k, v)
+    seq_s, seq_m, seq_c = J.mmdit_block_sparse_attn(xs["q"], xs["k"], xs["v"], 8, 32, 32, top_k=4, top_p=0.8)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    a.wait_stream(torch.cuda.current_stream())
+    b.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(a):
+            o = J.mmdit_joint_attn(q, k, v)
+        with torch.cuda.stream(b):
+            s, m, c = J.mmdit_block_sparse_attn(xs["q"], xs["k"], xs["v"], 8, 32, 32, top_k=4, top_p=0.8)
+        outs.append((o, s, m, c))
+    torch.cuda.synchronize()
+    for o, s, m, c in outs:
+        assert torch.equal(o, seq_o) and torch.equal(s, seq_s) and torch.equal(m, seq_m) and torch.equal(c, seq_c)
