@@ -144,6 +144,19 @@ mmdit_status mmdit_rope3d_build_table(const mmdit_rope_desc* desc, float* host_t
 size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t heads,
                              int32_t head_dim, int32_t dtype, const mmdit_sparse_desc* sp);
 
+/* Host-side tile table of a content-adaptive grid (see
+ * mmdit_block_sparse_attn_adaptive for the tiling): for the zone shape codes
+ * zone_shape [T*H*W/512] (host memory, a forward call's output copied back),
+ * tile s (nt = T*H*W/64 tiles) holds the tokens tile_base[s] + offset(r),
+ * r = 0..63 in raster order over a box of 2^(d & 3) x 2^((d >> 2) & 3) x
+ * 2^((d >> 4) & 3) tokens along (t, h, w), d = tile_dims[s], offset(r) =
+ * (a*H + b)*W + c for the box coordinates (a, b, c) of r; tile_block[s] is the
+ * tile's block.  The same arithmetic the library's kernels use.  Output arrays
+ * are host memory of nt entries and may be NULL.  T, H, W must be multiples
+ * of 8; codes above 15 are rejected. */
+mmdit_status mmdit_adaptive_tile_table(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
+                                       int32_t* tile_base, uint8_t* tile_dims, int32_t* tile_block);
+
 /* ---- device calls (async on `stream`) ------------------------------------- */
 
 /* Time-shifted 3D RoPE, in place on q and k ([n_tokens][heads][head_dim]).

@@ -10,7 +10,8 @@ the first call does (and raises if the library was not built).
 """
 from ._lib import (  # noqa: F401
     MmditError, RopeSpec, layout_segments, lib, mmdit_abi_version, mmdit_av_cross_attn,
-    mmdit_block_sparse_attn, mmdit_block_sparse_attn_adaptive, mmdit_block_sparse_attn_adaptive_bwd,
+    mmdit_adaptive_tile_table, mmdit_block_sparse_attn, mmdit_block_sparse_attn_adaptive,
+    mmdit_block_sparse_attn_adaptive_bwd,
     mmdit_block_sparse_attn_bwd,
     mmdit_block_sparse_attn_fwd, mmdit_joint_attn, mmdit_joint_attn_bwd, mmdit_joint_attn_fwd, mmdit_last_error,
     mmdit_rope3d, mmdit_rope3d_build_table, mmdit_rope3d_table_floats, mmdit_token_norms, mmdit_workspace_bytes,

@@ -98,6 +98,8 @@ def lib():
         L.mmdit_block_sparse_attn_bwd.restype = i32
         L.mmdit_block_sparse_attn_bwd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, ctypes.POINTER(SparseDesc),
                                                   f64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mmdit_adaptive_tile_table.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+        L.mmdit_adaptive_tile_table.restype = i32
         L.mmdit_token_norms.argtypes = [vp, i64, i64, vp, vp]
         L.mmdit_token_norms.restype = i32
         L.mmdit_block_sparse_attn_adaptive.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, f64,
@@ -373,6 +375,21 @@ def mmdit_block_sparse_attn_fwd(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4
                                              _ptr(o), _ptr(lse), _ptr(sel_mask), _ptr(sel_count), _ptr(ws), wsb,
                                              _stream(stream)))
     return o, lse, sel_mask, sel_count
+
+
+def mmdit_adaptive_tile_table(T, H, W, zone_shape):
+    """Host-side tile table of an adaptive grid: (tile_base int32 [nt],
+    tile_dims uint8 [nt], tile_block int32 [nt]) numpy arrays for the zone
+    shape codes (uint8, any array-like of T*H*W/512 entries)."""
+    import numpy as np
+    codes = np.ascontiguousarray(np.asarray(zone_shape, dtype=np.uint8))
+    nt = T * H * W // 64
+    base = np.empty(nt, dtype=np.int32)
+    dims = np.empty(nt, dtype=np.uint8)
+    block = np.empty(nt, dtype=np.int32)
+    cp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().mmdit_adaptive_tile_table(T, H, W, cp(codes), cp(base), cp(dims), cp(block)))
+    return base, dims, block
 
 
 def mmdit_token_norms(x, out=None, stream=None):

@@ -826,6 +826,38 @@ mmdit_status mmdit_block_sparse_attn_fwd(const void* q, const void* k, const voi
                       ws_bytes, stream, "block_sparse_fwd");
 }
 
+mmdit_status mmdit_adaptive_tile_table(int32_t T, int32_t H, int32_t W, const uint8_t* zone_shape,
+                                       int32_t* tile_base, uint8_t* tile_dims, int32_t* tile_block) {
+    if (T < 1 || H < 1 || W < 1 || T % kZoneEdge || H % kZoneEdge || W % kZoneEdge)
+        return fail(MMDIT_ERR_INVALID_ARG, "adaptive_tile_table: T, H, W must be positive multiples of %d",
+                    kZoneEdge);
+    const int64_t n = (int64_t)T * H * W;
+    if (n >= ((int64_t)1 << 31)) return fail(MMDIT_ERR_UNSUPPORTED, "adaptive_tile_table: grid too large");
+    if (!zone_shape) return fail(MMDIT_ERR_INVALID_ARG, "adaptive_tile_table: null zone_shape");
+    const int64_t nz = n / (kZoneTiles * kTileN);
+    for (int64_t m = 0; m < nz; ++m)
+        if (zone_shape[m] > 15)
+            return fail(MMDIT_ERR_INVALID_ARG, "adaptive_tile_table: zone %lld has shape code %d (0..15)",
+                        (long long)m, (int)zone_shape[m]);
+    SparseGeom g{};
+    g.T = T, g.H = H, g.W = W;
+    g.nzh = H / kZoneEdge, g.nzw = W / kZoneEdge;
+    int32_t blocks = 0;
+    for (int64_t m = 0; m < nz; ++m) {
+        for (int u = 0; u < kZoneTiles; ++u) {
+            const int s = (int)(m * kZoneTiles + u);
+            const TileGeom tg = tile_geom(g, s, zone_shape[m]);
+            if (tile_base) tile_base[s] = (int32_t)tg.base;
+            if (tile_dims) tile_dims[s] = (uint8_t)tg.dims;
+            if (tile_block) tile_block[s] = blocks + tg.blk;
+        }
+        int lt, lh, lw;
+        adaptive_candidate(zone_shape[m], lt, lh, lw);
+        blocks += 1 << (9 - (lt + lh + lw));
+    }
+    return MMDIT_OK;
+}
+
 mmdit_status mmdit_token_norms(const float* x, int64_t n, int64_t width, float* out, void* stream) {
     if (n < 0 || width < 4 || width % 4)
         return fail(MMDIT_ERR_INVALID_ARG, "token_norms: n >= 0 and width a positive multiple of 4 required");

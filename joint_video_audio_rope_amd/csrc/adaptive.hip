@@ -39,56 +39,12 @@ constexpr double kTau128 = 0.5;
 constexpr double kTau256 = 0.25;
 constexpr double kEps = 1e-6;
 
-// log2 edges of the 16 candidates, volume 64 (7), 128 (6), 256 (3), each
-// group in lexicographic (b_T, b_H, b_W) order.
-__constant__ uint8_t kCand[16][3] = {
-    {1, 2, 3}, {1, 3, 2}, {2, 1, 3}, {2, 2, 2}, {2, 3, 1}, {3, 1, 2}, {3, 2, 1},
-    {1, 3, 3}, {2, 2, 3}, {2, 3, 2}, {3, 1, 3}, {3, 2, 2}, {3, 3, 1},
-    {2, 3, 3}, {3, 2, 3}, {3, 3, 2}};
-
 __device__ __forceinline__ int64_t zone_origin(const SparseGeom& g, int m) {
     const int zt = m / (g.nzh * g.nzw);
     const int zr = m - zt * (g.nzh * g.nzw);
     const int zh = zr / g.nzw;
     const int zw = zr - zh * g.nzw;
     return ((int64_t)(zt * kZoneEdge) * g.H + zh * kZoneEdge) * g.W + zw * kZoneEdge;
-}
-
-// Geometry of tile s (zone s / 8, tile s % 8 of the zone) for zone shape
-// code `code`: the raster index of its first token, its log2 edges
-// (t | h << 2 | w << 4), its index inside its block and its block's index
-// inside the zone.
-struct TileGeom {
-    int64_t base;
-    uint32_t dims;
-    int sub, blk;
-};
-
-__device__ __forceinline__ TileGeom tile_geom(const SparseGeom& g, int s, int code) {
-    const int zm = s / kZoneTiles, u = s - zm * kZoneTiles;
-    const uint8_t* c = kCand[code];
-    const int lbt = c[0], lbh = c[1], lbw = c[2];
-    const int split = lbt + lbh + lbw - 6;   // tiles per block = 2^split
-    const int blk = u >> split, sub = u & ((1 << split) - 1);
-    // position of the block inside the zone, raster over (8 >> lbt, 8 >> lbh, 8 >> lbw)
-    const int nbh = 8 >> lbh, nbw = 8 >> lbw;
-    const int pt = blk / (nbh * nbw), ph = (blk / nbw) % nbh, pw = blk % nbw;
-    // tile edges: halve the longest edge (first of t, h, w) split times
-    int lt = lbt, lh = lbh, lw = lbw;
-    for (int i = 0; i < split; ++i) {
-        if (lt >= lh && lt >= lw) --lt;
-        else if (lh >= lw) --lh;
-        else --lw;
-    }
-    const int qh_n = 1 << (lbh - lh), qw_n = 1 << (lbw - lw);
-    const int qt = sub / (qh_n * qw_n), qh = (sub / qw_n) % qh_n, qw = sub % qw_n;
-    const int t = (pt << lbt) + (qt << lt), h = (ph << lbh) + (qh << lh), w = (pw << lbw) + (qw << lw);
-    TileGeom r;
-    r.base = zone_origin(g, zm) + ((int64_t)t * g.H + h) * g.W + w;
-    r.dims = (uint32_t)(lt | (lh << 2) | (lw << 4));
-    r.sub = sub;
-    r.blk = blk;
-    return r;
 }
 
 // Sum over 8 positions of (mean at the position - zone mean)^2, / 8.
@@ -248,11 +204,13 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
         int best = lb == 6 ? 0 : lb == 7 ? 7 : 13;
         double bd = __builtin_inf();
         for (int i = 0; i < 16; ++i) {
-            if (kCand[i][0] + kCand[i][1] + kCand[i][2] != lb) continue;
+            int e[3];
+            adaptive_candidate(i, e[0], e[1], e[2]);
+            if (e[0] + e[1] + e[2] != lb) continue;
             double dist = 0.0;
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
-                const double diff = (double)kCand[i][d] - (-0.5 * lg[d] + c3);
+                const double diff = (double)e[d] - (-0.5 * lg[d] + c3);
                 dist += diff * diff;
             }
             if (dist < bd) bd = dist, best = i;

@@ -192,6 +192,60 @@ struct AdaptiveWs {
     int32_t* nblocks;  // [1] number of blocks
 };
 
+// log2 edges (t, h, w) of content-adaptive candidate `code`: volume 64 (codes
+// 0-6), 128 (7-12), 256 (13-15), each group in lexicographic (b_T, b_H, b_W)
+// order of the boxes with edges in {2, 4, 8}.
+__host__ __device__ __forceinline__ void adaptive_candidate(int code, int& lt, int& lh, int& lw) {
+    constexpr uint8_t kCand[16] = {0x39, 0x2D, 0x36, 0x2A, 0x1E, 0x27, 0x1B,   // t | h << 2 | w << 4
+                                   0x3D, 0x3A, 0x2E, 0x37, 0x2B, 0x1F, 0x3E, 0x3B, 0x2F};
+    const int c = kCand[code];
+    lt = c & 3, lh = (c >> 2) & 3, lw = (c >> 4) & 3;
+}
+
+// Geometry of tile s (zone s / 8, tile s % 8 of the zone, zones in raster
+// order over a grid of whole 8 x 8 x 8 zones) for zone shape `code`: the
+// raster index of its first token, its log2 edges (t | h << 2 | w << 4), its
+// index inside its block and its block's index inside the zone.  A block of
+// B tokens is B / 64 tiles: its longest edge halved (the first of t, h, w
+// among equals) once per factor of two, tiles in raster order inside the
+// block, blocks in raster order of their position in the zone.
+struct TileGeom {
+    int64_t base;
+    uint32_t dims;
+    int sub, blk;
+};
+
+__host__ __device__ __forceinline__ TileGeom tile_geom(const SparseGeom& g, int s, int code) {
+    const int zm = s / kZoneTiles, u = s - zm * kZoneTiles;
+    int lbt, lbh, lbw;
+    adaptive_candidate(code, lbt, lbh, lbw);
+    const int split = lbt + lbh + lbw - 6;   // tiles per block = 2^split
+    const int blk = u >> split, sub = u & ((1 << split) - 1);
+    // position of the block inside the zone, raster over (8 >> lbt, 8 >> lbh, 8 >> lbw)
+    const int nbh = 8 >> lbh, nbw = 8 >> lbw;
+    const int pt = blk / (nbh * nbw), ph = (blk / nbw) % nbh, pw = blk % nbw;
+    // tile edges: halve the longest edge (first of t, h, w) split times
+    int lt = lbt, lh = lbh, lw = lbw;
+    for (int i = 0; i < split; ++i) {
+        if (lt >= lh && lt >= lw) --lt;
+        else if (lh >= lw) --lh;
+        else --lw;
+    }
+    const int qh_n = 1 << (lbh - lh), qw_n = 1 << (lbw - lw);
+    const int qt = sub / (qh_n * qw_n), qh = (sub / qw_n) % qh_n, qw = sub % qw_n;
+    const int t = (pt << lbt) + (qt << lt), h = (ph << lbh) + (qh << lh), w = (pw << lbw) + (qw << lw);
+    const int zt = zm / (g.nzh * g.nzw);
+    const int zr = zm - zt * (g.nzh * g.nzw);
+    const int zh = zr / g.nzw;
+    const int zw = zr - zh * g.nzw;
+    TileGeom r;
+    r.base = ((int64_t)(zt * kZoneEdge + t) * g.H + zh * kZoneEdge + h) * g.W + zw * kZoneEdge + w;
+    r.dims = (uint32_t)(lt | (lh << 2) | (lw << 4));
+    r.sub = sub;
+    r.blk = blk;
+    return r;
+}
+
 // Per zone channel statistics of V and the audio norms a (may be null), then
 // the one-workgroup pass that turns them into volumes, shapes and tile tables.
 hipError_t launch_zone_stats(const SparseGeom& g, const __bf16* v, const float* a, int hd, const AdaptiveWs& w,
@@ -236,7 +290,7 @@ hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStr
 
 // Offset from a tile's first token of its local token r (raster inside the
 // tile) for a tile with log2 edges code = lt | lh << 2 | lw << 4.
-__device__ __forceinline__ int64_t tile_local(const SparseGeom& g, uint32_t code, int r) {
+__host__ __device__ __forceinline__ int64_t tile_local(const SparseGeom& g, uint32_t code, int r) {
     const int lh = (code >> 2) & 3, lw = (code >> 4) & 3;
     const int a = r >> (lh + lw);
     const int b = (r >> lw) & ((1 << lh) - 1);

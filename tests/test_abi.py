@@ -30,7 +30,7 @@ def test_header_declares_the_calls():
     for n in ("mmdit_rope3d", "mmdit_joint_attn", "mmdit_av_cross_attn", "mmdit_block_sparse_attn",
               "mmdit_joint_attn_fwd", "mmdit_joint_attn_bwd", "mmdit_block_sparse_attn_fwd",
               "mmdit_block_sparse_attn_bwd", "mmdit_block_sparse_attn_adaptive", "mmdit_token_norms",
-              "mmdit_block_sparse_attn_adaptive_bwd",
+              "mmdit_block_sparse_attn_adaptive_bwd", "mmdit_adaptive_tile_table",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
               "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
         assert n in names
@@ -378,3 +378,40 @@ def test_adaptive_bwd_workspace_plan():
     need = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, 128, J.MMDIT_BF16, None)
     assert need == want
     assert _adaptive_bwd_call(ws_bytes=need - 1) == L.MMDIT_ERR_WORKSPACE
+
+
+def _tile_tokens(H, W, base, dims):
+    """Tokens of one tile from its first token and log2 edges (the header's formula)."""
+    lt, lh, lw = dims & 3, (dims >> 2) & 3, (dims >> 4) & 3
+    out = []
+    for r in range(64):
+        a, b, c = r >> (lh + lw), (r >> lw) & ((1 << lh) - 1), r & ((1 << lw) - 1)
+        out.append(int(base) + (a * H + b) * W + c)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_adaptive_tile_table_matches_oracle_partition(seed):
+    """The library's tile arithmetic (the same functions its kernels run)
+    reproduces the oracle's blocks: the tiles of block b hold exactly the
+    oracle's tokens of block b, and every zone has 8 tiles."""
+    from oracle import adaptive_blocks as AD
+    rng = np.random.default_rng(seed)
+    T, H, W = 8 * int(rng.integers(1, 3)), 8 * int(rng.integers(1, 4)), 8 * int(rng.integers(1, 4))
+    nz = T * H * W // 512
+    codes = np.arange(nz) % 16 if seed == 0 else rng.integers(0, 16, nz)
+    base, dims, block = J.mmdit_adaptive_tile_table(T, H, W, codes.astype(np.uint8))
+    blocks, _ = AD.adaptive_block_tokens(T, H, W, codes)
+    assert block.max() + 1 == len(blocks) and np.all(np.diff(block) >= 0)
+    got = {}
+    for s in range(len(base)):
+        got.setdefault(int(block[s]), []).extend(_tile_tokens(H, W, base[s], int(dims[s])))
+    for b, toks in enumerate(blocks):
+        assert sorted(got[b]) == sorted(toks.tolist()), (seed, b)
+
+
+def test_adaptive_tile_table_rejects_bad_input():
+    with pytest.raises(L.MmditError, match="multiples of 8"):
+        J.mmdit_adaptive_tile_table(8, 8, 12, [3])
+    with pytest.raises(L.MmditError, match="shape code"):
+        J.mmdit_adaptive_tile_table(8, 8, 16, [3, 16])
