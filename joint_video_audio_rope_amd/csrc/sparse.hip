@@ -198,7 +198,7 @@ constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup
 // average 0.73 (pairs), 0.62 (triples), 0.50 (4 blocks) of the tiles its
 // blocks select; with workgroup barriers per tile, pairs (two workgroups per
 // CU) took 164 ms and groups of 4 (idle waves on tiles only some blocks
-// selected) 205 ms, while groups of 4 fed by a producer wave take 142 ms.
+// selected) 205 ms, while groups of 4 fed by producer waves take 132-134 ms.
 constexpr int kStreamGroup = 4;
 constexpr int kStreamRing = 4;
 
@@ -425,22 +425,30 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     }
 }
 
-// Sparse attention with a producer wave.  A workgroup serves G consecutive
+// Sparse attention with producer waves.  A workgroup serves G consecutive
 // query blocks of one head with 2 G consumer waves (waves 2 b, 2 b + 1 own
-// block G p + b) and one producer wave.  The producer streams the union of
-// the G selections, in ascending block id, into a ring of R LDS tiles (K rows
-// gathered from the raster layout, the block's fp16 V^T); consumers follow the
-// same walk and compute only the tiles their block selected.  There is no
-// workgroup barrier in the walk: the producer publishes each landed tile
-// through an LDS flag, and reuses a ring slot once every consumer has released
-// the tile in it, so the consumers run up to R - 1 tiles apart and none waits
-// on another's compute except through a full ring.  Larger groups share each
-// staged tile among more blocks (a tile costs the same 32 KB however many
-// blocks use it), and the decoupled walk keeps the waves of blocks that did
-// not select a tile from idling on it.
+// block G p + b) and two producer waves.  The producers stream the union of
+// the G selections, in ascending block id, into a ring of R LDS tiles (the
+// block's K rows and fp16 V^T, each one contiguous image); producer p copies
+// the tiles t with t % 2 == p.  Consumers follow the same walk and compute
+// only the tiles their block selected.  There is no workgroup barrier in the
+// walk: a producer publishes each tile through its slot's LDS flag and reuses
+// a slot once every consumer has released the tile in it, so the consumers
+// run up to R - 1 tiles apart and none waits on another's compute except
+// through a full ring.  A producer publishes its previous tile as soon as its
+// copies have landed, before it waits for the slot of its next tile: when
+// publication waited behind that slot, a tile became visible only after the
+// consumers had released the tiles ahead of it, which shrank the consumers'
+// lead (4 % slower with one producer).  Two producers keep two tiles' copies
+// in flight (one more 1.3 % on the 24 x 64 x 112 grid; three or four gain no
+// more).  Larger groups share each staged tile among more blocks (a tile
+// costs the same 32 KB however many blocks use it), and the decoupled walk
+// keeps the waves of blocks that did not select a tile from idling on it.
 //
-// Flags: ready[s] = t + 1 once tile t (slot s = t mod R) has landed;
-// released[s] counts consumer waves done with slot s over all its uses.
+// Flags: ready[s] = t + 1 once tile t (slot s = t mod R) has landed (slots
+// are written in increasing t: tile t + R is issued only after every consumer
+// released tile t, which follows its publication); released[s] counts
+// consumer waves done with slot s over all its uses.
 constexpr int kSpinLimit = 1 << 18;
 typedef __attribute__((address_space(3))) int lds_int;
 
@@ -478,11 +486,11 @@ __device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken) {
 }
 
 template <int HD, int G, int R>
-__global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_kernel(
+__global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_kernel(
         SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
         SparseWs w, float* __restrict__ o, float* __restrict__ lse) {
     using L = TileLayout<HD>;
-    constexpr int NC = 2 * G;                          // consumer waves; wave NC produces
+    constexpr int NC = 2 * G;                          // consumer waves; waves NC, NC + 1 produce
     constexpr int KS = HD / 16;
     constexpr int KCP = kTileN * L::kKChunks / kWave;  // producer copies per tile: K
     constexpr int VCP = HD * 8 / kWave;                //                          V^T
@@ -502,7 +510,7 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     const int b0 = G * grp;
 
     const uint32_t* mrow = w.mask + ((int64_t)head * g.nb + b0) * nw;
-    for (int i = threadIdx.x; i < G * nw; i += (NC + 1) * kWave) {
+    for (int i = threadIdx.x; i < G * nw; i += (NC + 2) * kWave) {
         const int sd = i / nw, wd = i - (i / nw) * nw;
         msk[sd][wd] = (b0 + sd < g.nb) ? mrow[sd * nw + wd] : 0u;
     }
@@ -536,16 +544,10 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
         return word * 32 + b;
     };
     auto ready_at = [&](int s) { return (lds_int*)&ready[s]; };
-    // Tiles are published in order, so every tile up to the largest flag
-    // minus one has been published: one read of the R flags clears a run.
-    int pub = -1;
+    // tile t is published once its slot's flag reaches t + 1
     auto wait_published = [&](int t) {
-        for (int i = 0; t > pub; ++i) {
-            int hi = 0;
-#pragma unroll
-            for (int s2 = 0; s2 < R; ++s2) hi = max(hi, lds_load(ready_at(s2)));
-            pub = __builtin_amdgcn_readfirstlane(hi) - 1;
-            if (t <= pub) break;
+        for (int i = 0;; ++i) {
+            if (__builtin_amdgcn_readfirstlane(lds_load(ready_at(t & (R - 1)))) >= t + 1) break;
             if (__builtin_amdgcn_readfirstlane(lds_load((lds_int*)&broken)) != 0) break;
             if (i == kSpinLimit) {
                 __hip_atomic_store((lds_int*)&broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -558,13 +560,15 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
     auto released_at = [&](int s) { return (lds_int*)&released[s]; };
     lds_int* brk = (lds_int*)&broken;
 
-    if (wv == NC) {
-        // ---- producer: all copies of every tile ----
-        // K image and V^T of a block are contiguous 16 KB runs laid out as
-        // the LDS tile: copy i of a lane moves bytes 1024 i + 16 lane
-        int t = 0;
+    if (wv >= NC) {
+        // ---- producers: wave NC + p copies the tiles t with t % 2 == p ----
+        const int pp = wv - NC;
+        int t = 0, last = -1;
         for (int j = advance(); j >= 0; j = advance(), ++t) {
+            if (t % 2 != pp) continue;
             const int sl = t & (R - 1);
+            // publish this producer's previous tile once it has landed
+            if (last >= 0) publish_after<0>(ready_at(last & (R - 1)), last + 1);
             if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk);   // tile t - R is done
             char* lb = lds + sl * L::kBytes;
             const int64_t blk = (int64_t)head * g.nb + j;
@@ -574,10 +578,9 @@ __global__ __launch_bounds__((2 * G + 1) * kWave, 1) void sparse_attn_stream_ker
             const char* vt = reinterpret_cast<const char*>(w.vt + blk * (HD * kTileN)) + 16 * lane;
 #pragma unroll
             for (int i = 0; i < VCP; ++i) dma16(vt + i * 1024, lb + L::kKBytes + i * 1024);
-            // tile t - 1 has landed once only tile t's copies are outstanding
-            if (t >= 1) publish_after<KCP + VCP>(ready_at((t - 1) & (R - 1)), t);
+            last = t;
         }
-        if (t >= 1) publish_after<0>(ready_at((t - 1) & (R - 1)), t);
+        if (last >= 0) publish_after<0>(ready_at(last & (R - 1)), last + 1);
         return;
     }
 
@@ -694,7 +697,7 @@ hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
     const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
-    hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 1) * kWave), 0, s, g,
+    hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g,
                        q, k, scale_log2, w, o, lse);
     return hipGetLastError();
 }
