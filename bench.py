@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0         # the clock the published peaks assume
 
 
 def attn_flops(nq, nk, heads, d):
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--sparse-reps", type=int, default=3)
     ap.add_argument("--no-adaptive", action="store_true", help="skip the content-adaptive block-shape leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the GPU clock and socket power under sustained joint and sparse attention")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows of the oracle sample (all heads, all keys)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -84,6 +87,77 @@ def measured_traffic():
 
 
 COPY_BYTES = 1 << 30            # the probe's device copy: 1 GiB read + 1 GiB written
+
+
+def parse_smi_metrics(text):
+    """Mean gfx clock (MHz, over the XCDs) and socket power (W) from the JSON of
+    `amd-smi metric -c -p --json`; None for a value the text does not hold."""
+    try:
+        doc = json.loads(text)
+    except ValueError:
+        return None, None
+    clocks, power = [], []
+
+    def walk(o, path):
+        if isinstance(o, dict):
+            for key, val in o.items():
+                walk(val, path + (str(key),))
+        elif isinstance(o, list):
+            for val in o:
+                walk(val, path)
+        elif isinstance(o, (int, float)) and path[-1:] == ("value",):
+            if len(path) >= 4 and path[-2] == "clk" and path[-3].startswith("gfx_") and path[-4] == "clock":
+                clocks.append(float(o))
+            elif len(path) >= 3 and path[-2] == "socket_power" and path[-3] == "power":
+                power.append(float(o))
+
+    walk(doc, ())
+    return (sum(clocks) / len(clocks) if clocks else None), (power[0] if power else None)
+
+
+def clock_under(torch, fn, seconds=3.0):
+    """Run fn back to back for about `seconds` while a host thread samples the
+    gfx clock and socket power through amd-smi (a child process); returns the
+    means over the samples taken while the GPU was busy, or None without amd-smi."""
+    import shutil
+    import subprocess
+    import threading
+    import time
+    smi = shutil.which("amd-smi")
+    if smi is None:
+        return None
+    samples, busy, stop = [], [False], [False]
+
+    def sampler():
+        while not stop[0]:
+            try:
+                txt = subprocess.run([smi, "metric", "-c", "-p", "--json"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            if busy[0]:
+                samples.append(parse_smi_metrics(txt))
+            time.sleep(0.2)
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        if time.time() - t0 > 0.5:
+            busy[0] = True                   # let the clock settle first
+        fn()
+        torch.cuda.synchronize()
+    busy[0] = False
+    stop[0] = True
+    th.join(timeout=30)
+    mhz = [c for c, _ in samples if c is not None]
+    watts = [p for _, p in samples if p is not None]
+    if not mhz:
+        return None
+    return {"gfx_mhz": round(sum(mhz) / len(mhz)), "socket_w": round(sum(watts) / len(watts)) if watts else None,
+            "samples": len(mhz)}
 
 
 def traffic_from_counters(means):
@@ -280,6 +354,14 @@ def main():
                                "4*N^2*d*h = %.4g FLOP per call" % fl_joint},
     }
 
+    if not args.no_clock:
+        clk = clock_under(torch, lambda: J.mmdit_joint_attn(q, k, v, o=o_joint, ws=ws_joint, stream=stream))
+        out["joint_attn"]["clock"] = clk
+        if clk:
+            out["joint_attn"]["pct_peak_at_clock"] = round(
+                100.0 * joint_tflops / (PEAK_BF16_TFLOPS * clk["gfx_mhz"] / PEAK_CLOCK_MHZ), 2)
+        print("[bench] under sustained joint attention: %s" % clk, file=sys.stderr, flush=True)
+
     del o_vt, o_va, o_av, ws_vt, ws_av
     if not args.no_train:
         out["train"] = train_leg(args, torch, J, w, q, k, v, dev)
@@ -391,6 +473,8 @@ def sparse_leg(args, torch, J, w, sparse_inputs, dev):
            "speedup": round(t_dense / t_sparse, 3), "density": round(density, 4),
            "dense_tflops": round(fl_dense / t_dense * 1e-9, 1),
            "sparse_attn_tflops_incl_selection": round(fl_sparse / t_sparse * 1e-9, 1)}
+    if not args.no_clock:
+        out["clock_sparse"] = clock_under(torch, sparse)
     if not args.no_train:
         out.update(sparse_train_leg(args, torch, J, w, q, k, v, o, ws_d, ws_s, mask, cnt, timed, stream))
     return out

@@ -67,3 +67,16 @@ def test_summarize_kernel_trace(tmp_path, capsys):
     cells = [c.strip() for c in line.split("|")]
     assert cells[2:8] == ["1683456", "512", "2", "13.500", "13.000", "14.000"]
     assert any("rope_kernel" in l and "0.170" in l for l in out.splitlines())
+
+
+def test_parse_smi_metrics():
+    # shape of `amd-smi metric -c -p --json` (one GPU, two of its XCD clocks shown)
+    doc = [{"gpu": 0,
+            "power": {"socket_power": {"value": 1350, "unit": "W"}, "gfx_voltage": "N/A"},
+            "clock": {"gfx_0": {"clk": {"value": 1800, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                                "max_clk": {"value": 2400, "unit": "MHz"}},
+                      "gfx_1": {"clk": {"value": 1900, "unit": "MHz"}, "max_clk": {"value": 2400, "unit": "MHz"}},
+                      "mem_0": {"clk": {"value": 2000, "unit": "MHz"}}}}]
+    assert bench.parse_smi_metrics(json.dumps(doc)) == (1850.0, 1350.0)
+    assert bench.parse_smi_metrics("not json") == (None, None)
+    assert bench.parse_smi_metrics(json.dumps([{"gpu": 0}])) == (None, None)
