@@ -11,6 +11,8 @@ P and dS are rounded to bf16 (relative 2^-9) before the products and the sums
 run in fp32, so that is five times the rounding; at unit scale it is tighter
 than 2e-2.  The log-sum-exp: the forward sums the fp16-rounded probabilities
 (relative 2^-11 each), so 2e-3 absolute."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -43,6 +45,31 @@ def run(q, k, v, g, scale=None):
     dq, dk, dv = J.mmdit_joint_attn_bwd(q, k, v, o, lse, g, softmax_scale=scale)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
+
+
+def test_bwd_single_key():
+    """One key: every softmax row is the constant 1, so dv is the sum of dO over
+    the queries and dq, dk are exactly zero: dS = P (dP - D) with dP = dO . v
+    and D = dO . o, o = v.  The zeros come out of cancelling fp32 sums of 128
+    products, so they are held to the error bound of two such sums (3 gamma_128
+    times the sum of |dO_c v_c|, plus the bf16 rounding of dS), propagated
+    through |k| and |q|, not to a fraction of their own largest entry."""
+    nq, h, d = 160, 2, 128
+    q, k, v, g = normal_tensors([(nq, h, d), (1, h, d), (1, h, d), (nq, h, d)], seed=41, device=DEV)
+    o, lse, dq, dk, dv = run(q, k, v, g)
+    qq, kk, vv, gg = f64(q), f64(k), f64(v), f64(g)
+    check("o", f64(o), np.broadcast_to(vv, qq.shape), TOL_BF16)
+    check("dv", f64(dv), gg.sum(axis=0, keepdims=True), TOL_BF16, REL_BF16)
+    u = 2.0 ** -24
+    gamma = 128 * u / (1 - 128 * u)
+    ds_bound = 3 * gamma * np.einsum("ihc,hc->ih", np.abs(gg), np.abs(vv[0])) * (1 + 2.0 ** -8)   # [nq, h]
+    scale = 1.0 / math.sqrt(d)
+    dq_bound = scale * ds_bound[:, :, None] * np.abs(kk)                                        # [nq, h, d]
+    dk_bound = scale * np.einsum("ih,ihc->hc", ds_bound, np.abs(qq))[None]                      # [1, h, d]
+    print("dq max %.2e (bound %.2e), dk max %.2e (bound %.2e)" % (
+        np.abs(f64(dq)).max(), dq_bound.max(), np.abs(f64(dk)).max(), dk_bound.max()), flush=True)
+    assert (np.abs(f64(dq)) <= dq_bound).all()
+    assert (np.abs(f64(dk)) <= dk_bound).all()
 
 
 @pytest.mark.parametrize("nq,nk,h,d", [
