@@ -1,0 +1,113 @@
+"""Seeded random shapes through every attention call, against the fp64 oracle.
+
+The other GPU tests pick their shapes by hand (tile boundaries, ragged tails,
+maximum sizes).  These cases draw them from a fixed seed instead: token counts
+log-uniform over 1..6000, head counts, head dims, grids of whole zones and
+top-k / top-p values, so that combinations nobody chose still meet the same
+bars (bf16 2e-2, fp32 1e-4, lse 2e-3, gradients 1e-2 of the largest entry,
+block selection bit-exact)."""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import joint_video_audio_rope_amd as J
+import test_gpu_adaptive as AD
+import test_gpu_parity as P
+import test_gpu_sparse_bwd as SB
+from oracle import attention as A
+from oracle import attention_bwd as AB
+from synth import shrink
+
+pytestmark = pytest.mark.gpu
+_rng = random.Random(20260)
+
+
+def _logu(a, b):
+    return int(round(math.exp(_rng.uniform(math.log(a), math.log(b)))))
+
+
+DENSE = [(_logu(1, 3000), _logu(1, 6000), _rng.randint(1, 4), _rng.choice([64, 128]), _rng.choice([0.5, 1.0, 2.5]),
+          _rng.randint(0, 10**6)) for _ in range(12)]
+BWD = [(_logu(1, 1500), _logu(2, 2500), _rng.randint(1, 3), _rng.randint(0, 10**6)) for _ in range(4)]
+FP32 = [(_logu(1, 500), _logu(1, 700), _rng.randint(1, 3), _rng.choice([64, 128]), _rng.randint(0, 10**6))
+        for _ in range(4)]
+CROSS = [(_logu(1, 4000), _logu(1, 400), _rng.randint(1, 3), _rng.randint(0, 10**6)) for _ in range(4)]
+
+
+def _grid(z, cap):
+    while True:
+        T, H, W = z * _rng.randint(1, 16 // z), z * _rng.randint(1, 64 // z), z * _rng.randint(1, 64 // z)
+        if 64 <= T * H * W <= cap:
+            return T, H, W
+
+
+SPARSE = []
+for _ in range(6):
+    _z = _rng.choice([8, 4])
+    SPARSE.append(_grid(_z, 16384) + (_z, _rng.randint(1, 3), _rng.randint(0, 8), round(_rng.uniform(0.0, 1.0), 3),
+                                      _rng.randint(0, 10**6)))
+SPARSE_BWD = [_grid(4, 4096) + (_rng.randint(1, 2), _rng.randint(1, 6), round(_rng.uniform(0.2, 0.95), 3),
+                                _rng.randint(0, 10**6)) for _ in range(2)]
+ADAPTIVE = [(8 * _rng.randint(1, 2), 8 * _rng.randint(2, 4), 8 * _rng.randint(2, 4), _rng.randint(1, 2),
+             _rng.randint(1, 8), round(_rng.uniform(0.2, 0.95), 3), _rng.randint(0, 10**6)) for _ in range(3)]
+
+
+@pytest.mark.parametrize("nq,nkv,h,d,scale,seed", DENSE)
+def test_random_dense(nq, nkv, h, d, scale, seed):
+    q, k, v = P._rand((nq, h, d), seed, scale=scale), P._rand((nkv, h, d), seed + 1, scale=scale), \
+        P._rand((nkv, h, d), seed + 2)
+    o, lse = J.mmdit_joint_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = AB.attention_fwd_lse(P.f64(q), P.f64(k), P.f64(v))
+    assert np.max(np.abs(P.f64(o) - o_ref)) <= P.TOL_BF16
+    assert np.max(np.abs(P.f64(lse) - lse_ref)) <= 2e-3
+
+
+@pytest.mark.parametrize("nq,nkv,h,seed", BWD)
+def test_random_dense_bwd(nq, nkv, h, seed):
+    q, k, v = (P._rand(s, seed + j) for j, s in enumerate([(nq, h, 128), (nkv, h, 128), (nkv, h, 128)]))
+    g = P._rand((nq, h, 128), seed + 3)
+    o, lse = J.mmdit_joint_attn_fwd(q, k, v)
+    grads = J.mmdit_joint_attn_bwd(q, k, v, o, lse, g)
+    torch.cuda.synchronize()
+    refs = AB.attention_bwd(P.f64(q), P.f64(k), P.f64(v), P.f64(g))
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, refs):
+        err, peak = float(np.max(np.abs(P.f64(got) - ref))), float(np.max(np.abs(ref)))
+        assert err <= 1e-2 * peak, (name, err, peak)
+
+
+@pytest.mark.parametrize("nq,nkv,h,d,seed", FP32)
+def test_random_fp32(nq, nkv, h, d, seed):
+    q, k, v = (P._rand(s, seed + j, dtype=torch.float32) for j, s in enumerate([(nq, h, d), (nkv, h, d), (nkv, h, d)]))
+    o = J.mmdit_joint_attn(q, k, v)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(P.f64(o) - A.attention(P.f64(q), P.f64(k), P.f64(v)))) <= P.TOL_FP32
+
+
+@pytest.mark.parametrize("nv,na,h,seed", CROSS)
+def test_random_av_cross(nv, na, h, seed):
+    qv, kv, vv = (P._rand((nv, h, 128), seed + j) for j in range(3))
+    qa, ka, va = (P._rand((na, h, 128), seed + 3 + j) for j in range(3))
+    o_v, o_a = J.mmdit_av_cross_attn(qv, kv, vv, qa, ka, va)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(P.f64(o_v) - A.attention(P.f64(qv), P.f64(ka), P.f64(va)))) <= P.TOL_BF16
+    assert np.max(np.abs(P.f64(o_a) - A.attention(P.f64(qa), P.f64(kv), P.f64(vv)))) <= P.TOL_BF16
+
+
+@pytest.mark.parametrize("T,H,W,z,h,k_sel,p_sel,seed", SPARSE)
+def test_random_block_sparse(T, H, W, z, h, k_sel, p_sel, seed):
+    P._sparse_check(shrink("sparse2k", T=T, H=H, W=W, heads=h, zone=(z, z, z), seed=seed), k_sel, p_sel)
+
+
+@pytest.mark.parametrize("T,H,W,h,k_sel,p_sel,seed", SPARSE_BWD)
+def test_random_block_sparse_bwd(T, H, W, h, k_sel, p_sel, seed):
+    SB.full_check(shrink("sparse2k", T=T, H=H, W=W, heads=h, zone=(4, 4, 4), seed=seed), k_sel, p_sel)
+
+
+@pytest.mark.parametrize("T,H,W,h,k_sel,p_sel,seed", ADAPTIVE)
+def test_random_adaptive(T, H, W, h, k_sel, p_sel, seed):
+    AD.full_check(shrink("adaptive2k", T=T, H=H, W=W, heads=h, fg_radius=6.0, audio_radius=4.0, seed=seed),
+                  k_sel, p_sel)
