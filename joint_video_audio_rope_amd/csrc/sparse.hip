@@ -426,8 +426,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
 }
 
 // Sparse attention with producer waves.  A workgroup serves G consecutive
-// query blocks of one head with 2 G consumer waves (waves 2 b, 2 b + 1 own
-// block G p + b) and two producer waves.  The producers stream the union of
+// query blocks of one head with 2 G consumer waves, two per block (which
+// waves own which block is chosen for the SIMD placement described at the
+// consumers), and two producer waves.  The producers stream the union of
 // the G selections, in ascending block id, into a ring of R LDS tiles (the
 // block's K rows and fp16 V^T, each one contiguous image); producer p copies
 // the tiles t with t % 2 == p.  Consumers follow the same walk and compute
