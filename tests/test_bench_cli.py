@@ -80,3 +80,11 @@ def test_parse_smi_metrics():
     assert bench.parse_smi_metrics(json.dumps(doc)) == (1850.0, 1350.0)
     assert bench.parse_smi_metrics("not json") == (None, None)
     assert bench.parse_smi_metrics(json.dumps([{"gpu": 0}])) == (None, None)
+
+
+def test_clock_under_without_amd_smi(monkeypatch):
+    import shutil
+    monkeypatch.setattr(shutil, "which", lambda name: None)
+    calls = []
+    assert bench.clock_under(None, lambda: calls.append(1)) is None
+    assert calls == []          # nothing is run when there is no tool to sample with
