@@ -5,18 +5,21 @@
 //   block_pool     fp64 means of each block's 64 query rows and 64 key rows,
 //                  per head (HBM-bound: reads Q and K once); also records each
 //                  block's first raster token.
-//   vt_blocks      V of each block transposed to fp16 [d][64] for the P V^T
-//                  matrix-core product (HBM-bound).
+//   vt_blocks      each block's K rows (bf16) and V^T (fp16 [d][64]), each
+//                  laid out as the image of its LDS tile (HBM-bound).
 //   block_scores   fp64 logits Qbar Kbar^T * scale per head (fp64 FMA GEMM).
-//   block_select   per (head, query block): fp64 softmax, sort by probability
-//                  (ties to the lower block id), fp64 running sum, keep the
-//                  longer of the top-k and top-p prefixes; emits the bitmask,
-//                  the count and the selection bitmask.
-//   sparse_attn    attention of each query block over its selected key blocks
-//                  with the same online-softmax tile loop as the dense kernel.
+//   block_select   per (head, query block): fp64 softmax, then the top-p and
+//                  top-k cuts found by bisection over the probabilities' bit
+//                  patterns (ties to the lower block id), keeping the longer
+//                  prefix; emits the bitmask and the count.
+//   sparse_attn    attention of groups of query blocks over the union of
+//                  their selected key blocks, fed through an LDS ring by
+//                  producer waves, with the dense kernel's online-softmax
+//                  tile step.
 // Selection runs in fp64 throughout: on smooth-field inputs the probability
 // gaps and running-sum margins at the cut get down to ~1e-8, where fp32 flips
 // rows.
+#include <cstdlib>
 #include <algorithm>
 
 #include "attn_core.hpp"
@@ -470,14 +473,15 @@ __device__ __forceinline__ void publish_after(lds_int* flag, int v) {
     __asm__ volatile("s_waitcnt vmcnt(%2)\n\tds_write_b32 %0, %1" ::"v"(flag), "v"(v), "n"(N) : "memory");
 }
 
-// Wait until *p >= v.  After kSpinLimit sleeps the wait gives up and marks
-// the workgroup broken, which ends every later wait at once: a broken
-// protocol costs one bounded wait per workgroup and wrong results.
-__device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken) {
+// Wait until *p >= v.  After `limit` sleeps (kSpinLimit unless the host
+// lowers it) the wait gives up and marks the workgroup broken, which ends
+// every later wait at once: a broken protocol costs one bounded wait per
+// workgroup and wrong results, never a hang.
+__device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken, int limit) {
     for (int i = 0;; ++i) {
         if (__builtin_amdgcn_readfirstlane(lds_load(p)) >= v) break;
         if (__builtin_amdgcn_readfirstlane(lds_load(broken)) != 0) break;
-        if (i == kSpinLimit) {
+        if (i >= limit) {
             __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             break;
         }
@@ -489,7 +493,7 @@ __device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken) {
 template <int HD, int G, int R>
 __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_kernel(
         SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-        SparseWs w, float* __restrict__ o, float* __restrict__ lse) {
+        SparseWs w, float* __restrict__ o, float* __restrict__ lse, int spin_limit) {
     using L = TileLayout<HD>;
     constexpr int NC = 2 * G;                          // consumer waves; waves NC, NC + 1 produce
     constexpr int KS = HD / 16;
@@ -550,7 +554,7 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
         for (int i = 0;; ++i) {
             if (__builtin_amdgcn_readfirstlane(lds_load(ready_at(t & (R - 1)))) >= t + 1) break;
             if (__builtin_amdgcn_readfirstlane(lds_load((lds_int*)&broken)) != 0) break;
-            if (i == kSpinLimit) {
+            if (i >= spin_limit) {
                 __hip_atomic_store((lds_int*)&broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 break;
             }
@@ -570,7 +574,7 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
             const int sl = t & (R - 1);
             // publish this producer's previous tile once it has landed
             if (last >= 0) publish_after<0>(ready_at(last & (R - 1)), last + 1);
-            if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk);   // tile t - R is done
+            if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk, spin_limit);   // tile t - R is done
             char* lb = lds + sl * L::kBytes;
             const int64_t blk = (int64_t)head * g.nb + j;
             const char* kt = reinterpret_cast<const char*>(w.kimg + blk * (kTileN * HD)) + 16 * lane;
@@ -693,13 +697,25 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
     return hipGetLastError();
 }
 
+// Bound of every wait in the stream kernel, in sleeps of about 64 cycles.
+// MMDIT_SPARSE_SPIN_LIMIT (a non-negative integer) lowers it: tests set 0 to
+// force the give-up path from the host and check that the kernel still ends.
+static int stream_spin_limit() {
+    const char* e = std::getenv("MMDIT_SPARSE_SPIN_LIMIT");
+    if (!e || !*e) return kSpinLimit;
+    char* end = nullptr;
+    const long v = std::strtol(e, &end, 10);
+    if (*end != '\0' || v < 0) return kSpinLimit;
+    return (int)std::min<long>(v, kSpinLimit);
+}
+
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
                               float scale_log2, const SparseWs& w, float* o, float* lse, hipStream_t s) {
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
     const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
     hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g,
-                       q, k, scale_log2, w, o, lse);
+                       q, k, scale_log2, w, o, lse, stream_spin_limit());
     return hipGetLastError();
 }
 
