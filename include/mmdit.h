@@ -244,7 +244,12 @@ mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v
  * sel_mask [heads][nb][ceil(nb/32)] uint32: bit j%32 of word j/32 set iff key
  * block j is selected; sel_count [heads][nb] int32 = number of selected blocks.
  * Either may be NULL if not wanted.  T, H, W must be multiples of the zone,
- * the zone of the block; block volume 64; head_dim 128. */
+ * the zone of the block; block volume 64; head_dim 128.
+ * The attention kernel's internal waits are bounded (a wait that times out
+ * yields wrong values, never a hang).  The environment variable
+ * MMDIT_SPARSE_SPIN_LIMIT, a non-negative integer read at each call, lowers
+ * the bound; it exists for tests, and 0 gives wrong attention values.  The same
+ * holds for every block-sparse forward call below. */
 mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v, int32_t T,
                                      int32_t H, int32_t W, int32_t heads, int32_t head_dim,
                                      const mmdit_sparse_desc* sp, double softmax_scale, float* o,
