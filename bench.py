@@ -57,6 +57,18 @@ def parse():
     ap.add_argument("--traffic-out", metavar="JSON",
                     help="with --summarize over the two counter files of a --traffic-probe run: "
                          "write the copy-calibrated HBM bytes per joint-attention call here")
+    ap.add_argument("--probe", action="store_true",
+                    help="run every kernel of the library a few times on the bench's workloads (a 1 GiB copy for "
+                         "counter calibration, the 480p-latent step and training pair, the block-sparse call and "
+                         "its training pair), then exit (profile with rocprofv3 --kernel-trace or --pmc)")
+    ap.add_argument("--kernel-table", nargs="+", metavar="CSV",
+                    help="join rocprofv3 csv files of --probe runs (kernel_trace.csv and the counter_collection.csv "
+                         "of FETCH_SIZE, WRITE_SIZE, MfmaUtil passes) into one markdown table per kernel and grid: "
+                         "mean duration, copy-calibrated HBM bytes and GB/s, matrix-core utilisation; then exit")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="time the fp64 oracle on the host cores for every workload (no GPU used): the "
+                         "88-token, 5850-token and 480p-latent workloads in full, the 720p-latent and "
+                         "block-sparse ones on one head, scaled to 24 heads; print a markdown table, then exit")
     return ap.parse_args()
 
 
@@ -161,7 +173,8 @@ def clock_under(torch, fn, seconds=3.0):
 
 
 def traffic_from_counters(means):
-    """HBM bytes of one joint-attention call (V^T staging + attention kernel)
+    """HBM bytes of one joint-attention call (V prescale, V^T staging and the
+    attention kernel)
     from mean FETCH_SIZE / WRITE_SIZE KiB per dispatch, each scaled by what the
     counter reads for the 1 GiB copy."""
     def mean(part, counter):
@@ -174,7 +187,7 @@ def traffic_from_counters(means):
     w_scale = COPY_BYTES / (mean("copyBuffer", "WRITE_SIZE") * 1024.0)
     out = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
     total = 0.0
-    for part in ("vt_dense_kernel", "attn_bf16_kernel"):
+    for part in ("v_absmax_kernel", "vt_dense_kernel", "attn_bf16_kernel"):
         fb = mean(part, "FETCH_SIZE") * 1024.0 * f_scale
         wb = mean(part, "WRITE_SIZE") * 1024.0 * w_scale
         out["kernels"][part] = {"fetch_bytes": round(fb), "write_bytes": round(wb)}
@@ -223,6 +236,106 @@ def summarize(paths, traffic_out=None):
         print("traffic per joint-attention call: %.4g bytes (%s)" % (t["bytes_per_launch"], traffic_out))
 
 
+def kernel_table(paths):
+    """One markdown row per (kernel, grid) from --probe runs: mean duration
+    (kernel trace), FETCH_SIZE and WRITE_SIZE scaled by what they read for the
+    1 GiB copy, the GB/s they imply over that duration, and MfmaUtil."""
+    import collections
+    import csv
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0][:60]
+
+    dur = collections.defaultdict(list)
+    ctr = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if "Counter_Name" in r:
+                key = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
+                ctr[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            else:
+                g = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
+                dur[(short(r["Kernel_Name"]), g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+
+    def mean(x):
+        return sum(x) / len(x) if x else None
+
+    copy = [k for k in ctr if "copyBuffer" in k[0]]
+    f_scale = w_scale = None
+    if copy:
+        c = ctr[copy[0]]
+        if c.get("FETCH_SIZE"):
+            f_scale = COPY_BYTES / (mean(c["FETCH_SIZE"]) * 1024.0)
+        if c.get("WRITE_SIZE"):
+            w_scale = COPY_BYTES / (mean(c["WRITE_SIZE"]) * 1024.0)
+    print("Copy calibration (1 GiB copy): fetch x %s, write x %s\n" % (
+        "%.4f" % f_scale if f_scale else "-", "%.4f" % w_scale if w_scale else "-"))
+    print("| kernel | grid (threads) | calls | avg ms | fetch GB | write GB | GB/s | % of 8 TB/s | MfmaUtil % |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    keys = sorted(set(dur) | set(ctr), key=lambda k: -(sum(dur.get(k, [0])) or 0))
+    for k in keys:
+        d = mean(dur.get(k, []))
+        c = ctr.get(k, {})
+        fb = mean(c.get("FETCH_SIZE", [])) * 1024.0 * f_scale / 1e9 if c.get("FETCH_SIZE") and f_scale else None
+        wb = mean(c.get("WRITE_SIZE", [])) * 1024.0 * w_scale / 1e9 if c.get("WRITE_SIZE") and w_scale else None
+        mu = mean(c.get("MfmaUtil", []))
+        gbs = (fb or 0) + (wb or 0)
+        rate = gbs / (d * 1e-3) if d and (fb is not None or wb is not None) else None
+        f = lambda x, fmt: "-" if x is None else fmt % x
+        print("| %s | %d | %d | %s | %s | %s | %s | %s | %s |" % (
+            k[0], k[1], len(dur.get(k, [])), f(d, "%.3f"), f(fb, "%.3f"), f(wb, "%.3f"), f(rate, "%.0f"),
+            f(None if rate is None else 100 * rate / PEAK_HBM_GBS, "%.0f"), f(mu, "%.1f")))
+
+
+def probe():
+    """Every kernel of the library on the bench's workloads, a few calls each,
+    for rocprofv3 (kernel trace or one counter pass per run)."""
+    import torch
+
+    import joint_video_audio_rope_amd as J
+    from synth import WORKLOADS, joint_inputs, sparse_inputs, upstream_grad
+
+    dev = "cuda"
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(2):
+        dst.copy_(src)
+    del src, dst
+    w = WORKLOADS["480p"]
+    x = joint_inputs(w, dev)
+    q, k, v = x["q"], x["k"], x["v"]
+    n, h, d = q.shape
+    frame = w["H"] * w["W"]
+    n_vs = (w["n_cond_frames"] + w["T"]) * frame
+    a0, t0 = n_vs, n_vs + w["n_audio"]
+    spec = J.rope_spec_for(w)
+    for _ in range(2):
+        J.mmdit_joint_attn(q[:n_vs], k[t0:], v[t0:])
+        q2, k2 = q.clone(), k.clone()
+        J.mmdit_rope3d(spec, q2, k2)
+        J.mmdit_joint_attn(q2, k2, v)
+        J.mmdit_av_cross_attn(q2[:n_vs], k2[:n_vs], v[:n_vs], q2[a0:t0], k2[a0:t0], v[a0:t0])
+        J.mmdit_joint_attn_rope(spec, q, k, v)
+    g = upstream_grad(w, dev)
+    o, lse = J.mmdit_joint_attn_fwd(q2, k2, v)
+    J.mmdit_joint_attn_bwd(q2, k2, v, o, lse, g)
+    torch.cuda.synchronize()
+    del o, lse, g, q2, k2, x, q, k, v
+    ws = WORKLOADS["sparse2k"]
+    xs = sparse_inputs(ws, dev)
+    T, H, W = ws["T"], ws["H"], ws["W"]
+    args = (xs["q"], xs["k"], xs["v"], T, H, W, ws["zone"], ws["block"], ws["top_k"], ws["top_p"])
+    for _ in range(2):
+        J.mmdit_block_sparse_attn(*args)
+    o, lse, mask, _ = J.mmdit_block_sparse_attn_fwd(*args)
+    gs = torch.randn(xs["q"].shape, device=dev).to(torch.bfloat16)
+    J.mmdit_block_sparse_attn_bwd(xs["q"], xs["k"], xs["v"], o, lse, gs, mask, T, H, W, ws["zone"], ws["block"])
+    torch.cuda.synchronize()
+    print("probe done", flush=True)
+
+
 def traffic_probe():
     import torch
 
@@ -246,10 +359,169 @@ def traffic_probe():
     print("traffic probe done: 1 GiB copy x2, joint attention x3", flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_workers():
+    """Oracle worker processes: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_SHARED = {}
+
+
+def _oracle_task(task):
+    """Worker side of the oracle timing: one oracle call on arrays the parent
+    set up before forking (shared copy-on-write, nothing pickled)."""
+    kind, a = task
+    if kind == "attn":
+        from oracle import attention as A
+        qn, kn, vn, hd, r0, r1 = a
+        q, k, v = _SHARED[qn], _SHARED[kn], _SHARED[vn]
+        return A.attention(q[r0:r1, hd:hd + 1], k[:, hd:hd + 1], v[:, hd:hd + 1], chunk=128).shape
+    from oracle import block_sparse as B
+    b0, b1 = a
+    S = _SHARED
+    return len(B.block_sparse_attention(S["q"], S["k"], S["v"], S["idx"], S["mask"], query_blocks=range(b0, b1)))
+
+
+def oracle_times():
+    """The fp64 oracle (numpy, as it stands) timed on the host cores for each
+    workload, split over heads and query slices into single-threaded worker
+    processes (numpy's exp is single-threaded).  Inputs are the workloads'
+    seeded tensors drawn on the host (same distributions and shapes as on the
+    GPU; the bytes differ, which does not matter for timing).  This mode never
+    touches the GPU, so the workers are forked and share the inputs."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)            # no BLAS threads exist when the workers fork
+    except Exception:
+        pass
+    from oracle import attention as A
+    from oracle import block_sparse as B
+    from oracle import rope as R
+    from synth import WORKLOADS, joint_inputs, n_tokens, shrink, sparse_inputs
+
+    nw = host_workers()
+
+    def f32(t):
+        return t.to(torch.float32).numpy()
+
+    def run(tasks):
+        with mp.get_context("fork").Pool(nw) as pool:
+            t0 = time.perf_counter()
+            pool.map(_oracle_task, tasks, chunksize=1)
+            return time.perf_counter() - t0
+
+    def attn_tasks(qn, kn, vn, per_head):
+        nq, h = _SHARED[qn].shape[0], _SHARED[qn].shape[1]
+        step = -(-nq // per_head)
+        return [("attn", (qn, kn, vn, hd, r0, min(nq, r0 + step))) for hd in range(h) for r0 in range(0, nq, step)]
+
+    rows = []
+
+    def joint_layer(name, heads=None):
+        w = WORKLOADS[name] if heads is None else shrink(name, heads=heads)
+        x = joint_inputs(w, "cpu")
+        q, k, v = f32(x["q"]), f32(x["k"]), f32(x["v"])
+        pos, rot = R.token_positions(w)
+        t0 = time.perf_counter()
+        rq = R.apply_rope(q, pos, rot, w["split"], w["theta"])
+        rk = R.apply_rope(k, pos, rot, w["split"], w["theta"])
+        t_rope = time.perf_counter() - t0
+        seg = A.joint_segments(w)
+        (v0, v1), (a0, a1), (s0, s1) = seg["video_stream"], seg["audio"], seg["text"]
+        _SHARED.clear()
+        _SHARED.update(q=q, rq=rq, rk=rk, v=v, qv=rq[v0:v1], kv=rk[v0:v1], vv=v[v0:v1], qa=rq[a0:a1],
+                       ka=rk[a0:a1], va=v[a0:a1], qs=q[v0:v1], ks=k[s0:s1], vs=v[s0:s1])
+        per_head = max(1, -(-4 * nw // w["heads"]))
+        t_joint = run(attn_tasks("rq", "rk", "v", per_head))
+        t_av = run(attn_tasks("qv", "ka", "va", per_head) + attn_tasks("qa", "kv", "vv", 1))
+        t_vt = run(attn_tasks("qs", "ks", "vs", per_head)) if name == "480p" else None
+        return t_rope, t_joint, t_av, t_vt
+
+    for name, label in (("tiny", "88-token fp32 (2 x 64)"), ("block", "5850-token joint block"),
+                        ("480p", "480p-latent layer (35050 tokens)")):
+        t_rope, t_joint, t_av, t_vt = joint_layer(name)
+        rows.append((label, "in full", t_rope, t_joint, t_av, t_vt))
+        print("[oracle] %s: rope %.2f s, joint %.2f s, A<->V %.2f s%s" % (
+            label, t_rope, t_joint, t_av, "" if t_vt is None else ", video->text %.2f s" % t_vt),
+            file=sys.stderr, flush=True)
+    h = WORKLOADS["720p"]["heads"]
+    t_rope, t_joint, t_av, _ = joint_layer("720p", heads=1)
+    rows.append(("720p-latent layer (76330 tokens)", "one head x %d (extrapolated)" % h,
+                 t_rope * h, t_joint * h, t_av * h, None))
+    print("[oracle] 720p one head: joint %.2f s, A<->V %.2f s" % (t_joint, t_av), file=sys.stderr, flush=True)
+
+    w = shrink("sparse2k", heads=1)
+    T, H, W = w["T"], w["H"], w["W"]
+    x = sparse_inputs(w, "cpu")
+    q, k, v = f32(x["q"]), f32(x["k"]), f32(x["v"])
+    t0 = time.perf_counter()
+    idx = B.block_token_index(T, H, W, w["zone"], w["block"])
+    P = B.block_probs(B.block_means(q, idx), B.block_means(k, idx))
+    mask, counts, _ = B.select_blocks(P, w["top_k"], w["top_p"])
+    t_sel = time.perf_counter() - t0
+    nb = idx.shape[0]
+    _SHARED.clear()
+    _SHARED.update(q=q, k=k, v=v, idx=idx, mask=mask)
+    step = -(-nb // (4 * nw))
+    t_sparse = run([("sparse", (b0, min(nb, b0 + step))) for b0 in range(0, nb, step)])
+    t_dense = run(attn_tasks("q", "k", "v", 4 * nw))
+    _SHARED.clear()
+    hs = WORKLOADS["sparse2k"]["heads"]
+    dens = float(counts.mean()) / nb
+    rows.append(("block-sparse 24x64x112 (172032 tokens), dense", "one head x %d (extrapolated)" % hs,
+                 None, t_dense * hs, None, None))
+    rows.append(("block-sparse 24x64x112 (172032 tokens), sparse", "one head x %d (extrapolated)" % hs,
+                 None, (t_sel + t_sparse) * hs, None, None))
+    print("[oracle] sparse2k one head: selection %.2f s, sparse attention %.2f s (density %.3f), dense %.2f s" % (
+        t_sel, t_sparse, dens, t_dense), file=sys.stderr, flush=True)
+
+    print("CPU: %s; os.cpu_count() = %s; %d single-threaded worker processes (numpy %s)\n" % (
+        cpu_model(), os.cpu_count(), nw, np.__version__))
+    print("| workload | coverage | RoPE s | joint (or dense / sparse) attention s | A<->V s | video->text s |")
+    print("|---|---|---|---|---|---|")
+    fmt = lambda t: "-" if t is None else "%.1f" % t
+    for label, cov, a, b, c, d in rows:
+        print("| %s | %s | %s | %s | %s | %s |" % (label, cov, fmt(a), fmt(b), fmt(c), fmt(d)))
+    print("\nblock-sparse, one head: selection (pooling, scores, top-k/top-p) %.1f s, sparse attention over "
+          "all %d query blocks %.1f s at density %.3f, dense %.1f s" % (t_sel, nb, t_sparse, dens, t_dense))
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize, args.traffic_out)
+        return
+    if args.oracle_times:
+        oracle_times()
+        return
+    if args.kernel_table:
+        kernel_table(args.kernel_table)
+        return
+    if args.probe:
+        if args.gpus != 1:
+            sys.exit(2)
+        probe()
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -354,6 +626,10 @@ def main():
                                "4*N^2*d*h = %.4g FLOP per call" % fl_joint},
     }
 
+    out["fused_rope"] = fused_rope_leg(args, torch, J, spec, x, step, o_joint, o_vt, o_va, o_av, ws_vt, ws_av,
+                                       n_vs, a0, t0, dev, stream)
+    print("[bench] RoPE fused into the joint attention: %s" % out["fused_rope"], file=sys.stderr, flush=True)
+
     if not args.no_clock:
         clk = clock_under(torch, lambda: J.mmdit_joint_attn(q, k, v, o=o_joint, ws=ws_joint, stream=stream))
         out["joint_attn"]["clock"] = clk
@@ -378,6 +654,53 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args, torch, q, k, v)
         print("[bench] cpu baseline: %s" % out["cpu_baseline"], file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
+
+
+def fused_rope_leg(args, torch, J, spec, x, step, o_joint, o_vt, o_va, o_av, ws_vt, ws_av, n_vs, a0, t0, dev,
+                   stream):
+    """The same step with the RoPE fused into the joint attention
+    (mmdit_joint_attn_rope: K rotated in the V staging pass, Q in registers,
+    both written out for the cross-attentions): video->text, fused joint
+    attention, audio<->video on the rotated tensors.  The separate-call step
+    and the fused one are timed alternately, twice each, and the faster run
+    of each is kept, so that both see the same clock."""
+    n_a = o_av.shape[0]
+    v = x["v"]
+    n, h, d = v.shape
+    from synth import WORKLOADS, joint_inputs
+    fresh = joint_inputs(WORKLOADS["480p"], dev)     # unrotated Q, K (the step rotates its own in place)
+    qu, ku = fresh["q"], fresh["k"]
+    q_rot, k_rot = torch.empty_like(qu), torch.empty_like(ku)
+    ws_f = torch.empty(J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN_ROPE, n, n, h, d, J.MMDIT_BF16),
+                       dtype=torch.uint8, device=dev)
+    qv = qu[:n_vs]
+    kt, vt = ku[t0:], v[t0:]
+
+    def fused_step():
+        J.mmdit_joint_attn(qv, kt, vt, o=o_vt, ws=ws_vt, stream=stream)
+        J.mmdit_joint_attn_rope(spec, qu, ku, v, o=o_joint, q_rot=q_rot, k_rot=k_rot, ws=ws_f, stream=stream)
+        J.mmdit_av_cross_attn(q_rot[:n_vs], k_rot[:n_vs], v[:n_vs], q_rot[a0:a0 + n_a], k_rot[a0:a0 + n_a],
+                              v[a0:a0 + n_a], o_video=o_va, o_audio=o_av, ws=ws_av, stream=stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    sep, fus = [], []
+    for _ in range(2):
+        sep.append(timed(step))
+        fus.append(timed(fused_step))
+    del ws_f, q_rot, k_rot, fresh
+    return {"step_ms_fused": round(min(fus), 4), "step_ms_separate": round(min(sep), 4),
+            "saved_ms": round(min(sep) - min(fus), 4)}
 
 
 def train_leg(args, torch, J, w, q, k, v, dev):
@@ -615,6 +938,7 @@ def cpu_baseline(args, torch, q, k, v):
     dt = time.perf_counter() - t0
     fl = attn_flops(len(rows), k.shape[0], q.shape[1], q.shape[2])
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
             "sample": "joint attention of %d evenly spaced query rows x all 24 heads against all %d "
                       "keys (numpy fp64, BLAS threads for the products, exp single-threaded), "
                       "%.1f s" % (len(rows), k.shape[0], dt)}

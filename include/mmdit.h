@@ -34,6 +34,8 @@
  *              the caller's next synchronisation.  Nothing throws across the
  *              ABI.  mmdit_last_error() describes the last non-OK status of the
  *              calling thread.
+ *   Scale      softmax_scale multiplies <q, k> inside the softmax; it must be
+ *              finite and >= 0, and 0 selects 1/sqrt(head_dim).
  *   Outputs    Outputs are overwritten, never accumulated into, and must not
  *              alias inputs.  mmdit_rope3d works in place on Q and K.
  *   Threads    Calls are reentrant; concurrent calls must not share a workspace.
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MMDIT_ABI_VERSION 3
+#define MMDIT_ABI_VERSION 4
 #define MMDIT_MAX_SEGMENTS 16
 
 typedef enum {
@@ -70,7 +72,8 @@ typedef enum {
     MMDIT_OP_JOINT_ATTN_BWD = 3,
     MMDIT_OP_BLOCK_SPARSE_ATTN_BWD = 4,
     MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE = 5,
-    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD = 6
+    MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD = 6,
+    MMDIT_OP_JOINT_ATTN_ROPE = 7
 } mmdit_op;
 
 /* One run of tokens of one modality inside a [tokens][heads][head_dim] buffer.
@@ -114,6 +117,12 @@ typedef struct {
     int32_t block[3];
     int32_t top_k;         /* >= 0 */
     double top_p;          /* in [0, 1]; >= 1 keeps every block */
+    int32_t wait_limit;    /* 0 (use this): the default bound of the attention
+                              kernel's internal waits, 2^18 sleeps of about 64
+                              cycles.  1 .. 2^18 lowers it, for tests of the
+                              failure path: a wait that reaches the bound gives
+                              up, and the rows of the query blocks its workgroup
+                              serves (o rows, lse entries) are written as NaN. */
 } mmdit_sparse_desc;
 
 /* ---- host-only calls (no GPU needed) ------------------------------------- */
@@ -175,13 +184,40 @@ mmdit_status mmdit_rope3d(const mmdit_rope_desc* desc, const float* dev_table,
  * [cond|video|audio|text] buffer as q, k and v with n_q = n_kv; video->text
  * passes video queries and text keys.
  * q [n_q][heads][head_dim], k and v [n_kv][heads][head_dim] in `dtype`,
- * o [n_q][heads][head_dim] fp32.  head_dim 64 or 128.  bf16: products on
- * bf16 matrix cores with fp32 accumulation and fp32 online softmax; fp32: fp32
- * throughout.  n_q >= 0 (0 is a no-op), n_kv >= 1. */
+ * o [n_q][heads][head_dim] fp32.  head_dim 64 or 128.  bf16: Q K^T on bf16
+ * matrix cores, fp32 online softmax, P V on fp16 matrix cores (P in (0, 2^8]
+ * rounded to fp16; V scaled per head by a power of two 2^e that puts its
+ * largest magnitude in [2^14, 2^15), so its conversion is exact for every
+ * entry within 2^-28 of that maximum and nothing overflows; O is scaled back
+ * by 2^-e), fp32 accumulation; fp32: fp32 throughout.  n_q >= 0 (0 is a
+ * no-op), n_kv >= 1. */
 mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const void* v,
                               int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
                               float softmax_scale, float* o, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* The joint self-attention of one dual-stream block with its RoPE fused in:
+ * o = mmdit_joint_attn(R(q), R(k), v) where R is mmdit_rope3d's rotation for
+ * `desc` (n_q = n_kv = desc->n_tokens, heads and head_dim from desc), and the
+ * rotated tensors themselves, bit for bit those mmdit_rope3d writes, in q_rot
+ * and k_rot for the block's audio<->video cross-attention.  Sources:
+ * SkyReels-V4 analysis, workflow steps 1 and 3 (time-shifted 3D RoPE of the
+ * video/audio tokens, then joint self-attention and the cross-attentions in
+ * every block); trdm.cn article, sections 2.1-2.2.
+ * The fusion: the pass that stages V for the P V products also rotates K and
+ * writes it to k_rot (or the workspace), and the attention kernel rotates
+ * each Q row in registers as it loads it (storing it to q_rot), so the
+ * separate RoPE pass and one read of Q disappear.
+ * q, k, v [n_tokens][heads][head_dim] bf16 (unrotated q and k are left
+ * unchanged), o fp32; q_rot, k_rot bf16 of the same shape, 16-byte aligned,
+ * each either NULL (not wanted) or disjoint from q, k, v, o, each other and
+ * the workspace.  dev_table: the device copy of mmdit_rope3d_build_table's
+ * output for desc.  bf16 only (MMDIT_ERR_UNSUPPORTED for fp32).  Workspace:
+ * mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_ROPE, n_tokens, n_tokens, heads,
+ * head_dim, MMDIT_BF16, NULL). */
+mmdit_status mmdit_joint_attn_rope(const mmdit_rope_desc* desc, const float* dev_table, const void* q,
+                                   const void* k, const void* v, int32_t dtype, float softmax_scale, float* o,
+                                   void* q_rot, void* k_rot, void* ws, size_t ws_bytes, void* stream);
 
 /* mmdit_joint_attn for a training step: the same output o, plus
  * lse [heads][n_q] fp32, the natural log of sum_j exp(softmax_scale * <q_i, k_j>)
@@ -245,11 +281,13 @@ mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v
  * block j is selected; sel_count [heads][nb] int32 = number of selected blocks.
  * Either may be NULL if not wanted.  T, H, W must be multiples of the zone,
  * the zone of the block; block volume 64; head_dim 128.
- * The attention kernel's internal waits are bounded (a wait that times out
- * yields wrong values, never a hang).  The environment variable
- * MMDIT_SPARSE_SPIN_LIMIT, a non-negative integer read at each call, lowers
- * the bound; it exists for tests, and 0 gives wrong attention values.  The same
- * holds for every block-sparse forward call below. */
+ * The attention kernel's internal waits are bounded (sp->wait_limit): a wait
+ * that times out never hangs the call; the rows of the query blocks its
+ * workgroup serves come out as NaN, never as plausible wrong values.  The same
+ * holds for every block-sparse forward call below (the adaptive call uses the
+ * default bound).
+ * V enters the P V products as fp16 after a per-head power-of-two prescale
+ * (exact; no range limit on V), as in mmdit_joint_attn. */
 mmdit_status mmdit_block_sparse_attn(const void* q, const void* k, const void* v, int32_t T,
                                      int32_t H, int32_t W, int32_t heads, int32_t head_dim,
                                      const mmdit_sparse_desc* sp, double softmax_scale, float* o,

@@ -1,12 +1,14 @@
 """ctypes binding of libmmdit.so (include/mmdit.h).
 
 Argument marshalling only: every step of the hot path runs in the library's
-HIP kernels.  Tensors are torch tensors used as device memory; the current
-torch stream is passed as the hipStream_t.  There is no fallback: if the
-library is missing, every call raises.
+HIP kernels.  Tensors are torch tensors used as device memory.  Calls run on
+`stream` when given (outputs and workspace the wrapper allocates are then
+taken on that stream), else on torch's current stream.  softmax_scale=None
+passes 0, for which the library uses 1/sqrt(head_dim).  There is no
+fallback: if the library is missing, every call raises.
 """
+import contextlib
 import ctypes
-import math
 import os
 
 import torch
@@ -18,7 +20,8 @@ MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMD
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
 (MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,
- MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD) = range(7)
+ MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD,
+ MMDIT_OP_JOINT_ATTN_ROPE) = range(8)
 
 # (b_T, b_H, b_W) of the content-adaptive shape codes, in code order
 ADAPTIVE_SHAPES = ((2, 4, 8), (2, 8, 4), (4, 2, 8), (4, 4, 4), (4, 8, 2), (8, 2, 4), (8, 4, 2),
@@ -51,7 +54,7 @@ class RopeDesc(ctypes.Structure):
 
 class SparseDesc(ctypes.Structure):
     _fields_ = [("zone", ctypes.c_int32 * 3), ("block", ctypes.c_int32 * 3),
-                ("top_k", ctypes.c_int32), ("top_p", ctypes.c_double)]
+                ("top_k", ctypes.c_int32), ("top_p", ctypes.c_double), ("wait_limit", ctypes.c_int32)]
 
 
 _lib = None
@@ -81,6 +84,9 @@ def lib():
         L.mmdit_rope3d.argtypes = [ctypes.POINTER(RopeDesc), vp, vp, vp, i32, vp]
         L.mmdit_joint_attn.restype = i32
         L.mmdit_joint_attn.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, sz, vp]
+        L.mmdit_joint_attn_rope.restype = i32
+        L.mmdit_joint_attn_rope.argtypes = [ctypes.POINTER(RopeDesc), vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz,
+                                            vp]
         L.mmdit_joint_attn_fwd.restype = i32
         L.mmdit_joint_attn_fwd.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]
         L.mmdit_joint_attn_bwd.restype = i32
@@ -135,6 +141,13 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context for the tensors a wrapper allocates (outputs, workspace): they
+    are taken on the stream the kernels run on, so the caching allocator does
+    not hand a freed workspace to other work before those kernels are done."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _ws(nbytes, device, ws):
     if nbytes == 0:
         return None, 0
@@ -159,7 +172,8 @@ def layout_segments(T, H, W, n_cond_frames=0, n_audio=0, n_text=0, audio_scale=N
 
     Conditioning frames form a VIDEO segment at t0 = -n_cond_frames (so one
     frame sits at t = -1); generated frames start at t = 0; audio token j sits
-    at j * audio_scale, audio_scale given as (num, den) (default T / n_audio).
+    at j * audio_scale, audio_scale given as (num, den) (e.g. (21, 218) for
+    218 audio tokens over 21 frames); required when n_audio > 0.
     """
     segs = []
     off = 0
@@ -172,7 +186,9 @@ def layout_segments(T, H, W, n_cond_frames=0, n_audio=0, n_text=0, audio_scale=N
     segs.append(dict(kind=MMDIT_SEG_VIDEO, offset=off, count=n, t0=0, T=T, H=H, W=W))
     off += n
     if n_audio:
-        num, den = audio_scale if audio_scale is not None else (T, n_audio)
+        if audio_scale is None:
+            raise ValueError("layout_segments: audio_scale (num, den) is required with audio tokens")
+        num, den = audio_scale
         segs.append(dict(kind=MMDIT_SEG_AUDIO, offset=off, count=n_audio, t_scale=num / den))
         off += n_audio
     if n_text:
@@ -234,20 +250,50 @@ def mmdit_rope3d(spec, q, k, stream=None):
     return q, k
 
 
+def _scale(softmax_scale):
+    """0 asks the library for its default, 1/sqrt(head_dim)."""
+    return 0.0 if softmax_scale is None else float(softmax_scale)
+
+
 def mmdit_joint_attn(q, k, v, softmax_scale=None, o=None, ws=None, stream=None):
     """Softmax attention of q [n_q, h, d] against k, v [n_kv, h, d]; fp32 output."""
     n_q, h, d = q.shape
     n_kv = k.shape[0]
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
     assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    if o is None:
-        o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_joint_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
-                                  _ptr(o), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_joint_attn(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), _scale(softmax_scale),
+                                      _ptr(o), _ptr(ws), wsb, _stream(stream)))
     return o
+
+
+def mmdit_joint_attn_rope(spec, q, k, v, softmax_scale=None, o=None, q_rot=None, k_rot=None, want_rotated=True,
+                          ws=None, stream=None):
+    """Joint self-attention with the RoPE of `spec` fused in: returns (o fp32,
+    q_rot, k_rot), o the attention of the rotated q, k (bf16, unchanged) over
+    v, and q_rot, k_rot the rotated tensors (None unless want_rotated or
+    given)."""
+    n, h, d = q.shape
+    assert q.dtype == k.dtype == v.dtype == torch.bfloat16 and q.shape == k.shape == v.shape
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    tab = spec.device_table(q.device)
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+        if want_rotated and q_rot is None:
+            q_rot = torch.empty_like(q)
+        if want_rotated and k_rot is None:
+            k_rot = torch.empty_like(k)
+        need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_ROPE, n, n, h, d, MMDIT_BF16)
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_joint_attn_rope(ctypes.byref(spec.desc), _ptr(tab), _ptr(q), _ptr(k), _ptr(v), MMDIT_BF16,
+                                           _scale(softmax_scale), _ptr(o), _ptr(q_rot), _ptr(k_rot), _ptr(ws), wsb,
+                                           _stream(stream)))
+    return o, q_rot, k_rot
 
 
 def mmdit_joint_attn_fwd(q, k, v, softmax_scale=None, o=None, lse=None, ws=None, stream=None):
@@ -257,15 +303,15 @@ def mmdit_joint_attn_fwd(q, k, v, softmax_scale=None, o=None, lse=None, ws=None,
     n_kv = k.shape[0]
     assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
     assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    if o is None:
-        o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((h, n_q), dtype=torch.float32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_joint_attn_fwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
-                                      _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((h, n_q), dtype=torch.float32, device=q.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, n_q, n_kv, h, d, _dtype(q))
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_joint_attn_fwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q),
+                                          _scale(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(stream)))
     return o, lse
 
 
@@ -280,18 +326,18 @@ def mmdit_joint_attn_bwd(q, k, v, o, lse, d_o, softmax_scale=None, dq=None, dk=N
     assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype == d_o.dtype
     assert o.shape == d_o.shape == (n_q, h, d) and o.dtype == torch.float32
     assert lse.shape == (h, n_q) and lse.dtype == torch.float32
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    if dq is None:
-        dq = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
-    if dk is None:
-        dk = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_BWD, n_q, n_kv, h, d, _dtype(q))
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_joint_attn_bwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q), scale,
-                                      _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
-                                      wsb, _stream(stream)))
+    with _on(stream):
+        if dq is None:
+            dq = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+        if dk is None:
+            dk = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
+        if dv is None:
+            dv = torch.empty((n_kv, h, d), dtype=torch.float32, device=q.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN_BWD, n_q, n_kv, h, d, _dtype(q))
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_joint_attn_bwd(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q),
+                                          _scale(softmax_scale), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(ws), wsb, _stream(stream)))
     return dq, dk, dv
 
 
@@ -302,78 +348,81 @@ def mmdit_av_cross_attn(q_v, k_v, v_v, q_a, k_a, v_a, softmax_scale=None, o_vide
     n_a = q_a.shape[0]
     for t in (q_v, k_v, v_v, q_a, k_a, v_a):
         assert t.is_contiguous() and t.dtype == q_v.dtype
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    if o_video is None:
-        o_video = torch.empty((n_v, h, d), dtype=torch.float32, device=q_v.device)
-    if o_audio is None:
-        o_audio = torch.empty((n_a, h, d), dtype=torch.float32, device=q_v.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_AV_CROSS_ATTN, n_v, n_a, h, d, _dtype(q_v))
-    ws, wsb = _ws(need, q_v.device, ws)
-    _check(lib().mmdit_av_cross_attn(_ptr(q_v), _ptr(k_v), _ptr(v_v), n_v, _ptr(q_a), _ptr(k_a),
-                                     _ptr(v_a), n_a, h, d, _dtype(q_v), scale, _ptr(o_video),
-                                     _ptr(o_audio), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        if o_video is None:
+            o_video = torch.empty((n_v, h, d), dtype=torch.float32, device=q_v.device)
+        if o_audio is None:
+            o_audio = torch.empty((n_a, h, d), dtype=torch.float32, device=q_v.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_AV_CROSS_ATTN, n_v, n_a, h, d, _dtype(q_v))
+        ws, wsb = _ws(need, q_v.device, ws)
+        _check(lib().mmdit_av_cross_attn(_ptr(q_v), _ptr(k_v), _ptr(v_v), n_v, _ptr(q_a), _ptr(k_a),
+                                         _ptr(v_a), n_a, h, d, _dtype(q_v), _scale(softmax_scale), _ptr(o_video),
+                                         _ptr(o_audio), _ptr(ws), wsb, _stream(stream)))
     return o_video, o_audio
 
 
-def sparse_desc(zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9):
+def sparse_desc(zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9, wait_limit=0):
     sd = SparseDesc()
     for i in range(3):
         sd.zone[i] = zone[i]
         sd.block[i] = block[i]
     sd.top_k = top_k
     sd.top_p = top_p
+    sd.wait_limit = wait_limit
     return sd
 
 
 def mmdit_block_sparse_attn(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4), top_k=32,
                             top_p=0.9, softmax_scale=None, o=None, sel_mask=None, sel_count=None,
-                            ws=None, stream=None, want_selection=True):
+                            ws=None, stream=None, want_selection=True, wait_limit=0):
     """Block-sparse self-attention over a T x H x W raster grid.
 
     Returns (o fp32, sel_mask uint32-as-int32 [h, nb, ceil(nb/32)], sel_count int32 [h, nb]).
+    wait_limit: see mmdit_sparse_desc (0: the library's bound; tests of the
+    failure path only).
     """
     n, h, d = q.shape
     assert n == T * H * W and q.dtype == torch.bfloat16
-    sd = sparse_desc(zone, block, top_k, top_p)
+    sd = sparse_desc(zone, block, top_k, top_p, wait_limit)
     nb = n // (block[0] * block[1] * block[2])
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    if o is None:
-        o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
-    if want_selection and sel_mask is None:
-        sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
-    if want_selection and sel_count is None:
-        sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_block_sparse_attn(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d,
-                                         ctypes.byref(sd), scale, _ptr(o), _ptr(sel_mask),
-                                         _ptr(sel_count), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+        if want_selection and sel_mask is None:
+            sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+        if want_selection and sel_count is None:
+            sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_block_sparse_attn(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d,
+                                             ctypes.byref(sd), _scale(softmax_scale), _ptr(o), _ptr(sel_mask),
+                                             _ptr(sel_count), _ptr(ws), wsb, _stream(stream)))
     return o, sel_mask, sel_count
 
 
 def mmdit_block_sparse_attn_fwd(q, k, v, T, H, W, zone=(8, 8, 8), block=(4, 4, 4), top_k=32, top_p=0.9,
                                 softmax_scale=None, o=None, lse=None, sel_mask=None, sel_count=None, ws=None,
-                                stream=None):
+                                stream=None, wait_limit=0):
     """Block-sparse attention for a training step: (o fp32, lse fp32 [h, n],
     sel_mask, sel_count); sel_mask feeds mmdit_block_sparse_attn_bwd."""
     n, h, d = q.shape
     assert n == T * H * W and q.dtype == torch.bfloat16
-    sd = sparse_desc(zone, block, top_k, top_p)
+    sd = sparse_desc(zone, block, top_k, top_p, wait_limit)
     nb = n // (block[0] * block[1] * block[2])
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    if o is None:
-        o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
-    if sel_mask is None:
-        sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
-    if sel_count is None:
-        sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd), scale,
-                                             _ptr(o), _ptr(lse), _ptr(sel_mask), _ptr(sel_count), _ptr(ws), wsb,
-                                             _stream(stream)))
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((h, n), dtype=torch.float32, device=q.device)
+        if sel_mask is None:
+            sel_mask = torch.empty((h, nb, (nb + 31) // 32), dtype=torch.int32, device=q.device)
+        if sel_count is None:
+            sel_count = torch.empty((h, nb), dtype=torch.int32, device=q.device)
+        need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN, n, n, h, d, MMDIT_BF16, sd)
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd),
+                                                 _scale(softmax_scale), _ptr(o), _ptr(lse), _ptr(sel_mask),
+                                                 _ptr(sel_count), _ptr(ws), wsb, _stream(stream)))
     return o, lse, sel_mask, sel_count
 
 
@@ -398,9 +447,10 @@ def mmdit_token_norms(x, out=None, stream=None):
     assert x.dtype == torch.float32 and x.is_contiguous()
     n = x.shape[0]
     width = x.numel() // max(n, 1)
-    if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=x.device)
-    _check(lib().mmdit_token_norms(_ptr(x), n, width, _ptr(out), _stream(stream)))
+    with _on(stream):
+        if out is None:
+            out = torch.empty(n, dtype=torch.float32, device=x.device)
+        _check(lib().mmdit_token_norms(_ptr(x), n, width, _ptr(out), _stream(stream)))
     return out
 
 
@@ -418,23 +468,23 @@ def mmdit_block_sparse_attn_adaptive(q, k, v, T, H, W, a_norm=None, top_k=32, to
         assert a_norm.dtype == torch.float32 and a_norm.numel() == n and a_norm.is_contiguous()
     nt, nz = n // 64, n // 512
     dev = q.device
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    if o is None:
-        o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
-    if lse is None and want_lse:
-        lse = torch.empty((h, n), dtype=torch.float32, device=dev)
-    out = dict(o=o, lse=lse,
-               zone_shape=torch.empty(nz, dtype=torch.uint8, device=dev),
-               tile_block=torch.empty(nt, dtype=torch.int32, device=dev),
-               n_blocks=torch.empty(1, dtype=torch.int32, device=dev),
-               sel_mask=torch.empty((h, nt, (nt + 31) // 32), dtype=torch.int32, device=dev),
-               sel_count=torch.empty((h, nt), dtype=torch.int32, device=dev))
-    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, n, 0, h, d, MMDIT_BF16, None)
-    ws, wsb = _ws(need, dev, ws)
-    _check(lib().mmdit_block_sparse_attn_adaptive(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(a_norm), T, H, W, h, d, top_k, top_p, scale, _ptr(o), _ptr(lse),
-        _ptr(out["zone_shape"]), _ptr(out["tile_block"]), _ptr(out["n_blocks"]), _ptr(out["sel_mask"]),
-        _ptr(out["sel_count"]), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n, h, d), dtype=torch.float32, device=dev)
+        if lse is None and want_lse:
+            lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+        out = dict(o=o, lse=lse,
+                   zone_shape=torch.empty(nz, dtype=torch.uint8, device=dev),
+                   tile_block=torch.empty(nt, dtype=torch.int32, device=dev),
+                   n_blocks=torch.empty(1, dtype=torch.int32, device=dev),
+                   sel_mask=torch.empty((h, nt, (nt + 31) // 32), dtype=torch.int32, device=dev),
+                   sel_count=torch.empty((h, nt), dtype=torch.int32, device=dev))
+        need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, n, 0, h, d, MMDIT_BF16, None)
+        ws, wsb = _ws(need, dev, ws)
+        _check(lib().mmdit_block_sparse_attn_adaptive(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(a_norm), T, H, W, h, d, top_k, top_p, _scale(softmax_scale), _ptr(o),
+            _ptr(lse), _ptr(out["zone_shape"]), _ptr(out["tile_block"]), _ptr(out["n_blocks"]),
+            _ptr(out["sel_mask"]), _ptr(out["sel_count"]), _ptr(ws), wsb, _stream(stream)))
     return out
 
 
@@ -448,15 +498,15 @@ def mmdit_block_sparse_attn_adaptive_bwd(q, k, v, fwd, d_o, T, H, W, softmax_sca
     assert fwd["lse"] is not None, "the forward must keep the log-sum-exp (want_lse=True)"
     for t in (q, k, v, d_o, fwd["o"], fwd["lse"], fwd["zone_shape"], fwd["sel_mask"]):
         assert t.is_contiguous()
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=q.device) if t is None else t
-                  for t in (dq, dk, dv))
-    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, d, MMDIT_BF16, None)
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_block_sparse_attn_adaptive_bwd(
-        _ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, scale, _ptr(fwd["o"]), _ptr(fwd["lse"]), _ptr(d_o),
-        _ptr(fwd["zone_shape"]), _ptr(fwd["sel_mask"]), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
-        _stream(stream)))
+    with _on(stream):
+        dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=q.device) if t is None else t
+                      for t in (dq, dk, dv))
+        need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, d, MMDIT_BF16, None)
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_block_sparse_attn_adaptive_bwd(
+            _ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, _scale(softmax_scale), _ptr(fwd["o"]), _ptr(fwd["lse"]),
+            _ptr(d_o), _ptr(fwd["zone_shape"]), _ptr(fwd["sel_mask"]), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
+            _stream(stream)))
     return dq, dk, dv
 
 
@@ -469,16 +519,13 @@ def mmdit_block_sparse_attn_bwd(q, k, v, o, lse, d_o, sel_mask, T, H, W, zone=(8
     for t in (q, k, v, o, lse, d_o, sel_mask):
         assert t.is_contiguous()
     sd = sparse_desc(zone, block, 0, 1.0)
-    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    if dq is None:
-        dq = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
-    if dk is None:
-        dk = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty((n, h, d), dtype=torch.float32, device=q.device)
-    need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, d, MMDIT_BF16, sd)
-    ws, wsb = _ws(need, q.device, ws)
-    _check(lib().mmdit_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd), scale,
-                                             _ptr(o), _ptr(lse), _ptr(d_o), _ptr(sel_mask), _ptr(dq), _ptr(dk),
-                                             _ptr(dv), _ptr(ws), wsb, _stream(stream)))
+    with _on(stream):
+        dq, dk, dv = (torch.empty((n, h, d), dtype=torch.float32, device=q.device) if t is None else t
+                      for t in (dq, dk, dv))
+        need = mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, d, MMDIT_BF16, sd)
+        ws, wsb = _ws(need, q.device, ws)
+        _check(lib().mmdit_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), T, H, W, h, d, ctypes.byref(sd),
+                                                 _scale(softmax_scale), _ptr(o), _ptr(lse), _ptr(d_o),
+                                                 _ptr(sel_mask), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), wsb,
+                                                 _stream(stream)))
     return dq, dk, dv

@@ -42,14 +42,23 @@ size_t elem_size(int dtype) { return dtype == MMDIT_BF16 ? 2 : 4; }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// softmax_scale 0 selects the usual 1/sqrt(head_dim) (the scale of the
+// attention the pages describe; SkyReels-V4 analysis, workflow step 3).
+double resolve_scale(double s, int hd) { return s == 0.0 ? 1.0 / std::sqrt((double)hd) : s; }
+float resolve_scale(float s, int hd) { return s == 0.f ? (float)(1.0 / std::sqrt((double)hd)) : s; }
+
+bool scale_ok(double s) { return std::isfinite(s) && s >= 0.0 && std::isfinite((float)s); }
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- dense attention plan ----------------------------------------------------
+// Workspace of a bf16 attention: fp16 V^T, the partial maxima of V (its
+// prescale exponents) and, for split key ranges, the partial O and (m, l).
 struct AttnPlan {
     int64_t n_pad, n_q_pad;
     int32_t q_tile, q_tiles, kv_tiles, splits, tiles_per_split;
-    size_t vt_bytes, part_o_bytes, part_ml_bytes;
-    size_t total() const { return vt_bytes + part_o_bytes + part_ml_bytes; }
+    size_t vt_bytes, vmax_bytes, part_o_bytes, part_ml_bytes;
+    size_t total() const { return vt_bytes + vmax_bytes + part_o_bytes + part_ml_bytes; }
 };
 
 AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
@@ -70,6 +79,7 @@ AttnPlan plan_attn(int64_t n_q, int64_t n_kv, int heads, int hd, int dtype) {
     p.tiles_per_split = (p.kv_tiles + splits - 1) / splits;
     p.splits = (p.kv_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
     p.vt_bytes = align256((size_t)heads * hd * p.n_pad * 2);
+    p.vmax_bytes = align256((size_t)heads * kVmaxParts * 4);
     if (p.splits > 1) {
         p.part_o_bytes = align256((size_t)p.splits * heads * p.n_q_pad * hd * 4);
         p.part_ml_bytes = align256((size_t)p.splits * heads * p.n_q_pad * 2 * 4);
@@ -88,8 +98,9 @@ mmdit_status check_attn_args(const void* q, int64_t n_q, const void* k, const vo
     if (heads < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: heads %d < 1", who, heads);
     if (n_q < 0) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_q %lld < 0", who, (long long)n_q);
     if (n_kv < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_kv %lld < 1", who, (long long)n_kv);
-    if (!std::isfinite(scale) || !(scale > 0.f))
-        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    if (!scale_ok(scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0 (0: 1/sqrt(head_dim))",
+                    who);
     const int64_t lim = (int64_t)1 << 31;
     if (n_q * heads >= lim || n_kv * heads >= lim)
         return fail(MMDIT_ERR_UNSUPPORTED, "%s: tokens * heads must stay below 2^31", who);
@@ -130,8 +141,10 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
     a.vt = (const _Float16*)ws;
     a.o = o;
     a.lse = lse;
-    a.part_o = p.splits > 1 ? (float*)(ws + p.vt_bytes) : nullptr;
-    a.part_ml = p.splits > 1 ? (float*)(ws + p.vt_bytes + p.part_o_bytes) : nullptr;
+    uint32_t* vmax = (uint32_t*)(ws + p.vt_bytes);
+    a.vmax = vmax;
+    a.part_o = p.splits > 1 ? (float*)(ws + p.vt_bytes + p.vmax_bytes) : nullptr;
+    a.part_ml = p.splits > 1 ? (float*)(ws + p.vt_bytes + p.vmax_bytes + p.part_o_bytes) : nullptr;
     a.n_q = n_q;
     a.n_kv = n_kv;
     a.n_pad = p.n_pad;
@@ -143,7 +156,9 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
     a.tiles_per_split = p.tiles_per_split;
     a.kv_tiles = p.kv_tiles;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    e = launch_vt_dense((const __bf16*)v, n_kv, p.n_pad, heads, hd, (_Float16*)ws, s);
+    e = launch_v_absmax((const __bf16*)v, n_kv, heads, hd, vmax, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    e = launch_vt_dense((const __bf16*)v, n_kv, p.n_pad, heads, hd, vmax, (_Float16*)ws, s);
     if (e != hipSuccess) return hip_fail(e, who);
     e = launch_attn_bf16(a, hd, s);
     if (e != hipSuccess) return hip_fail(e, who);
@@ -152,6 +167,12 @@ mmdit_status run_attn(const void* q, int64_t n_q, const void* k, const void* v, 
         if (e != hipSuccess) return hip_fail(e, who);
     }
     return MMDIT_OK;
+}
+
+// The RoPE-fused joint attention: the attention workspace, then room for the
+// rotated K when the caller does not take it.
+size_t rope_attn_ws_bytes(int64_t n, int heads, int hd) {
+    return plan_attn(n, n, heads, hd, MMDIT_BF16).total() + align256((size_t)n * heads * hd * 2);
 }
 
 // ---- dense attention backward plan -------------------------------------------------
@@ -276,12 +297,13 @@ mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
 // ---- block sparse plan ------------------------------------------------------------
 struct SparsePlan {
     SparseGeom g{};
-    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, total;
+    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, off_vmax, total;
 };
 
 // Workspace layout of a block-sparse call (shared by the plan and the size
 // query): fp64 block means, fp64 scores, selection bitmask and counts, block
-// first tokens, per-block fp16 V^T and per-block K tile images.
+// first tokens, per-block fp16 V^T and per-block K tile images, the partial
+// maxima of V (its prescale exponents).
 void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -297,6 +319,7 @@ void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
     p->off_base = take((size_t)nb * 4);
     p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
     p->off_kimg = take((size_t)heads * nb * hd * kTileN * 2);
+    p->off_vmax = take((size_t)heads * kVmaxParts * 4);
     p->total = off;
 }
 
@@ -317,6 +340,8 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     if (sp->top_k < 0) return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: top_k < 0");
     if (!(sp->top_p >= 0.0 && sp->top_p <= 1.0))
         return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: top_p must lie in [0, 1]");
+    if (sp->wait_limit < 0 || sp->wait_limit > kSpinLimit)
+        return fail(MMDIT_ERR_INVALID_ARG, "block_sparse: wait_limit must lie in [0, %d]", kSpinLimit);
     const int64_t n = (int64_t)T * H * W;
     if (n * heads >= ((int64_t)1 << 31))
         return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: tokens * heads must stay below 2^31");
@@ -392,8 +417,10 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
         ap = adaptive_layout(p.total, p.g.nb, heads, head_dim);
         p.total = ap.total;
     }
-    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
-        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    if (!scale_ok(softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0 (0: 1/sqrt(head_dim))",
+                    who);
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     if (!q || !k || !v || !o) return fail(MMDIT_ERR_INVALID_ARG, "%s: null q, k, v or o", who);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(MMDIT_ERR_INVALID_ARG, "%s: q, k, v, o must be 16-byte aligned", who);
@@ -436,6 +463,7 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
     sw.base = (int32_t*)(w + p.off_base);
     sw.vt = (_Float16*)(w + p.off_vt);
     sw.kimg = (__bf16*)(w + p.off_kimg);
+    sw.vmax = (uint32_t*)(w + p.off_vmax);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (ad) {
@@ -457,6 +485,8 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
     }
     if ((e = launch_block_pool(p.g, (const __bf16*)q, (const __bf16*)k, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse pool");
+    if ((e = launch_v_absmax((const __bf16*)v, (int64_t)T * H * W, heads, head_dim, sw.vmax, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse v prescale");
     if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse vt");
     if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
@@ -464,8 +494,8 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
     if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, sel_mask, sel_count, s)) != hipSuccess)
         return hip_fail(e, "block_sparse select");
     if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
-                                (float)(softmax_scale * 1.4426950408889634), sw, o, lse, s)) !=
-        hipSuccess)
+                                (float)(softmax_scale * 1.4426950408889634), sw, o, lse,
+                                sp->wait_limit ? sp->wait_limit : kSpinLimit, s)) != hipSuccess)
         return hip_fail(e, "block_sparse attention");
     return MMDIT_OK;
 }
@@ -613,6 +643,10 @@ size_t mmdit_workspace_bytes(int32_t op, int64_t n_q, int64_t n_kv, int32_t head
         if (n_kv < 1) return 0;
         return plan_attn(n_q, n_kv, heads, head_dim, dtype).total();
     }
+    if (op == MMDIT_OP_JOINT_ATTN_ROPE) {
+        if (n_q < 1) return 0;
+        return rope_attn_ws_bytes(n_q, heads, head_dim);
+    }
     if (op == MMDIT_OP_AV_CROSS_ATTN) {
         if (n_q < 1 || n_kv < 1) return 0;
         return plan_attn(n_q, n_kv, heads, head_dim, dtype).total() +
@@ -666,8 +700,80 @@ mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const v
     if (st != MMDIT_OK) return st;
     const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
     if (n_q > 0 && (st = check_ws(ws, ws_bytes, p.total(), "joint_attn")) != MMDIT_OK) return st;
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, nullptr, (char*)ws, p,
                     (hipStream_t)stream, "joint_attn");
+}
+
+mmdit_status mmdit_joint_attn_rope(const mmdit_rope_desc* desc, const float* dev_table, const void* q,
+                                   const void* k, const void* v, int32_t dtype, float softmax_scale, float* o,
+                                   void* q_rot, void* k_rot, void* ws, size_t ws_bytes, void* stream) {
+    const char* who = "joint_attn_rope";
+    RopePlan rp;
+    mmdit_status st = plan_rope(desc, dtype, &rp);
+    if (st != MMDIT_OK) return st;
+    if (dtype != MMDIT_BF16)
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: bf16 only (fp32: mmdit_rope3d, then mmdit_joint_attn)", who);
+    const int64_t n = desc->n_tokens;
+    const int heads = desc->heads, hd = desc->head_dim;
+    if (n < 1) return fail(MMDIT_ERR_INVALID_ARG, "%s: n_tokens must be >= 1", who);
+    if ((st = check_attn_args(q, n, k, v, n, heads, hd, dtype, softmax_scale, o, who)) != MMDIT_OK) return st;
+    if (rp.floats > 0 && (!dev_table || (reinterpret_cast<uintptr_t>(dev_table) & 7u)))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: the table must be a non-null 8-byte aligned device pointer", who);
+    const size_t tb = (size_t)n * heads * hd * 2;
+    if ((q_rot && !aligned16(q_rot)) || (k_rot && !aligned16(k_rot)))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: q_rot and k_rot must be 16-byte aligned", who);
+    const void* ins[4] = {q, k, v, o};
+    const size_t isz[4] = {tb, tb, tb, tb * 2};
+    for (void* out : {q_rot, k_rot}) {
+        if (!out) continue;
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(out, tb, ins[j], isz[j]))
+                return fail(MMDIT_ERR_INVALID_ARG, "%s: q_rot and k_rot must not overlap q, k, v or o", who);
+    }
+    if (q_rot && k_rot && overlaps(q_rot, tb, k_rot, tb))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: q_rot and k_rot overlap", who);
+    const AttnPlan p = plan_attn(n, n, heads, hd, dtype);
+    if ((st = check_ws(ws, ws_bytes, rope_attn_ws_bytes(n, heads, hd), who)) != MMDIT_OK) return st;
+    if (ws_bytes && (overlaps(ws, rope_attn_ws_bytes(n, heads, hd), q_rot ? q_rot : ws, q_rot ? tb : 0) ||
+                     overlaps(ws, rope_attn_ws_bytes(n, heads, hd), k_rot ? k_rot : ws, k_rot ? tb : 0)))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: the workspace overlaps q_rot or k_rot", who);
+    softmax_scale = resolve_scale(softmax_scale, hd);
+    char* w = (char*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    RopeFused rf{};
+    rf.a = rp.args;
+    rf.tab = reinterpret_cast<const float2*>(dev_table);
+    rf.k = (const __bf16*)k;
+    rf.k_out = k_rot ? (__bf16*)k_rot : (__bf16*)(w + p.total());
+    rf.q_out = (__bf16*)q_rot;
+    AttnArgs a{};
+    a.q = (const __bf16*)q;
+    a.k = rf.k_out;
+    a.vt = (const _Float16*)w;
+    uint32_t* vmax = (uint32_t*)(w + p.vt_bytes);
+    a.vmax = vmax;
+    a.part_o = p.splits > 1 ? (float*)(w + p.vt_bytes + p.vmax_bytes) : nullptr;
+    a.part_ml = p.splits > 1 ? (float*)(w + p.vt_bytes + p.vmax_bytes + p.part_o_bytes) : nullptr;
+    a.o = o;
+    a.n_q = a.n_kv = n;
+    a.n_pad = p.n_pad;
+    a.n_q_pad = p.n_q_pad;
+    a.heads = heads;
+    a.q_tile = p.q_tile;
+    a.q_tiles = p.q_tiles;
+    a.splits = p.splits;
+    a.tiles_per_split = p.tiles_per_split;
+    a.kv_tiles = p.kv_tiles;
+    a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+    hipError_t e;
+    if ((e = launch_v_absmax((const __bf16*)v, n, heads, hd, vmax, s)) != hipSuccess ||
+        (e = launch_vt_dense_rope((const __bf16*)v, n, p.n_pad, heads, hd, vmax, (_Float16*)w, rf, s)) !=
+            hipSuccess ||
+        (e = launch_attn_bf16_rope(a, hd, rf, s)) != hipSuccess ||
+        (p.splits > 1 && (e = launch_attn_combine(a, hd, s)) != hipSuccess))
+        return hip_fail(e, who);
+    return MMDIT_OK;
 }
 
 mmdit_status mmdit_joint_attn_fwd(const void* q, int64_t n_q, const void* k, const void* v,
@@ -689,6 +795,7 @@ mmdit_status mmdit_joint_attn_fwd(const void* q, int64_t n_q, const void* k, con
     }
     const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
     if (n_q > 0 && (st = check_ws(ws, ws_bytes, p.total(), "joint_attn_fwd")) != MMDIT_OK) return st;
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, lse, (char*)ws, p,
                     (hipStream_t)stream, "joint_attn_fwd");
 }
@@ -726,6 +833,7 @@ mmdit_status mmdit_joint_attn_bwd(const void* q, int64_t n_q, const void* k, con
     }
     const BwdPlan p = plan_bwd(n_q, n_kv, heads, head_dim, dtype);
     if ((st = check_ws(ws, ws_bytes, p.total, who)) != MMDIT_OK) return st;
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
@@ -796,6 +904,7 @@ mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v
     const AttnPlan pav = plan_attn(n_audio, n_video, heads, head_dim, dtype);
     if ((st = check_ws(ws, ws_bytes, pva.total() + pav.total(), "av_cross_attn")) != MMDIT_OK)
         return st;
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     char* w = (char*)ws;
     st = run_attn(q_v, n_video, k_a, v_a, n_audio, heads, head_dim, dtype, softmax_scale, o_video,
                   nullptr, w, pva, (hipStream_t)stream, "av_cross_attn (video->audio)");
@@ -900,8 +1009,10 @@ mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const voi
     SparsePlan p{};
     mmdit_status st = plan_sparse(T, H, W, heads, head_dim, sp, &p);
     if (st != MMDIT_OK) return st;
-    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
-        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    if (!scale_ok(softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0 (0: 1/sqrt(head_dim))",
+                    who);
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     const void* al16[8] = {q, k, v, o, d_o, dq, dk, dv};
     for (const void* ptr : al16)
         if (!ptr || !aligned16(ptr))
@@ -952,8 +1063,10 @@ mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, 
     SparsePlan p{};
     mmdit_status st = plan_sparse(1, 1, (int)std::min<int64_t>(n, INT32_MAX), heads, head_dim, &flat, &p);
     if (st != MMDIT_OK) return st;
-    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0) || !std::isfinite((float)softmax_scale))
-        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be positive and finite", who);
+    if (!scale_ok(softmax_scale))
+        return fail(MMDIT_ERR_INVALID_ARG, "%s: softmax_scale must be finite and >= 0 (0: 1/sqrt(head_dim))",
+                    who);
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
     const void* al16[8] = {q, k, v, o, d_o, dq, dk, dv};
     for (const void* ptr : al16)
         if (!ptr || !aligned16(ptr))

@@ -23,13 +23,46 @@ namespace mmdit {
 
 namespace {
 
-// ---- V^T staging: [n_kv][heads][hd] bf16 -> [heads][hd][n_pad] fp16 -------
+// ---- V prescale: per-head largest magnitude -----------------------------------
+// Workgroup (part, head) scans tokens [part * per, (part + 1) * per) of one
+// head: each thread reads 16-byte chunks of a fixed column of the head's row.
+template <int HD>
+__global__ __launch_bounds__(256) void v_absmax_kernel(const __bf16* __restrict__ v, int64_t n, int heads,
+                                                       uint32_t* __restrict__ vmax) {
+    __shared__ uint32_t wmax[4];
+    const int part = blockIdx.x, head = blockIdx.y;
+    constexpr int CPR = HD / 8;          // 16-byte chunks per (token, head) row
+    constexpr int RPI = 256 / CPR;       // rows per iteration
+    const int64_t per = (n + kVmaxParts - 1) / kVmaxParts;
+    const int64_t t0 = (int64_t)part * per;
+    const int64_t t1 = t0 + per < n ? t0 + per : n;
+    const int c = threadIdx.x % CPR;
+    uint32_t m = 0u;
+    for (int64_t t = t0 + threadIdx.x / CPR; t < t1; t += RPI) {
+        const uint4 u = *reinterpret_cast<const uint4*>(v + (t * heads + head) * HD + c * 8);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+            m = max(m, max(lo, hi));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        vmax[(int64_t)head * kVmaxParts + part] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+}
+
+// ---- V^T staging: [n_kv][heads][hd] bf16 -> [heads][hd][n_pad] fp16, x 2^e ----
 template <int HD>
 __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict__ v, int64_t n_kv,
-                                                       int64_t n_pad, int heads,
+                                                       int64_t n_pad, int heads, const uint32_t* __restrict__ vmax,
                                                        _Float16* __restrict__ vt) {
     __shared__ _Float16 tile[kTileN][HD + 2];
     const int head = blockIdx.y;
+    const float sc = __builtin_ldexpf(1.f, v_scale_exp(vmax, head));
     const int64_t k0 = (int64_t)blockIdx.x * kTileN;
     constexpr int CPR = HD / 8;                 // 16-byte chunks per row
     for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
@@ -37,7 +70,7 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
         const int64_t key = k0 + r;
         const bf16x8 x = load_bf16x8(v + (key * heads + head) * HD + c * 8, key < n_kv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)(float)x[i];
+        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)((float)x[i] * sc);
     }
     __syncthreads();
     // each thread writes 8 consecutive keys of one d row
@@ -50,10 +83,47 @@ __global__ __launch_bounds__(256) void vt_dense_kernel(const __bf16* __restrict_
     }
 }
 
+// The staging pass of the RoPE-fused joint attention: the same V^T tile as
+// vt_dense_kernel, and the tile's 64 K rows of this head rotated into k_out
+// (16 lanes per 256-byte row, one 8-element chunk each).
+template <int HD>
+__global__ __launch_bounds__(256) void vt_dense_rope_kernel(const __bf16* __restrict__ v, int64_t n_kv,
+                                                            int64_t n_pad, int heads,
+                                                            const uint32_t* __restrict__ vmax,
+                                                            _Float16* __restrict__ vt, RopeFused r) {
+    __shared__ _Float16 tile[kTileN][HD + 2];
+    const int head = blockIdx.y;
+    const float sc = __builtin_ldexpf(1.f, v_scale_exp(vmax, head));
+    const int64_t k0 = (int64_t)blockIdx.x * kTileN;
+    constexpr int CPR = HD / 8;
+    for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
+        const int rr = u / CPR, c = u % CPR;
+        const int64_t key = k0 + rr;
+        const int64_t off = (key * heads + head) * HD + c * 8;
+        const bf16x8 x = load_bf16x8(v + off, key < n_kv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[rr][c * 8 + i] = (_Float16)((float)x[i] * sc);
+        if (key < n_kv) {
+            const bf16x8 kx = load_bf16x8(r.k + off, true);
+            *reinterpret_cast<bf16x8*>(r.k_out + off) = rope_chunk_bf16(kx, r.tab, rope_table_index(r.a, key, c * 8));
+        }
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < HD * (kTileN / 8); u += 256) {
+        const int d = u / (kTileN / 8), c = u % (kTileN / 8);
+        f16x8 y;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = tile[c * 8 + i][d];
+        *reinterpret_cast<f16x8*>(vt + ((int64_t)head * HD + d) * n_pad + k0 + c * 8) = y;
+    }
+}
+
 // NW waves of QB blocks of 32 queries: a workgroup serves 32 NW QB queries.
 // Four-wave workgroups run two per CU, so they must fit two waves per SIMD.
-template <int HD, int QB, int NW>
-__global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs a) {
+// With ROPE, each lane rotates its Q fragments as it loads them (the RoPE-
+// fused joint attention) and the first key split stores them to r->q_out.
+template <int HD, int QB, int NW, bool ROPE>
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFused* r) {
     using L = TileLayout<HD>;
     constexpr int QT = 32 * NW * QB;
     constexpr int KS = HD / 16;
@@ -79,6 +149,8 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs 
     const int64_t rstride = (int64_t)a.heads * HD;
     const int64_t krb = rstride * 2;                            // bytes per key row
 
+    // O^T accumulates V scaled by 2^ve; the epilogue scales back (exact)
+    const int ve = v_scale_exp(a.vmax, head);
     // query row of this lane in query block qb: qrow0 + 32 qb
     const int64_t qrow0 = (int64_t)qt * QT + w * 32 * QB + m;
     bf16x8 qf[QB][KS];
@@ -89,6 +161,20 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs 
             const int64_t qrow = qrow0 + 32 * qb;
             qf[qb][ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
         }
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int64_t qrow = qrow0 + 32 * qb;
+            if (qrow >= a.n_q) continue;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int dim = 16 * ks + 8 * hh;
+                qf[qb][ks] = rope_chunk_bf16(qf[qb][ks], r->tab, rope_table_index(r->a, qrow, dim));
+                if (r->q_out && split == 0)
+                    *reinterpret_cast<bf16x8*>(r->q_out + qrow * rstride + head * HD + dim) = qf[qb][ks];
+            }
+        }
+    }
 
     // Each lane's share of the tile copies, fixed for the whole key walk: the
     // byte offset (from the tile's first key row) of the 16-byte chunk that
@@ -218,16 +304,26 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs 
         const int64_t qrow = qrow0 + 32 * qb;
         if (qrow >= a.n_q) continue;
         if (a.splits == 1) {
-            store_o<HD>(a.o + qrow * rstride + head * HD, st.o[qb], 1.f / l_tot);
+            store_o<HD>(a.o + qrow * rstride + head * HD, st.o[qb], __builtin_ldexpf(1.f / l_tot, -ve));
             // log-sum-exp of the scaled logits, natural log: the reference
             // maximum and the running sum are in the exp2 domain
             if (a.lse && hh == 0) a.lse[(int64_t)head * a.n_q + qrow] = (st.m_run[qb] + log2f(l_tot)) * kLn2;
         } else {
             const int64_t prow = ((int64_t)split * a.heads + head) * a.n_q_pad + qrow;
-            store_o<HD>(a.part_o + prow * HD, st.o[qb], 1.f);
+            store_o<HD>(a.part_o + prow * HD, st.o[qb], __builtin_ldexpf(1.f, -ve));
             if (hh == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(st.m_run[qb], l_tot);
         }
     }
+}
+
+template <int HD, int QB, int NW>
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_kernel(AttnArgs a) {
+    attn_bf16_body<HD, QB, NW, false>(a, nullptr);
+}
+
+template <int HD, int QB, int NW>
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void attn_bf16_rope_kernel(AttnArgs a, RopeFused r) {
+    attn_bf16_body<HD, QB, NW, true>(a, &r);
 }
 
 // Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
@@ -302,13 +398,22 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(const float* __restrict__
 
 }  // namespace
 
+hipError_t launch_v_absmax(const __bf16* v, int64_t n, int heads, int hd, uint32_t* vmax, hipStream_t s) {
+    dim3 grid((unsigned)kVmaxParts, (unsigned)heads);
+    if (hd == 128)
+        hipLaunchKernelGGL(v_absmax_kernel<128>, grid, dim3(256), 0, s, v, n, heads, vmax);
+    else
+        hipLaunchKernelGGL(v_absmax_kernel<64>, grid, dim3(256), 0, s, v, n, heads, vmax);
+    return hipGetLastError();
+}
+
 hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
-                           _Float16* vt, hipStream_t s) {
+                           const uint32_t* vmax, _Float16* vt, hipStream_t s) {
     dim3 grid((unsigned)(n_pad / kTileN), (unsigned)heads);
     if (hd == 128)
-        hipLaunchKernelGGL(vt_dense_kernel<128>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vt);
+        hipLaunchKernelGGL(vt_dense_kernel<128>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vmax, vt);
     else
-        hipLaunchKernelGGL(vt_dense_kernel<64>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vt);
+        hipLaunchKernelGGL(vt_dense_kernel<64>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vmax, vt);
     return hipGetLastError();
 }
 
@@ -326,6 +431,33 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s) {
         hipLaunchKernelGGL((attn_bf16_kernel<128, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
     } else {
         hipLaunchKernelGGL((attn_bf16_kernel<64, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_vt_dense_rope(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
+                                const uint32_t* vmax, _Float16* vt, const RopeFused& r, hipStream_t s) {
+    dim3 grid((unsigned)(n_pad / kTileN), (unsigned)heads);
+    if (hd == 128)
+        hipLaunchKernelGGL(vt_dense_rope_kernel<128>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vmax, vt, r);
+    else
+        hipLaunchKernelGGL(vt_dense_rope_kernel<64>, grid, dim3(256), 0, s, v, n_kv, n_pad, heads, vmax, vt, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_rope(const AttnArgs& a, int hd, const RopeFused& r, hipStream_t s) {
+    const int total = a.q_tiles * a.heads * a.splits;
+    const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    constexpr int QB = kDenseQB, NW = dense_threads(QB) / kWave, NS = kShortQ / 32;
+    if (a.q_tile == kShortQ) {
+        if (hd == 128)
+            hipLaunchKernelGGL((attn_bf16_rope_kernel<128, 1, NS>), dim3(blocks), dim3(NS * kWave), 0, s, a, r);
+        else
+            hipLaunchKernelGGL((attn_bf16_rope_kernel<64, 1, NS>), dim3(blocks), dim3(NS * kWave), 0, s, a, r);
+    } else if (hd == 128) {
+        hipLaunchKernelGGL((attn_bf16_rope_kernel<128, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a, r);
+    } else {
+        hipLaunchKernelGGL((attn_bf16_rope_kernel<64, QB, NW>), dim3(blocks), dim3(dense_threads(QB)), 0, s, a, r);
     }
     return hipGetLastError();
 }

@@ -62,15 +62,101 @@ struct RopeArgs {
 hipError_t launch_rope(const RopeArgs& a, const float* table, void* q, void* k, int dtype,
                        hipStream_t s);
 
+// Rotation of one adjacent pair (x0, x1) by the angle whose (cos, sin) is
+// (c, s), with the roundings spelled out (one product, then one fused
+// multiply-add per output) so that every kernel that rotates produces the
+// same bits.
+__device__ __forceinline__ void rope_pair(float x0, float x1, float c, float s, float& y0, float& y1) {
+    y0 = __builtin_fmaf(x0, c, -(x1 * s));
+    y1 = __builtin_fmaf(x0, s, x1 * c);
+}
+
+// float2 index into the (cos, sin) table of the first pair of the 8-element
+// chunk that starts at element `dim` (a multiple of 8) of token `tok` (an
+// index into the [n_tokens][heads][head_dim] buffer), or -1 when that chunk
+// is not rotated (text and other tokens outside every segment, and the h and
+// w slices of audio tokens, which sit at position 0).
+__device__ __forceinline__ int rope_table_index(const RopeArgs& a, int64_t tok, int dim) {
+    for (int i = 0; i < a.n_segs; ++i) {
+        const RopeSeg& sg = a.seg[i];
+        const int64_t count = (sg.chunk_end - sg.chunk_begin) / a.chunks_per_token;
+        if (tok < sg.offset || tok >= sg.offset + count) continue;
+        const int t = (int)(tok - sg.offset);
+        if (dim < a.d_t) {
+            const int p = sg.kind == MMDIT_SEG_VIDEO ? t / (sg.H * sg.W) : t;
+            return sg.tab_t + p * (a.d_t >> 1) + (dim >> 1);
+        }
+        if (sg.kind != MMDIT_SEG_VIDEO) return -1;
+        if (dim < a.d_t + a.d_h) return sg.tab_h + ((t / sg.W) % sg.H) * (a.d_h >> 1) + ((dim - a.d_t) >> 1);
+        return sg.tab_w + (t % sg.W) * (a.d_w >> 1) + ((dim - a.d_t - a.d_h) >> 1);
+    }
+    return -1;
+}
+
+// Rotate 8 bf16 values (elements dim .. dim + 7 of one token row) in fp32
+// with table pairs tab[ti .. ti + 3]; results rounded to bf16 (nearest even).
+__device__ __forceinline__ bf16x8 rope_chunk_bf16(bf16x8 x, const float2* __restrict__ tab, int ti) {
+    if (ti < 0) return x;
+    bf16x8 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float2 cs = tab[ti + i];
+        float y0, y1;
+        rope_pair((float)x[2 * i], (float)x[2 * i + 1], cs.x, cs.y, y0, y1);
+        y[2 * i] = (__bf16)y0;
+        y[2 * i + 1] = (__bf16)y1;
+    }
+    return y;
+}
+
+// ---- fp16 staging of V -----------------------------------------------------------
+// V enters the P V products as fp16 (three more mantissa bits than bf16, for
+// P).  A bf16 value converts to fp16 exactly only inside fp16's normal range,
+// so each head's V is first scaled by a power of two 2^e chosen from the
+// head's largest magnitude: the largest entry lands in [2^14, 2^15), nothing
+// overflows whatever the range of V, every entry within 2^-28 of the largest
+// converts exactly, and O is scaled back by 2^-e (also exact).  For values
+// that are already inside fp16's range the results are bitwise those of an
+// unscaled conversion.
+constexpr int kVmaxParts = 64;   // partial maxima per head, reduced by one wave
+
+// vmax [heads][kVmaxParts]: the largest bf16 magnitude (bits & 0x7FFF) of
+// each head over kVmaxParts slices of the n tokens of v [n][heads][hd].
+hipError_t launch_v_absmax(const __bf16* v, int64_t n, int heads, int hd, uint32_t* vmax, hipStream_t s);
+
+// Exponent e of the prescale for the largest bf16 magnitude m (bits): 0 for
+// an all-zero head or one holding inf / NaN (they propagate as in the
+// definition), else 14 - floor(log2(max)), at most 100 (V below 2^-86 is left
+// partly subnormal in fp16).
+__host__ __device__ __forceinline__ int v_exp_from_max(uint32_t m) {
+    if (m == 0u || m >= 0x7F80u) return 0;
+    const int e = 14 - ((int)(m >> 7) - 127);
+    return e < 100 ? e : 100;
+}
+
+// The head's exponent from its partial maxima, computed by a whole wave
+// (every lane loads one partial); wave-uniform.
+__device__ __forceinline__ int v_scale_exp(const uint32_t* vmax, int head) {
+    uint32_t m = vmax[(int64_t)head * kVmaxParts + (threadIdx.x & 63)];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = (uint32_t)__shfl_xor((int)m, o);
+        m = m > x ? m : x;
+    }
+    return v_exp_from_max(__builtin_amdgcn_readfirstlane(m));
+}
+
 // ---- dense attention ---------------------------------------------------------
-// V of one key range transposed to fp16 [heads][head_dim][n_pad] (pad keys zero).
+// V of one key range transposed to fp16 [heads][head_dim][n_pad] (pad keys
+// zero), each head scaled by its prescale 2^e (from vmax).
 hipError_t launch_vt_dense(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
-                           _Float16* vt, hipStream_t s);
+                           const uint32_t* vmax, _Float16* vt, hipStream_t s);
 
 struct AttnArgs {
     const __bf16* q;
     const __bf16* k;
-    const _Float16* vt;    // [heads][hd][n_pad]
+    const _Float16* vt;    // [heads][hd][n_pad], head h scaled by 2^e(h)
+    const uint32_t* vmax;  // [heads][kVmaxParts] partial maxima of V (the prescale exponents)
     float* o;              // [n_q][heads][hd], used when splits == 1
     float* part_o;         // [splits][heads][n_q_pad][hd], splits > 1
     float* part_ml;        // [splits][heads][n_q_pad][2]
@@ -87,6 +173,22 @@ struct AttnArgs {
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int hd, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, int hd, hipStream_t s);
+
+// RoPE fused into the joint attention: the staging pass also rotates K (all
+// n_kv tokens, those outside every rotated segment copied) into k_out, and
+// the attention kernel rotates each Q row in registers as it loads it,
+// optionally storing the rotated row to q_out.  Token indices are those of
+// the [n][heads][hd] buffers the RoPE descriptor describes.
+struct RopeFused {
+    RopeArgs a;
+    const float2* tab;     // device (cos, sin) table of the descriptor
+    const __bf16* k;       // K before rotation
+    __bf16* k_out;         // rotated K (the attention reads it)
+    __bf16* q_out;         // rotated Q, or null
+};
+hipError_t launch_vt_dense_rope(const __bf16* v, int64_t n_kv, int64_t n_pad, int heads, int hd,
+                                const uint32_t* vmax, _Float16* vt, const RopeFused& r, hipStream_t s);
+hipError_t launch_attn_bf16_rope(const AttnArgs& a, int hd, const RopeFused& r, hipStream_t s);
 
 hipError_t launch_attn_fp32(const float* q, int64_t n_q, const float* k, const float* v,
                             int64_t n_kv, int heads, int hd, float scale, float* o, float* lse,
@@ -152,8 +254,9 @@ struct SparseWs {
     uint32_t* mask;     // [heads][nb][ceil(nb/32)] selected key blocks, bit j of word j/32
     int32_t* count;     // [heads][nb]
     int32_t* base;      // [nb] raster token index of each block's first token
-    _Float16* vt;       // [heads][nb][hd * 64]: each key block's V^T in LDS tile order
+    _Float16* vt;       // [heads][nb][hd * 64]: each key block's V^T (prescaled) in LDS tile order
     __bf16* kimg;       // [heads][nb][64 * hd]: each key block's K rows in LDS tile order
+    uint32_t* vmax;     // [heads][kVmaxParts] partial maxima of V (the prescale exponents)
     // Content-adaptive blocks (null for uniform blocks).  "Blocks" above are
     // then 64-token tiles; a block of 128 or 256 tokens is 2 or 4 consecutive
     // tiles, and base[] is filled by the shape pass.
@@ -169,8 +272,13 @@ hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const 
                                hipStream_t s);
 hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s);
+// wait_limit: bound of each of the kernel's internal waits, in sleeps of
+// about 64 cycles (1 .. kSpinLimit).  A wait that reaches it gives up and the
+// workgroup writes NaN to its o rows and lse entries.
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
-                              float scale_log2, const SparseWs& w, float* o, float* lse, hipStream_t s);
+                              float scale_log2, const SparseWs& w, float* o, float* lse, int wait_limit,
+                              hipStream_t s);
+constexpr int kSpinLimit = 1 << 18;
 
 // Largest number of blocks per head (selection rows staged in LDS).
 constexpr int kSelMax = 4096;

@@ -89,13 +89,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a, const float2* __r
     Chunk<EPC>::load(k + off, xk);
 #pragma unroll
     for (int i = 0; i < EPC / 2; ++i) {
-        const float co = cs[i].x, si = cs[i].y;
-        const float q0 = xq[2 * i], q1 = xq[2 * i + 1];
-        const float k0 = xk[2 * i], k1 = xk[2 * i + 1];
-        xq[2 * i] = q0 * co - q1 * si;
-        xq[2 * i + 1] = q0 * si + q1 * co;
-        xk[2 * i] = k0 * co - k1 * si;
-        xk[2 * i + 1] = k0 * si + k1 * co;
+        rope_pair(xq[2 * i], xq[2 * i + 1], cs[i].x, cs[i].y, xq[2 * i], xq[2 * i + 1]);
+        rope_pair(xk[2 * i], xk[2 * i + 1], cs[i].x, cs[i].y, xk[2 * i], xk[2 * i + 1]);
     }
     Chunk<EPC>::store(q + off, xq);
     Chunk<EPC>::store(k + off, xk);

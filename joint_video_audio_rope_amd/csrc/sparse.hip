@@ -19,7 +19,6 @@
 // Selection runs in fp64 throughout: on smooth-field inputs the probability
 // gaps and running-sum margins at the cut get down to ~1e-8, where fp32 flips
 // rows.
-#include <cstdlib>
 #include <algorithm>
 
 #include "attn_core.hpp"
@@ -99,7 +98,8 @@ __global__ __launch_bounds__(512) void block_pool_kernel(SparseGeom g, const __b
 
 // One workgroup per (block, head): gather the block's 64 rows of K and of V
 // and write each as the exact image of its LDS tile (K rows in the MFMA row
-// order, V transposed to fp16 [d][64], 16-byte chunks swizzled), so that the
+// order, V transposed to fp16 [d][64] with the head's prescale 2^e applied,
+// 16-byte chunks swizzled), so that the
 // attention kernel stages a tile with two contiguous 16 KB copies instead of
 // 64 scattered 256-byte rows.
 template <int HD>
@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
     using L = TileLayout<HD>;
     __shared__ _Float16 tile[kTileN][HD + 2];
     const int j = blockIdx.x, head = blockIdx.y;
+    const float sc = __builtin_ldexpf(1.f, v_scale_exp(w.vmax, head));   // the head's V prescale
     const int64_t base = w.tdim ? (int64_t)w.base[j] : block_token(g, j, 0);
     const uint32_t code = w.tdim ? w.tdim[j] : 0u;
     auto local = [&](int r) { return w.tdim ? tile_local(g, code, r) : block_local(g, r); };
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
         const int64_t tok = base + local(r);
         const bf16x8 x = load_bf16x8(v + tok * rs + head * HD + c * 8, true);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)(float)x[i];
+        for (int i = 0; i < 8; ++i) tile[r][c * 8 + i] = (_Float16)((float)x[i] * sc);
     }
     // K image: LDS chunk index u holds (row, chunk) = k_at(u) of the tile,
     // row counted after the MFMA row permutation of each 32-row half
@@ -453,7 +454,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
 // are written in increasing t: tile t + R is issued only after every consumer
 // released tile t, which follows its publication); released[s] counts
 // consumer waves done with slot s over all its uses.
-constexpr int kSpinLimit = 1 << 18;
 typedef __attribute__((address_space(3))) int lds_int;
 
 __device__ __forceinline__ int lds_load(lds_int* p) {
@@ -473,16 +473,26 @@ __device__ __forceinline__ void publish_after(lds_int* flag, int v) {
     __asm__ volatile("s_waitcnt vmcnt(%2)\n\tds_write_b32 %0, %1" ::"v"(flag), "v"(v), "n"(N) : "memory");
 }
 
-// Wait until *p >= v.  After `limit` sleeps (kSpinLimit unless the host
-// lowers it) the wait gives up and marks the workgroup broken, which ends
-// every later wait at once: a broken protocol costs one bounded wait per
-// workgroup and wrong results, never a hang.
+// Mark the workgroup broken and wait until the flag store has reached LDS
+// (lgkmcnt(0); vmcnt and expcnt keep their no-wait maxima), so that anything
+// this wave writes to LDS afterwards, a tile copy included, lands after it.
+__device__ __forceinline__ void mark_broken(lds_int* broken) {
+    __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __asm__ volatile("" ::: "memory");
+}
+
+// Wait until *p >= v.  After `limit` sleeps the wait gives up and marks the
+// workgroup broken, which ends every later wait at once: a broken protocol
+// costs one bounded wait per workgroup, never a hang, and the workgroup
+// writes NaN instead of its results.
 __device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken, int limit) {
     for (int i = 0;; ++i) {
         if (__builtin_amdgcn_readfirstlane(lds_load(p)) >= v) break;
         if (__builtin_amdgcn_readfirstlane(lds_load(broken)) != 0) break;
         if (i >= limit) {
-            __hip_atomic_store(broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            mark_broken(broken);
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -555,7 +565,7 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
             if (__builtin_amdgcn_readfirstlane(lds_load(ready_at(t & (R - 1)))) >= t + 1) break;
             if (__builtin_amdgcn_readfirstlane(lds_load((lds_int*)&broken)) != 0) break;
             if (i >= spin_limit) {
-                __hip_atomic_store((lds_int*)&broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                mark_broken((lds_int*)&broken);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -640,12 +650,20 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
     }
 
     if (b0 + side >= g.nb) return;
+    // A wave that gave up on a wait, or whose tiles a producer that gave up
+    // may have overwritten, finds the flag set here (the flag store completes
+    // before any later copy of that producer lands): its rows become NaN.
+    const bool bad = __builtin_amdgcn_readfirstlane(lds_load(brk)) != 0;
     const float l_tot = st.l_run[0] + __shfl_xor(st.l_run[0], 32);
-    store_o<HD>(o + qtok * rstride + head * HD, st.o[0], 1.f / l_tot);
+    // O^T accumulated V scaled by 2^ve: scale back (exact)
+    const int ve = v_scale_exp(w.vmax, head);
+    store_o<HD>(o + qtok * rstride + head * HD, st.o[0],
+                bad ? __builtin_nanf("") : __builtin_ldexpf(1.f / l_tot, -ve));
     // log-sum-exp over the selected keys, natural log (reference maximum and
     // running sum are in the exp2 domain)
     if (lse && hh == 0)
-        lse[(int64_t)head * ((int64_t)g.T * g.H * g.W) + qtok] = (st.m_run[0] + log2f(l_tot)) * kLn2;
+        lse[(int64_t)head * ((int64_t)g.T * g.H * g.W) + qtok] =
+            bad ? __builtin_nanf("") : (st.m_run[0] + log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -697,25 +715,14 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
     return hipGetLastError();
 }
 
-// Bound of every wait in the stream kernel, in sleeps of about 64 cycles.
-// MMDIT_SPARSE_SPIN_LIMIT (a non-negative integer) lowers it: tests set 0 to
-// force the give-up path from the host and check that the kernel still ends.
-static int stream_spin_limit() {
-    const char* e = std::getenv("MMDIT_SPARSE_SPIN_LIMIT");
-    if (!e || !*e) return kSpinLimit;
-    char* end = nullptr;
-    const long v = std::strtol(e, &end, 10);
-    if (*end != '\0' || v < 0) return kSpinLimit;
-    return (int)std::min<long>(v, kSpinLimit);
-}
-
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
-                              float scale_log2, const SparseWs& w, float* o, float* lse, hipStream_t s) {
+                              float scale_log2, const SparseWs& w, float* o, float* lse, int wait_limit,
+                              hipStream_t s) {
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
     const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
     hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g,
-                       q, k, scale_log2, w, o, lse, stream_spin_limit());
+                       q, k, scale_log2, w, o, lse, wait_limit);
     return hipGetLastError();
 }
 

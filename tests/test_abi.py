@@ -32,7 +32,7 @@ def test_header_declares_the_calls():
               "mmdit_block_sparse_attn_bwd", "mmdit_block_sparse_attn_adaptive", "mmdit_token_norms",
               "mmdit_block_sparse_attn_adaptive_bwd", "mmdit_adaptive_tile_table",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
-              "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table"):
+              "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table", "mmdit_joint_attn_rope"):
         assert n in names
 
 
@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_empty_error():
-    assert J.mmdit_abi_version() == 3
+    assert J.mmdit_abi_version() == 4
     assert isinstance(J.mmdit_last_error(), str)
 
 
@@ -55,7 +55,8 @@ def test_struct_layout_matches_header():
     # the binding's ctypes structs follow the C layout on x86-64
     assert ctypes.sizeof(L.Segment) == 48
     assert L.Segment.t_scale.offset == 40
-    assert ctypes.sizeof(L.SparseDesc) == 40
+    assert ctypes.sizeof(L.SparseDesc) == 48
+    assert L.SparseDesc.top_p.offset == 32 and L.SparseDesc.wait_limit.offset == 40
     assert L.RopeDesc.segs.offset == 32 and L.RopeDesc.n_tokens.offset == 48
 
 
@@ -88,7 +89,8 @@ def test_workspace_plans():
     ws = J.mmdit_workspace_bytes
     # bf16 joint attention: V^T in fp16, key count padded to 64
     n = 35050
-    assert ws(J.MMDIT_OP_JOINT_ATTN, n, n, 24, 128, J.MMDIT_BF16) == 24 * 128 * 35072 * 2
+    # (plus the per-head partial maxima of V for its prescale: 24 x 64 uint32)
+    assert ws(J.MMDIT_OP_JOINT_ATTN, n, n, 24, 128, J.MMDIT_BF16) == 24 * 128 * 35072 * 2 + 24 * 64 * 4
     assert ws(J.MMDIT_OP_JOINT_ATTN, 88, 88, 2, 64, J.MMDIT_FP32) == 0
     # audio queries against video keys split the keys and add partials
     big = ws(J.MMDIT_OP_AV_CROSS_ATTN, 34320, 218, 24, 128, J.MMDIT_BF16)
@@ -117,6 +119,8 @@ def _call_joint(**over):
     (dict(q=8), L.MMDIT_ERR_INVALID_ARG),                     # misaligned
     (dict(o=16), L.MMDIT_ERR_INVALID_ARG),                    # output aliases q
     (dict(scale=math.inf), L.MMDIT_ERR_INVALID_ARG),
+    (dict(scale=-0.125), L.MMDIT_ERR_INVALID_ARG),
+    (dict(scale=math.nan), L.MMDIT_ERR_INVALID_ARG),
     (dict(ws=0), L.MMDIT_ERR_WORKSPACE),
     (dict(ws_bytes=100), L.MMDIT_ERR_WORKSPACE),
 ])
@@ -199,12 +203,14 @@ def test_rope_rejects_bad_descriptors():
     (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
     (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
     (dict(ws_bytes=10), L.MMDIT_ERR_WORKSPACE),
+    (dict(wait_limit=-1), L.MMDIT_ERR_INVALID_ARG),
+    (dict(wait_limit=(1 << 18) + 1), L.MMDIT_ERR_INVALID_ARG),
 ])
 def test_block_sparse_rejects_bad_arguments(over, status):
     a = dict(T=24, H=64, W=112, heads=24, hd=128, zone=(8, 8, 8), block=(4, 4, 4), top_k=32,
-             top_p=0.9, ws_bytes=1 << 40)
+             top_p=0.9, ws_bytes=1 << 40, wait_limit=0)
     a.update(over)
-    sd = J.sparse_desc(a["zone"], a["block"], a["top_k"], a["top_p"])
+    sd = J.sparse_desc(a["zone"], a["block"], a["top_k"], a["top_p"], a["wait_limit"])
     lib = J.lib()
     st = lib.mmdit_block_sparse_attn(1 << 20, 1 << 30, 1 << 31, a["T"], a["H"], a["W"], a["heads"],
                                      a["hd"], ctypes.byref(sd), 0.088, 1 << 36, None, None,
@@ -299,7 +305,7 @@ def _adaptive_call(**over):
     (dict(T=48), L.MMDIT_ERR_UNSUPPORTED),                  # 672 zones, 5376 tiles
     (dict(top_k=-1), L.MMDIT_ERR_INVALID_ARG),
     (dict(top_p=1.5), L.MMDIT_ERR_INVALID_ARG),
-    (dict(scale=0.0), L.MMDIT_ERR_INVALID_ARG),
+    (dict(scale=-0.5), L.MMDIT_ERR_INVALID_ARG),
     (dict(a=(4 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),       # misaligned norms
     (dict(lse=(9 << 32) + 2), L.MMDIT_ERR_INVALID_ARG),
     (dict(tblock=(5 << 32) + 1024), L.MMDIT_ERR_INVALID_ARG),   # tile_block inside o
@@ -415,3 +421,27 @@ def test_adaptive_tile_table_rejects_bad_input():
         J.mmdit_adaptive_tile_table(8, 8, 12, [3])
     with pytest.raises(L.MmditError, match="shape code"):
         J.mmdit_adaptive_tile_table(8, 8, 16, [3, 16])
+
+
+def test_fused_rope_attention_checks():
+    """mmdit_joint_attn_rope validates on the host before enqueueing anything."""
+    w = WORKLOADS["block"]
+    spec = J.rope_spec_for(w)
+    lib = J.lib()
+    n, h, d = 5850, 24, 128
+    tb = n * h * d * 2
+    need = J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN_ROPE, n, n, h, d, J.MMDIT_BF16)
+    assert need == J.mmdit_workspace_bytes(J.MMDIT_OP_JOINT_ATTN, n, n, h, d, J.MMDIT_BF16) + \
+        (tb + 255) // 256 * 256
+
+    def call(q=1 << 32, k=2 << 32, v=3 << 32, o=4 << 32, qr=5 << 32, kr=6 << 32, dtype=J.MMDIT_BF16, tab=7 << 32,
+             ws=8 << 32, wsb=need):
+        return lib.mmdit_joint_attn_rope(ctypes.byref(spec.desc), tab, q, k, v, dtype, 0.0, o, qr, kr, ws, wsb, None)
+    assert call(dtype=J.MMDIT_FP32) == L.MMDIT_ERR_UNSUPPORTED
+    assert call(qr=1 << 32) == L.MMDIT_ERR_INVALID_ARG                    # q_rot = q (in place) is refused
+    assert call(kr=(5 << 32) + 4096) == L.MMDIT_ERR_INVALID_ARG           # k_rot overlaps q_rot
+    assert call(qr=(4 << 32) + tb) == L.MMDIT_ERR_INVALID_ARG             # q_rot inside o
+    assert call(kr=(6 << 32) + 8) == L.MMDIT_ERR_INVALID_ARG              # misaligned
+    assert call(tab=0) == L.MMDIT_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == L.MMDIT_ERR_WORKSPACE
+    assert call(ws=(5 << 32) - 4096) == L.MMDIT_ERR_INVALID_ARG           # workspace runs into q_rot

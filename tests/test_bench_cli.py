@@ -27,6 +27,8 @@ def test_traffic_from_counters_scaling():
     # the 1 GiB copy reads as 512 MiB through FETCH_SIZE (scale 2) and 1 GiB through WRITE_SIZE (scale 1)
     means = {("__amd_rocclr_copyBuffer", "FETCH_SIZE"): 524288.0,
              ("__amd_rocclr_copyBuffer", "WRITE_SIZE"): 1048576.0,
+             ("v_absmax_kernel<128>", "FETCH_SIZE"): 50.0,
+             ("v_absmax_kernel<128>", "WRITE_SIZE"): 1.0,
              ("vt_dense_kernel<128>", "FETCH_SIZE"): 100.0,
              ("vt_dense_kernel<128>", "WRITE_SIZE"): 200.0,
              ("mmdit::attn_bf16_kernel<128, 1, 8>", "FETCH_SIZE"): 1000.0,
@@ -35,7 +37,8 @@ def test_traffic_from_counters_scaling():
     assert t["fetch_scale"] == 2.0 and t["write_scale"] == 1.0
     assert t["kernels"]["vt_dense_kernel"] == {"fetch_bytes": 200 * 1024, "write_bytes": 200 * 1024}
     assert t["kernels"]["attn_bf16_kernel"] == {"fetch_bytes": 2000 * 1024, "write_bytes": 300 * 1024}
-    assert t["bytes_per_launch"] == (200 + 200 + 2000 + 300) * 1024
+    assert t["kernels"]["v_absmax_kernel"] == {"fetch_bytes": 100 * 1024, "write_bytes": 1 * 1024}
+    assert t["bytes_per_launch"] == (100 + 1 + 200 + 200 + 2000 + 300) * 1024
     assert t["source_sha256"] == bench.kernel_source_hash()
     del means[("vt_dense_kernel<128>", "WRITE_SIZE")]
     with pytest.raises(SystemExit):
