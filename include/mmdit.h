@@ -196,6 +196,28 @@ mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const v
                               float softmax_scale, float* o, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Bytes of the per-GPU scratch array of mmdit_joint_attn_noalloc (64 MiB). */
+#define MMDIT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* mmdit_joint_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and output, bit for bit, with the workspace taken from
+ * a fixed scratch array of MMDIT_NOALLOC_SCRATCH_BYTES that the library's
+ * code object holds on each GPU it runs on until the process ends.  The call
+ * allocates and frees nothing.  Sizes whose workspace
+ * (mmdit_workspace_bytes(MMDIT_OP_JOINT_ATTN, ...)) exceeds the scratch are
+ * rejected with MMDIT_ERR_WORKSPACE before anything is enqueued: with 24 heads
+ * of 128 that is up to about 10900 keys (the 5850-token joint block, the
+ * video->text and video->audio shapes).  The first call on a device looks up
+ * the array's address there (the calling thread's current device, which must
+ * own `stream`).  Every call on a GPU shares its one array, and nothing in it
+ * needs to start cleared: calls that overlap on one GPU (concurrent streams,
+ * threads) race and give wrong results; serialise them.  Arguments as for
+ * mmdit_joint_attn. */
+mmdit_status mmdit_joint_attn_noalloc(const void* q, int64_t n_q, const void* k, const void* v,
+                                      int64_t n_kv, int32_t heads, int32_t head_dim, int32_t dtype,
+                                      float softmax_scale, float* o, void* stream);
+
 /* The joint self-attention of one dual-stream block with its RoPE fused in:
  * o = mmdit_joint_attn(R(q), R(k), v) where R is mmdit_rope3d's rotation for
  * `desc` (n_q = n_kv = desc->n_tokens, heads and head_dim from desc), and the

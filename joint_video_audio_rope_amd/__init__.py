@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     mmdit_block_sparse_attn_adaptive_bwd,
     mmdit_block_sparse_attn_bwd,
     mmdit_block_sparse_attn_fwd, mmdit_joint_attn, mmdit_joint_attn_bwd, mmdit_joint_attn_fwd, mmdit_last_error,
-    mmdit_joint_attn_rope, MMDIT_OP_JOINT_ATTN_ROPE,
+    mmdit_joint_attn_noalloc, MMDIT_NOALLOC_SCRATCH_BYTES, mmdit_joint_attn_rope, MMDIT_OP_JOINT_ATTN_ROPE,
     mmdit_rope3d, mmdit_rope3d_build_table, mmdit_rope3d_table_floats, mmdit_token_norms, mmdit_workspace_bytes,
     sparse_desc, ADAPTIVE_SHAPES,
     MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmmdit.so")
 
 MMDIT_OK, MMDIT_ERR_INVALID_ARG, MMDIT_ERR_UNSUPPORTED, MMDIT_ERR_WORKSPACE, MMDIT_ERR_HIP = range(5)
+MMDIT_NOALLOC_SCRATCH_BYTES = 64 << 20
 MMDIT_FP32, MMDIT_BF16 = 0, 1
 MMDIT_SEG_VIDEO, MMDIT_SEG_AUDIO, MMDIT_SEG_TEXT = 0, 1, 2
 (MMDIT_OP_JOINT_ATTN, MMDIT_OP_AV_CROSS_ATTN, MMDIT_OP_BLOCK_SPARSE_ATTN, MMDIT_OP_JOINT_ATTN_BWD,
@@ -87,6 +88,8 @@ def lib():
         L.mmdit_joint_attn_rope.restype = i32
         L.mmdit_joint_attn_rope.argtypes = [ctypes.POINTER(RopeDesc), vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz,
                                             vp]
+        L.mmdit_joint_attn_noalloc.restype = i32
+        L.mmdit_joint_attn_noalloc.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp]
         L.mmdit_joint_attn_fwd.restype = i32
         L.mmdit_joint_attn_fwd.argtypes = [vp, i64, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]
         L.mmdit_joint_attn_bwd.restype = i32
@@ -294,6 +297,22 @@ def mmdit_joint_attn_rope(spec, q, k, v, softmax_scale=None, o=None, q_rot=None,
                                            _scale(softmax_scale), _ptr(o), _ptr(q_rot), _ptr(k_rot), _ptr(ws), wsb,
                                            _stream(stream)))
     return o, q_rot, k_rot
+
+
+def mmdit_joint_attn_noalloc(q, k, v, softmax_scale=None, o=None, stream=None):
+    """mmdit_joint_attn with the library's fixed per-GPU scratch instead of a
+    workspace (for callers that cannot allocate; pass o to allocate nothing
+    here either).  Calls that overlap on one GPU race."""
+    n_q, h, d = q.shape
+    n_kv = k.shape[0]
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+    assert k.shape == v.shape == (n_kv, h, d) and q.dtype == k.dtype == v.dtype
+    with _on(stream):
+        if o is None:
+            o = torch.empty((n_q, h, d), dtype=torch.float32, device=q.device)
+        _check(lib().mmdit_joint_attn_noalloc(_ptr(q), n_q, _ptr(k), _ptr(v), n_kv, h, d, _dtype(q),
+                                              _scale(softmax_scale), _ptr(o), _stream(stream)))
+    return o
 
 
 def mmdit_joint_attn_fwd(q, k, v, softmax_scale=None, o=None, lse=None, ws=None, stream=None):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -594,6 +595,37 @@ mmdit_status run_sparse_bwd(const SparsePlan& p, const SparseBwdPlan& bp, const 
     return MMDIT_OK;
 }
 
+// ---- scratch of the allocation-free joint attention -------------------------------
+// One array per GPU, in the library's code object: it exists on every device
+// the library has launched a kernel on, until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory; the device
+// address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) and kept.
+static __device__ __align__(256) char scratch[MMDIT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The calling thread's current device's address of `scratch`.
+mmdit_status scratch_address(void** out, const char* who) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MMDIT_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", who, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, who);
+        if (!p) return fail(MMDIT_ERR_HIP, "%s: no device address for the scratch array", who);
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MMDIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -703,6 +735,25 @@ mmdit_status mmdit_joint_attn(const void* q, int64_t n_q, const void* k, const v
     softmax_scale = resolve_scale(softmax_scale, head_dim);
     return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, nullptr, (char*)ws, p,
                     (hipStream_t)stream, "joint_attn");
+}
+
+mmdit_status mmdit_joint_attn_noalloc(const void* q, int64_t n_q, const void* k, const void* v, int64_t n_kv,
+                                      int32_t heads, int32_t head_dim, int32_t dtype, float softmax_scale, float* o,
+                                      void* stream) {
+    const char* who = "joint_attn_noalloc";
+    mmdit_status st = check_attn_args(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, who);
+    if (st != MMDIT_OK) return st;
+    const AttnPlan p = plan_attn(n_q, n_kv, heads, head_dim, dtype);
+    if (p.total() > (size_t)MMDIT_NOALLOC_SCRATCH_BYTES)
+        return fail(MMDIT_ERR_WORKSPACE,
+                    "%s: these sizes need %zu bytes of scratch, more than its fixed %zu (use mmdit_joint_attn "
+                    "with a workspace)", who, p.total(), (size_t)MMDIT_NOALLOC_SCRATCH_BYTES);
+    if (n_q == 0) return MMDIT_OK;
+    void* ws = nullptr;
+    if (p.total() > 0 && (st = scratch_address(&ws, who)) != MMDIT_OK) return st;
+    softmax_scale = resolve_scale(softmax_scale, head_dim);
+    return run_attn(q, n_q, k, v, n_kv, heads, head_dim, dtype, softmax_scale, o, nullptr, (char*)ws, p,
+                    (hipStream_t)stream, who);
 }
 
 mmdit_status mmdit_joint_attn_rope(const mmdit_rope_desc* desc, const float* dev_table, const void* q,

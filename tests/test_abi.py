@@ -32,7 +32,7 @@ def test_header_declares_the_calls():
               "mmdit_block_sparse_attn_bwd", "mmdit_block_sparse_attn_adaptive", "mmdit_token_norms",
               "mmdit_block_sparse_attn_adaptive_bwd", "mmdit_adaptive_tile_table",
               "mmdit_workspace_bytes", "mmdit_last_error", "mmdit_abi_version",
-              "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table", "mmdit_joint_attn_rope"):
+              "mmdit_rope3d_table_floats", "mmdit_rope3d_build_table", "mmdit_joint_attn_noalloc"):
         assert n in names
 
 
@@ -421,6 +421,20 @@ def test_adaptive_tile_table_rejects_bad_input():
         J.mmdit_adaptive_tile_table(8, 8, 12, [3])
     with pytest.raises(L.MmditError, match="shape code"):
         J.mmdit_adaptive_tile_table(8, 8, 16, [3, 16])
+
+
+def test_noalloc_checks_run_before_any_device_call():
+    """The allocation-free joint attention validates its arguments and the
+    scratch size on the host first: these fail without touching a GPU."""
+    lib = J.lib()
+    call = lambda n_q, n_kv, heads, hd, q=1 << 30, o=1 << 34: lib.mmdit_joint_attn_noalloc(
+        q, n_q, 2 << 30, 3 << 30, n_kv, heads, hd, J.MMDIT_BF16, 0.0, o, None)
+    assert call(8, 11000, 24, 128) == L.MMDIT_ERR_WORKSPACE
+    assert "scratch" in J.mmdit_last_error() and str(64 << 20) in J.mmdit_last_error()
+    assert call(8, 1000, 24, 96) == L.MMDIT_ERR_UNSUPPORTED
+    assert call(8, 1000, 24, 128, q=(1 << 30) + 8) == L.MMDIT_ERR_INVALID_ARG
+    assert call(8, 1000, 24, 128, o=(1 << 30) + 256) == L.MMDIT_ERR_INVALID_ARG     # o aliases q
+    assert J.MMDIT_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_fused_rope_attention_checks():
