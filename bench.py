@@ -245,6 +245,12 @@ def kernel_table(paths):
 
     def short(name):
         name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        if name.startswith("_ZN5mmdit12_GLOBAL__N_1"):     # mangled: keep the kernel's own name
+            rest = name[len("_ZN5mmdit12_GLOBAL__N_1"):]
+            i = 0
+            while rest[i].isdigit():
+                i += 1
+            name = "mmdit::" + rest[i:i + int(rest[:i])]
         return name.split("(")[0][:60]
 
     dur = collections.defaultdict(list)
@@ -261,19 +267,18 @@ def kernel_table(paths):
     def mean(x):
         return sum(x) / len(x) if x else None
 
-    copy = [k for k in ctr if "copyBuffer" in k[0]]
-    f_scale = w_scale = None
-    if copy:
-        c = ctr[copy[0]]
-        if c.get("FETCH_SIZE"):
-            f_scale = COPY_BYTES / (mean(c["FETCH_SIZE"]) * 1024.0)
-        if c.get("WRITE_SIZE"):
-            w_scale = COPY_BYTES / (mean(c["WRITE_SIZE"]) * 1024.0)
+    # the 1 GiB copy is the largest copy the probe makes: its dispatch reads
+    # the largest FETCH_SIZE and WRITE_SIZE of all copyBuffer dispatches
+    def copy_max(counter):
+        v = [x for k, c in ctr.items() if "copyBuffer" in k[0] for x in c.get(counter, [])]
+        return max(v) if v else None
+    f_scale = COPY_BYTES / (copy_max("FETCH_SIZE") * 1024.0) if copy_max("FETCH_SIZE") else None
+    w_scale = COPY_BYTES / (copy_max("WRITE_SIZE") * 1024.0) if copy_max("WRITE_SIZE") else None
     print("Copy calibration (1 GiB copy): fetch x %s, write x %s\n" % (
         "%.4f" % f_scale if f_scale else "-", "%.4f" % w_scale if w_scale else "-"))
     print("| kernel | grid (threads) | calls | avg ms | fetch GB | write GB | GB/s | % of 8 TB/s | MfmaUtil % |")
     print("|---|---|---|---|---|---|---|---|---|")
-    keys = sorted(set(dur) | set(ctr), key=lambda k: -(sum(dur.get(k, [0])) or 0))
+    keys = sorted((k for k in set(dur) | set(ctr) if "mmdit" in k[0]), key=lambda k: -(sum(dur.get(k, [0])) or 0))
     for k in keys:
         d = mean(dur.get(k, []))
         c = ctr.get(k, {})
@@ -612,17 +617,21 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "pv_dtype": "fp16 (P in (0, 256]; V prescaled per head by a power of two, exact)",
         "data": "synthetic (seeded N(0,1) Q/K/V, bf16, resident in HBM)",
         "config": {"workload": "480p-latent layer: video 21x30x52 + 1 cond frame (t=-1), 218 audio, "
                                "512 text; 35050 tokens, 24 heads x 128; step = video->text + RoPE + "
                                "joint self-attn + audio<->video cross-attn",
-                   "tokens": n, "heads": h, "head_dim": d, "step_flop": fl_step},
+                   "tokens": n, "heads": h, "head_dim": d, "step_flop": fl_step,
+                   "value_is": "TFLOP/s of the whole step: 4*Nq*Nk*d*h summed over its four attention calls, "
+                               "over the step time; the joint self-attention call alone (the metric's "
+                               "kernel) is roofline.achieved / joint_attn.tflops"},
         "joint_attn": {"ms": round(joint_ms, 4), "tflops": round(joint_tflops, 2),
                        "pct_bf16_peak": round(100.0 * joint_tflops / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(joint_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(joint_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "joint attention call (V^T staging + attn_bf16_kernel<128>), "
+                     "kernel": "joint attention call (V prescale + V^T staging + attn_bf16_kernel<128>), "
                                "4*N^2*d*h = %.4g FLOP per call" % fl_joint},
     }
 

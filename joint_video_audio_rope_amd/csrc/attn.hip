@@ -161,21 +161,6 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
             const int64_t qrow = qrow0 + 32 * qb;
             qf[qb][ks] = load_bf16x8(a.q + qrow * rstride + head * HD + 16 * ks + 8 * hh, qrow < a.n_q);
         }
-    if constexpr (ROPE) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int64_t qrow = qrow0 + 32 * qb;
-            if (qrow >= a.n_q) continue;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int dim = 16 * ks + 8 * hh;
-                qf[qb][ks] = rope_chunk_bf16(qf[qb][ks], r->tab, rope_table_index(r->a, qrow, dim));
-                if (r->q_out && split == 0)
-                    *reinterpret_cast<bf16x8*>(r->q_out + qrow * rstride + head * HD + dim) = qf[qb][ks];
-            }
-        }
-    }
-
     // Each lane's share of the tile copies, fixed for the whole key walk: the
     // byte offset (from the tile's first key row) of the 16-byte chunk that
     // belongs at its LDS position.
@@ -244,6 +229,24 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
     issue_k(tile0, kbuf(0));
     issue_v(tile0, vbuf(0));
     if (tile0 + 1 < tile1) issue_k(tile0 + 1, kbuf(1));
+    // RoPE-fused calls rotate the Q fragments here, while the first tiles'
+    // copies are in flight (their table reads and the rotated rows' stores
+    // overlap the copies).
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int64_t qrow = qrow0 + 32 * qb;
+            if (qrow >= a.n_q) continue;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int dim = 16 * ks + 8 * hh;
+                qf[qb][ks] = rope_chunk_bf16(qf[qb][ks], r->tab, rope_table_index(r->a, qrow, dim));
+                if (r->q_out && split == 0)
+                    *reinterpret_cast<bf16x8*>(r->q_out + qrow * rstride + head * HD + dim) = qf[qb][ks];
+            }
+        }
+    }
+
     wait_dma();
     __syncthreads();
     f32x16 sa[QB][2], sb[QB][2];
