@@ -302,7 +302,8 @@ mmdit_status mmdit_av_cross_attn(const void* q_v, const void* k_v, const void* v
  * sel_mask [heads][nb][ceil(nb/32)] uint32: bit j%32 of word j/32 set iff key
  * block j is selected; sel_count [heads][nb] int32 = number of selected blocks.
  * Either may be NULL if not wanted.  T, H, W must be multiples of the zone,
- * the zone of the block; block volume 64; head_dim 128.
+ * the zone of the block; block volume 64; head_dim 128; at most 32768 blocks
+ * per head (MMDIT_ERR_UNSUPPORTED beyond).
  * The attention kernel's internal waits are bounded (sp->wait_limit): a wait
  * that times out never hangs the call; the rows of the query blocks its
  * workgroup serves come out as NaN, never as plausible wrong values.  The same

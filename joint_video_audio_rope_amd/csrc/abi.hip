@@ -298,8 +298,18 @@ mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
 // ---- block sparse plan ------------------------------------------------------------
 struct SparsePlan {
     SparseGeom g{};
+    int32_t chunk_rows;   // query blocks whose logits are computed and selected at once
     size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, off_vmax, total;
 };
+
+// Query blocks per chunk of block logits: whole 128-row tiles of the score
+// GEMM within kScoreChunkBytes for all heads, or every block when they fit.
+int32_t score_chunk_rows(int64_t nb, int32_t heads) {
+    int64_t c = (int64_t)kScoreChunkBytes / ((int64_t)heads * nb * 8);
+    c = c / 128 * 128;
+    if (c < 128) c = 128;
+    return (int32_t)(c < nb ? c : nb);
+}
 
 // Workspace layout of a block-sparse call (shared by the plan and the size
 // query): fp64 block means, fp64 scores, selection bitmask and counts, block
@@ -314,7 +324,8 @@ void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
     };
     p->off_qbar = take((size_t)heads * nb * hd * 8);
     p->off_kbar = take((size_t)heads * nb * hd * 8);
-    p->off_scores = take((size_t)heads * nb * nb * 8);
+    p->chunk_rows = score_chunk_rows(nb, heads);
+    p->off_scores = take((size_t)heads * p->chunk_rows * nb * 8);
     p->off_mask = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
     p->off_count = take((size_t)heads * nb * 4);
     p->off_base = take((size_t)nb * 4);
@@ -347,7 +358,8 @@ mmdit_status plan_sparse(int T, int H, int W, int heads, int hd, const mmdit_spa
     if (n * heads >= ((int64_t)1 << 31))
         return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: tokens * heads must stay below 2^31");
     const int64_t nb = n / kTileN;
-    if (nb > 4096) return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: %lld blocks (max 4096)", (long long)nb);
+    if (nb > kSelMax)
+        return fail(MMDIT_ERR_UNSUPPORTED, "block_sparse: %lld blocks per head (max %d)", (long long)nb, kSelMax);
     SparseGeom& g = p->g;
     g.T = T, g.H = H, g.W = W;
     g.ZT = sp->zone[0], g.ZH = sp->zone[1], g.ZW = sp->zone[2];
@@ -490,10 +502,14 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
         return hip_fail(e, "block_sparse v prescale");
     if ((e = launch_vt_blocks(p.g, (const __bf16*)k, (const __bf16*)v, head_dim, sw, s)) != hipSuccess)
         return hip_fail(e, "block_sparse vt");
-    if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse scores");
-    if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, sel_mask, sel_count, s)) != hipSuccess)
-        return hip_fail(e, "block_sparse select");
+    for (int r0 = 0; r0 < p.g.nb; r0 += p.chunk_rows) {
+        const int rows = std::min(p.chunk_rows, p.g.nb - r0);
+        if ((e = launch_block_scores(p.g, head_dim, softmax_scale, sw, r0, rows, s)) != hipSuccess)
+            return hip_fail(e, "block_sparse scores");
+        if ((e = launch_block_select(p.g, sp->top_k, sp->top_p, sw, r0, rows, sel_mask, sel_count, s)) !=
+            hipSuccess)
+            return hip_fail(e, "block_sparse select");
+    }
     if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
                                 (float)(softmax_scale * 1.4426950408889634), sw, o, lse,
                                 sp->wait_limit ? sp->wait_limit : kSpinLimit, s)) != hipSuccess)

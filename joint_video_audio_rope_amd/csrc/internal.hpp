@@ -250,7 +250,7 @@ struct SparseGeom {
 struct SparseWs {
     double* qbar;       // [heads][nb][hd]
     double* kbar;       // [heads][nb][hd]
-    double* scores;     // [heads][nb][nb] (logits, scaled)
+    double* scores;     // [heads][chunk rows][nb] (logits, scaled) of the chunk of query blocks being selected
     uint32_t* mask;     // [heads][nb][ceil(nb/32)] selected key blocks, bit j of word j/32
     int32_t* count;     // [heads][nb]
     int32_t* base;      // [nb] raster token index of each block's first token
@@ -268,9 +268,12 @@ hipError_t launch_block_pool(const SparseGeom& g, const __bf16* q, const __bf16*
                              const SparseWs& w, hipStream_t s);
 hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* k, const __bf16* v, int hd, const SparseWs& w,
                             hipStream_t s);
-hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w,
+// The block logits and the selection run in chunks of query blocks: the
+// scores of query blocks row0 .. row0 + rows - 1 (all heads) are computed
+// into w.scores ([heads][rows][nb]) and selected from there.
+hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w, int row0, int rows,
                                hipStream_t s);
-hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
+hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w, int row0, int rows,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s);
 // wait_limit: bound of each of the kernel's internal waits, in sleeps of
 // about 64 cycles (1 .. kSpinLimit).  A wait that reaches it gives up and the
@@ -280,8 +283,13 @@ hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16
                               hipStream_t s);
 constexpr int kSpinLimit = 1 << 18;
 
-// Largest number of blocks per head (selection rows staged in LDS).
-constexpr int kSelMax = 4096;
+// Largest number of blocks (64-token tiles) per head: selection rows of up to
+// 4096 blocks are held by one wave, longer ones by 2, 4 or 8 waves; the
+// attention kernels stage their blocks' selection rows in LDS.
+constexpr int kSelMax = 32768;
+// Bytes of block logits computed and selected at once (the chunk of query
+// blocks is sized to stay within it).
+constexpr size_t kScoreChunkBytes = size_t(1) << 30;
 
 // ---- content-adaptive block shapes ----------------------------------------------
 constexpr int kZoneEdge = 8;       // macro-zone edge in tokens along t, h and w

@@ -144,15 +144,18 @@ __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf
     }
 }
 
-// fp64 GEMM: scores[h][i][j] = scale * <qbar[h][i], kbar[h][j]>.
-// 256 threads compute a 128x128 tile, 8x8 per thread; d staged 16 at a time.
+// fp64 GEMM for one chunk of query blocks: scores[h][i - row0][j] = scale *
+// <qbar[h][i], kbar[h][j]> for i in [row0, row0 + rows).  256 threads compute
+// a 128x128 tile, 8x8 per thread; d staged 16 at a time.
 constexpr int kSB = 128, kSK = 16;
 template <int HD>
-__global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double scale, SparseWs w) {
+__global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double scale, SparseWs w, int row0,
+                                                           int rows) {
     __shared__ double As[kSK][kSB + 1];
     __shared__ double Bs[kSK][kSB + 1];
     const int head = blockIdx.z;
-    const int i0 = blockIdx.y * kSB, j0 = blockIdx.x * kSB;
+    const int i0 = row0 + blockIdx.y * kSB, j0 = blockIdx.x * kSB;
+    const int i_end = row0 + rows;
     const int nb = g.nb;
     const double* A = w.qbar + (int64_t)head * nb * HD;
     const double* B = w.kbar + (int64_t)head * nb * HD;
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
     for (int d0 = 0; d0 < HD; d0 += kSK) {
         for (int u = threadIdx.x; u < kSB * kSK; u += 256) {
             const int r = u / kSK, c = u % kSK;
-            As[c][r] = (i0 + r < nb) ? A[(int64_t)(i0 + r) * HD + d0 + c] : 0.0;
+            As[c][r] = (i0 + r < i_end) ? A[(int64_t)(i0 + r) * HD + d0 + c] : 0.0;
             Bs[c][r] = (j0 + r < nb) ? B[(int64_t)(j0 + r) * HD + d0 + c] : 0.0;
         }
         __syncthreads();
@@ -183,20 +186,20 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
         }
         __syncthreads();
     }
-    double* S = w.scores + (int64_t)head * nb * nb;
+    double* S = w.scores + (int64_t)head * rows * nb;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
         const int i = i0 + ty + 16 * a;
-        if (i >= nb) continue;
+        if (i >= i_end) continue;
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             const int j = j0 + tx + 16 * b;
-            if (j < nb) S[(int64_t)i * nb + j] = acc[a][b] * scale;
+            if (j < nb) S[(int64_t)(i - row0) * nb + j] = acc[a][b] * scale;
         }
     }
 }
 
-constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup
+constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup of one-wave rows
 // Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
 // Measured on the 24 x 64 x 112 grid (density 27.6 %): a group stages on
 // average 0.73 (pairs), 0.62 (triples), 0.50 (4 blocks) of the tiles its
@@ -223,27 +226,97 @@ __device__ __forceinline__ double wave_max(double x) {
 __device__ __forceinline__ double key_value(uint64_t key) { return __longlong_as_double((long long)key); }
 __device__ __forceinline__ uint64_t value_key(double x) { return (uint64_t)__double_as_longlong(x); }
 
-// Selection of one row of block probabilities, one wave per row.  Lane l
-// holds blocks j = l + 64 r.  The blocks in descending order of probability
-// (equal probabilities by ascending id) are never sorted: for a non-negative
-// double the bit pattern read as an unsigned integer orders like the value,
-// so the row is searched by bisection over that integer range.
+// Reductions over the W waves that share one selection row (W == 1: the
+// wave alone).  Each wave reduces its lanes, writes its partial to LDS, and
+// after a barrier every wave adds the W partials in wave order, so all waves
+// hold the same bits and take the same decisions (every barrier is reached by
+// all of them).  Slots alternate so one barrier per reduction suffices.
+template <int W>
+struct RowReduce {
+    double* d;    // [2][W]
+    int* c;       // [2][W]
+    int flip = 0;
+    __device__ double sum(double x) {
+        x = wave_sum(x);
+        if constexpr (W == 1) {
+            return x;
+        } else {
+            if ((threadIdx.x & 63) == 0) d[flip * W + wave_id()] = x;
+            __syncthreads();
+            double t = 0.0;
+#pragma unroll
+            for (int k = 0; k < W; ++k) t += d[flip * W + k];
+            flip ^= 1;
+            return t;
+        }
+    }
+    __device__ double max(double x) {
+        x = wave_max(x);
+        if constexpr (W == 1) {
+            return x;
+        } else {
+            if ((threadIdx.x & 63) == 0) d[flip * W + wave_id()] = x;
+            __syncthreads();
+            double t = d[flip * W];
+#pragma unroll
+            for (int k = 1; k < W; ++k) t = fmax(t, d[flip * W + k]);
+            flip ^= 1;
+            return t;
+        }
+    }
+    // wave-level count -> row count; with `below`, also the counts of the
+    // waves before this one
+    __device__ int count(int x, int* below = nullptr) {
+        if constexpr (W == 1) {
+            if (below) *below = 0;
+            return x;
+        } else {
+            if ((threadIdx.x & 63) == 0) c[flip * W + wave_id()] = x;
+            __syncthreads();
+            int t = 0, b = 0;
+            const int me = wave_id();
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const int v = c[flip * W + k];
+                b += k < me ? v : 0;
+                t += v;
+            }
+            flip ^= 1;
+            if (below) *below = b;
+            return t;
+        }
+    }
+};
+
+// Selection of one row of block probabilities.  W == 1: one wave per row
+// (kSelWaves rows per workgroup); W > 1: W waves per row, wave w holding the
+// blocks w 64 EM .. (w + 1) 64 EM - 1.  Lane l of a wave holds its range's
+// blocks l + 64 r.  The blocks in descending order of probability (equal
+// probabilities by ascending id) are never sorted: for a non-negative double
+// the bit pattern read as an unsigned integer orders like the value, so the
+// row is searched by bisection over that integer range.
 //   top-p: the element e at which the descending running sum first reaches p
 //          is the largest key x with sum(P >= x) >= p; within a run of equal
 //          values the running sum advances one element at a time.
 //   top-k: the k-th element is the largest key x with count(P >= x) >= k.
 // The selection is the longer of the two prefixes.  Slots past the row hold
-// P = -1, which no threshold >= 0 admits.
-template <int EM, bool AD>   // elements per lane: nb <= 64 EM; AD: adaptive blocks (w.lead set)
-__global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom g, int top_k,
-                                                                      double top_p, SparseWs w,
-                                                                      uint32_t* __restrict__ sel_mask,
-                                                                      int32_t* __restrict__ sel_count) {
+// P = -1, which no threshold >= 0 admits.  Rows are the query blocks
+// row0 .. row0 + rows - 1 of every head, whose scores hold the chunk.
+template <int EM, int W, bool AD>   // EM: elements per lane per wave; AD: adaptive blocks (w.lead set)
+__global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_kernel(
+        SparseGeom g, int top_k, double top_p, SparseWs w, int row0, int rows, uint32_t* __restrict__ sel_mask,
+        int32_t* __restrict__ sel_count) {
+    __shared__ double red_d[2 * W];
+    __shared__ int red_c[2 * W];
+    RowReduce<W> R{red_d, red_c};
     const int nb = g.nb;
-    const int row = (int)blockIdx.x * kSelWaves + wave_id();   // head * nb + i
-    if (row >= g.heads * nb) return;
+    const int local = W == 1 ? (int)blockIdx.x * kSelWaves + wave_id() : (int)blockIdx.x;   // head * rows + i - row0
+    if (local >= g.heads * rows) return;   // W == 1 only: a whole wave leaves, no barrier is skipped
+    const int head = local / rows;
+    const int row = head * nb + row0 + (local - head * rows);   // head * nb + i
     const int lane = threadIdx.x & 63;
-    const double* L = w.scores + (int64_t)row * nb;
+    const int jbase = W == 1 ? 0 : wave_id() * 64 * EM;        // first block of this wave's range
+    const double* L = w.scores + (int64_t)local * nb;
 
     // Columns that are blocks: every column with uniform blocks; with adaptive
     // blocks only each block's first tile (the other tiles of the block repeat
@@ -253,25 +326,26 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     if constexpr (AD) {
 #pragma unroll
         for (int r = 0; r < EM; ++r) {
-            const int j = lane + 64 * r;
+            const int j = jbase + lane + 64 * r;
             if (j < nb && w.lead[j] == j) okm |= 1ull << r;
         }
         nv = 0;
 #pragma unroll
         for (int r = 0; r < EM; ++r) nv += __popcll(__ballot((okm >> r) & 1ull));
+        nv = R.count(nv);
     }
-    auto col_ok = [&](int r) { return AD ? ((okm >> r) & 1ull) != 0 : lane + 64 * r < nb; };
+    auto col_ok = [&](int r) { return AD ? ((okm >> r) & 1ull) != 0 : jbase + lane + 64 * r < nb; };
 
     // softmax over the row's blocks, fp64
     double P[EM];
     double mx = -__builtin_inf();
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
-        const int j = lane + 64 * r;
+        const int j = jbase + lane + 64 * r;
         P[r] = col_ok(r) ? L[j] : -__builtin_inf();
         mx = fmax(mx, P[r]);
     }
-    mx = wave_max(mx);
+    mx = R.max(mx);
     double se = 0.0;
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
@@ -280,7 +354,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
             se += P[r];
         }
     }
-    se = wave_sum(se);
+    se = R.sum(se);
     double tot = 0.0;
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
@@ -291,35 +365,35 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
             P[r] = -1.0;
         }
     }
-    tot = wave_sum(tot);
+    tot = R.sum(tot);
 
     auto count_ge = [&](double t) {
         int c = 0;
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             c += __popcll(__ballot(P[r] >= t));
-        return c;
+        return R.count(c);
     };
     auto count_eq = [&](double t) {
         int c = 0;
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             c += __popcll(__ballot(P[r] == t));
-        return c;
+        return R.count(c);
     };
     auto count_in = [&](double lo, double hi) {
         int c = 0;
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             c += __popcll(__ballot(P[r] >= lo && P[r] < hi));
-        return c;
+        return R.count(c);
     };
     auto sum_ge = [&](double t) {
         double x = 0.0;
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             if (P[r] >= t) x += P[r];
-        return wave_sum(x);
+        return R.sum(x);
     };
     // the one value left in [lo, hi) once the bisection stops
     auto value_in = [&](double lo, double hi) {
@@ -327,7 +401,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             if (P[r] >= lo && P[r] < hi) x = fmax(x, P[r]);
-        return wave_max(x);
+        return R.max(x);
     };
     const uint64_t kInf = 0x7FF0000000000000ull;   // +inf: above every probability
 
@@ -340,7 +414,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
             double x = P[0];
 #pragma unroll
             for (int r = 1; r < EM; ++r) x = fmax(x, P[r]);
-            vp = wave_max(x);
+            vp = R.max(x);
             mp = 1;
             n_p = 1;
         } else {
@@ -391,10 +465,19 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
     const bool all = K >= nv;
     const double v = kk > n_p ? vk : vp;
     const int mrun = kk > n_p ? mk : mp;
+    // run elements (== v) in the waves before this one
+    int before = 0;
+    if constexpr (W > 1) {
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r) c += __popcll(__ballot(P[r] >= 0.0 && P[r] == v));
+        R.count(c, &before);
+    }
     const int nw = (nb + 31) >> 5;
     uint32_t* mrow = w.mask + (int64_t)row * nw;
     uint32_t* srow = sel_mask ? sel_mask + (int64_t)row * nw : nullptr;
-    int before = 0;        // run elements with a lower id
+    // Adaptive blocks never straddle a zone (8 tiles), so every 64-column word
+    // of a wave's range starts a block and a block's tiles share its word.
     uint64_t prev = 0, prev_starts = 0;   // block-start decisions and positions of the previous 64 columns
 #pragma unroll
     for (int r = 0; r < EM; ++r) {
@@ -414,16 +497,16 @@ __global__ __launch_bounds__(64 * kSelWaves) void block_select_kernel(SparseGeom
                                   : (prev_starts && ((prev >> (63 - __clzll(prev_starts))) & 1ull));
             prev = b;
             prev_starts = starts;
-            b = __ballot(sel || (inh && lane + 64 * r < nb));
+            b = __ballot(sel || (inh && jbase + lane + 64 * r < nb));
         }
-        const int wd = 2 * r + lane;
+        const int wd = (jbase >> 5) + 2 * r + lane;
         if (lane < 2 && wd < nw) {   // words past the row hold no bits
             const uint32_t word = lane ? (uint32_t)(b >> 32) : (uint32_t)b;
             mrow[wd] = word;
             if (srow) srow[wd] = word;
         }
     }
-    if (lane == 0) {
+    if (lane == 0 && (W == 1 || wave_id() == 0)) {
         w.count[row] = K;
         if (sel_count) sel_count[row] = K;
     }
@@ -684,34 +767,40 @@ hipError_t launch_vt_blocks(const SparseGeom& g, const __bf16* k, const __bf16* 
     return hipGetLastError();
 }
 
-hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w,
+hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const SparseWs& w, int row0, int rows,
                                hipStream_t s) {
-    const unsigned nt = (unsigned)((g.nb + kSB - 1) / kSB);
-    hipLaunchKernelGGL(block_scores_kernel<128>, dim3(nt, nt, g.heads), dim3(256), 0, s, g, scale,
-                       w);
+    const unsigned ct = (unsigned)((g.nb + kSB - 1) / kSB), rt = (unsigned)((rows + kSB - 1) / kSB);
+    hipLaunchKernelGGL(block_scores_kernel<128>, dim3(ct, rt, g.heads), dim3(256), 0, s, g, scale, w, row0, rows);
     (void)hd;
     return hipGetLastError();
 }
 
-hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w,
+hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w, int row0, int rows,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s) {
-    const unsigned blocks = (unsigned)((g.heads * g.nb + kSelWaves - 1) / kSelWaves);
-    const dim3 grid(blocks), block(64 * kSelWaves);
-    const int em = (g.nb + 63) / 64;
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, block, 0, s, g, top_k, top_p, w, sel_mask, sel_count);
-    };
+    const int em = (g.nb + 63) / 64;   // elements per lane with one wave per row
     const bool ad = w.lead != nullptr;
+    auto go = [&](auto kernel, unsigned blocks, unsigned threads) {
+        hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, s, g, top_k, top_p, w, row0, rows, sel_mask,
+                           sel_count);
+    };
+    const unsigned one = (unsigned)((g.heads * rows + kSelWaves - 1) / kSelWaves), wide = (unsigned)(g.heads * rows);
     if (em <= 8)
-        ad ? go(block_select_kernel<8, true>) : go(block_select_kernel<8, false>);
+        ad ? go(block_select_kernel<8, 1, true>, one, 64 * kSelWaves) : go(block_select_kernel<8, 1, false>, one, 64 * kSelWaves);
     else if (em <= 16)
-        ad ? go(block_select_kernel<16, true>) : go(block_select_kernel<16, false>);
+        ad ? go(block_select_kernel<16, 1, true>, one, 64 * kSelWaves) : go(block_select_kernel<16, 1, false>, one, 64 * kSelWaves);
     else if (em <= 32)
-        ad ? go(block_select_kernel<32, true>) : go(block_select_kernel<32, false>);
+        ad ? go(block_select_kernel<32, 1, true>, one, 64 * kSelWaves) : go(block_select_kernel<32, 1, false>, one, 64 * kSelWaves);
     else if (em <= 48)
-        ad ? go(block_select_kernel<48, true>) : go(block_select_kernel<48, false>);
+        ad ? go(block_select_kernel<48, 1, true>, one, 64 * kSelWaves) : go(block_select_kernel<48, 1, false>, one, 64 * kSelWaves);
+    else if (em <= 64)
+        ad ? go(block_select_kernel<64, 1, true>, one, 64 * kSelWaves) : go(block_select_kernel<64, 1, false>, one, 64 * kSelWaves);
+    // more than 4096 blocks: 2, 4 or 8 waves per row, 64 elements per lane
+    else if (em <= 128)
+        ad ? go(block_select_kernel<64, 2, true>, wide, 128) : go(block_select_kernel<64, 2, false>, wide, 128);
+    else if (em <= 256)
+        ad ? go(block_select_kernel<64, 4, true>, wide, 256) : go(block_select_kernel<64, 4, false>, wide, 256);
     else
-        ad ? go(block_select_kernel<64, true>) : go(block_select_kernel<64, false>);
+        ad ? go(block_select_kernel<64, 8, true>, wide, 512) : go(block_select_kernel<64, 8, false>, wide, 512);
     return hipGetLastError();
 }
 

@@ -97,7 +97,12 @@ def test_workspace_plans():
     assert big > 24 * 128 * 34368 * 2
     sd = J.sparse_desc()
     b = ws(J.MMDIT_OP_BLOCK_SPARSE_ATTN, 172032, 172032, 24, 128, J.MMDIT_BF16, sd)
-    assert b >= 24 * 2688 * 2688 * 8 + 24 * 2688 * 84 * 4 + 24 * 2688 * 128 * 64 * 2
+    # block logits are computed and selected 2048 query blocks at a time (1 GiB for all heads)
+    assert b >= 24 * 2048 * 2688 * 8 + 24 * 2688 * 84 * 4 + 2 * 24 * 2688 * 128 * 64 * 2
+    assert b < 24 * 2688 * 2688 * 8 + 2 * 24 * 2688 * 128 * 64 * 2 + (1 << 28)
+    # a million-token grid: the logits stay within the 1 GiB chunk
+    big = ws(J.MMDIT_OP_BLOCK_SPARSE_ATTN, 32 * 128 * 256, 0, 24, 128, J.MMDIT_BF16, sd)
+    assert big < 2 * 24 * 16384 * 128 * 64 * 2 + (3 << 30)
 
 
 def _call_joint(**over):
@@ -203,6 +208,7 @@ def test_rope_rejects_bad_descriptors():
     (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
     (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
     (dict(ws_bytes=10), L.MMDIT_ERR_WORKSPACE),
+    (dict(T=32, H=256, W=272), L.MMDIT_ERR_UNSUPPORTED),    # 34816 blocks per head (max 32768)
     (dict(wait_limit=-1), L.MMDIT_ERR_INVALID_ARG),
     (dict(wait_limit=(1 << 18) + 1), L.MMDIT_ERR_INVALID_ARG),
 ])
@@ -302,7 +308,7 @@ def _adaptive_call(**over):
     (dict(T=20), L.MMDIT_ERR_INVALID_ARG),                  # not whole 8 x 8 x 8 zones
     (dict(W=100), L.MMDIT_ERR_INVALID_ARG),
     (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
-    (dict(T=48), L.MMDIT_ERR_UNSUPPORTED),                  # 672 zones, 5376 tiles
+    (dict(T=64, H=128, W=272), L.MMDIT_ERR_UNSUPPORTED),    # 4352 zones, 34816 tiles (max 32768)
     (dict(top_k=-1), L.MMDIT_ERR_INVALID_ARG),
     (dict(top_p=1.5), L.MMDIT_ERR_INVALID_ARG),
     (dict(scale=-0.5), L.MMDIT_ERR_INVALID_ARG),
@@ -358,7 +364,7 @@ def _adaptive_bwd_call(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(T=20), L.MMDIT_ERR_INVALID_ARG),
-    (dict(T=48), L.MMDIT_ERR_UNSUPPORTED),
+    (dict(T=64, H=128, W=272), L.MMDIT_ERR_UNSUPPORTED),    # 4352 zones (max 4096)
     (dict(hd=64), L.MMDIT_ERR_UNSUPPORTED),
     (dict(scale=float("inf")), L.MMDIT_ERR_INVALID_ARG),
     (dict(shape=0), L.MMDIT_ERR_INVALID_ARG),

@@ -425,3 +425,83 @@ def test_block_sparse_explicit_softmax_scale():
     ref = B.block_sparse_attention(q64, k64, v64, idx, m_ref, scale=s)
     worst = max(float(np.max(np.abs(f64(o)[idx[i], hh] - r))) for (hh, i), r in ref.items())
     assert worst <= TOL_BF16, worst
+
+
+# ---- more than 4096 blocks per head: selection rows over several waves ---------------
+def _sparse_large(T, H, W, heads, k_sel, p_sel, n_qblocks, seed, check_heads=None):
+    """Selection bit-exact on the checked heads, O on sampled query blocks of
+    those heads (with the largest and smallest selections), through the
+    oracle; only the checked heads' tensors come to the host."""
+    w = shrink("sparse2k", T=T, H=H, W=W, heads=heads, seed=seed)
+    x = sparse_inputs(w, DEV)
+    o, mask, cnt = J.mmdit_block_sparse_attn(x["q"], x["k"], x["v"], T, H, W, w["zone"], w["block"], k_sel, p_sel)
+    torch.cuda.synchronize()
+    hs = list(range(heads)) if check_heads is None else check_heads
+    idx = B.block_token_index(T, H, W, w["zone"], w["block"])
+    nb = idx.shape[0]
+    sel = torch.tensor(hs, device=DEV)
+    q32, k32, v32 = (x[t].index_select(1, sel).float().cpu().numpy() for t in ("q", "k", "v"))
+    del x
+    P = B.block_probs(B.block_means(q32, idx), B.block_means(k32, idx))
+    m_ref, c_ref, margin = B.select_blocks(P, k_sel, p_sel)
+    del P
+    assert margin["cumsum"] > 1e-12 and margin["rel_gap"] > 1e-12, margin
+    got = mask.index_select(0, sel).cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, B.pack_mask(m_ref))
+    assert np.array_equal(cnt.index_select(0, sel).cpu().numpy(), c_ref)
+    calls = []
+    for hi in range(len(hs)):
+        qbs = sample_rows(nb, n_qblocks, seed + hi, must=[int(np.argmax(c_ref[hi])), int(np.argmin(c_ref[hi]))])
+        sl = np.s_[:, hi:hi + 1]
+        calls.append(((q32[sl], k32[sl], v32[sl], idx, m_ref[hi:hi + 1]), dict(query_blocks=[int(i) for i in qbs],
+                                                                              heads=[0])))
+    out = o.index_select(1, sel)
+    worst = 0.0
+    for hi, ref in enumerate(OP.starmap("oracle.block_sparse", "block_sparse_attention", calls)):
+        for (_, i), r in ref.items():
+            rows = torch.from_numpy(idx[i]).to(DEV)
+            worst = max(worst, float(np.max(np.abs(out[rows, hi].double().cpu().numpy() - r))))
+    dens = float(c_ref.mean()) / nb
+    print("%d x %d x %d (%d tokens, %d blocks/head): selection of %d heads bit-exact, density %.3f, "
+          "O max-abs %.3e on %d query blocks per head" % (T, H, W, T * H * W, nb, len(hs), dens, worst,
+                                                          len(calls[0][1]["query_blocks"])), flush=True)
+    assert worst <= TOL_BF16, worst
+    return c_ref
+
+
+def test_block_sparse_8192_blocks():
+    """8192 blocks per head: each selection row held by two waves."""
+    _sparse_large(16, 128, 256, 2, 32, 0.9, 24, 31)
+
+
+def test_block_sparse_million_tokens():
+    """32 x 128 x 256 = 1048576 tokens, 16384 blocks per head, 24 heads (rows
+    over four waves; the block logits computed and selected in chunks of
+    query blocks): selection of two heads bit-exact, O on sampled query
+    blocks of those heads."""
+    _sparse_large(32, 128, 256, 24, 32, 0.9, 16, 32, check_heads=[0, 23])
+
+
+def test_block_sparse_eight_wave_rows():
+    """24 x 176 x 256 = 1081344 tokens, 16896 blocks per head: rows over eight waves."""
+    _sparse_large(24, 176, 256, 1, 32, 0.9, 16, 33)
+
+
+def test_block_sparse_ties_across_waves():
+    """Every key block equal (K constant) on an 8192-block grid: the
+    probabilities are exactly 2^-13, top-p 0.7 needs 5735 blocks, so the cut
+    falls in the second wave of each row and the ids below it in the first
+    wave must be counted (ties go to the lower id)."""
+    T, H, W = 16, 128, 256
+    w = shrink("sparse2k", T=T, H=H, W=W, heads=1, seed=34)
+    x = sparse_inputs(w, DEV)
+    k = x["k"][:1].expand_as(x["k"]).contiguous()
+    o, mask, cnt = J.mmdit_block_sparse_attn(x["q"], k, x["v"], T, H, W, top_k=5, top_p=0.7)
+    torch.cuda.synchronize()
+    assert (cnt == 5735).all()
+    m = mask.cpu().numpy().view(np.uint32)
+    want = np.zeros_like(m[0, 0])
+    bits = np.zeros(8192, dtype=bool)
+    bits[:5735] = True
+    want = np.packbits(bits.reshape(-1, 32)[:, ::-1], axis=1).view(">u4").astype(np.uint32).reshape(-1)
+    assert (m == want[None, None, :]).all()
