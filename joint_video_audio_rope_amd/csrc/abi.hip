@@ -510,7 +510,7 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
             hipSuccess)
             return hip_fail(e, "block_sparse select");
     }
-    if ((e = launch_sparse_attn(p.g, (const __bf16*)q, (const __bf16*)k, head_dim,
+    if ((e = launch_sparse_attn(p.g, (const __bf16*)q, head_dim,
                                 (float)(softmax_scale * 1.4426950408889634), sw, o, lse,
                                 sp->wait_limit ? sp->wait_limit : kSpinLimit, s)) != hipSuccess)
         return hip_fail(e, "block_sparse attention");

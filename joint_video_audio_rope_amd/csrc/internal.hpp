@@ -278,7 +278,8 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 // wait_limit: bound of each of the kernel's internal waits, in sleeps of
 // about 64 cycles (1 .. kSpinLimit).  A wait that reaches it gives up and the
 // workgroup writes NaN to its o rows and lse entries.
-hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
+// K and V come from the staged block images in w.
+hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, int hd,
                               float scale_log2, const SparseWs& w, float* o, float* lse, int wait_limit,
                               hipStream_t s);
 constexpr int kSpinLimit = 1 << 18;

@@ -96,6 +96,47 @@ __global__ __launch_bounds__(512) void block_pool_kernel(SparseGeom g, const __b
     }
 }
 
+// LDS image of one staged key block for the sparse attention kernel: K (64
+// rows x HD bf16) and then V^T (HD rows x 64 keys fp16), 16-byte chunks.  A
+// wave reads 32 rows x 16 bytes per fragment: lane (m, hh) reads chunk hh of
+// a 32-byte pair in row m.  Each pair of chunks of a row is stored
+// contiguously, row after row, one 2 KB (K) or 4 KB (V^T) panel per pair;
+// rows 8..15 of every 16 swap the two chunks of their pair, so the 16 lanes
+// served together (16 rows, one chunk each) hit 16 different 16-byte slots of
+// a 256-byte line.  Every fragment of a lane then sits at one per-lane offset
+// plus a constant: no per-fragment address registers.
+//   K chunk (row r, d chunk c):   (c >> 1) * 2048 + r * 32 + ((c & 1) ^ ((r >> 3) & 1)) * 16
+//   V^T chunk (row d, key chunk c): kKBytes + (c >> 1) * 4096 + d * 32 + ((c & 1) ^ ((d >> 3) & 1)) * 16
+template <int HD>
+struct StreamTile {
+    static constexpr int kKBytes = kTileN * HD * 2;
+    static constexpr int kVBytes = HD * kTileN * 2;
+    static constexpr int kBytes = kKBytes + kVBytes;
+    static constexpr int kKPanel = kTileN * 32;    // one d-chunk pair of all 64 K rows
+    static constexpr int kVPanel = HD * 32;        // one key-chunk pair of all HD V^T rows
+    // inverse maps: which (row, chunk) a 16-byte chunk index u of the K or V^T part holds
+    __host__ __device__ static void k_at(int u, int& row, int& c) {
+        row = (u % (kKPanel / 16)) >> 1;
+        c = 2 * (u / (kKPanel / 16)) + ((u & 1) ^ ((row >> 3) & 1));
+    }
+    __host__ __device__ static void v_at(int u, int& d, int& c) {
+        d = (u % (kVPanel / 16)) >> 1;
+        c = 2 * (u / (kVPanel / 16)) + ((u & 1) ^ ((d >> 3) & 1));
+    }
+    // lane (m, hh)'s offset inside a panel; fragment (step ks, key half kb)
+    // of K and (row block db, key group gq) of V^T add constants to it
+    __device__ static int lane_offset() {
+        const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
+        return m * 32 + ((hh ^ ((m >> 3) & 1)) << 4);
+    }
+    __device__ static bf16x8 k_frag(const char* tile, int lo, int ks, int kb) {
+        return *reinterpret_cast<const bf16x8*>(tile + lo + ks * kKPanel + kb * 32 * 32);
+    }
+    __device__ static f16x8 v_frag(const char* tile, int lo, int db, int gq) {
+        return *reinterpret_cast<const f16x8*>(tile + kKBytes + lo + gq * kVPanel + db * 32 * 32);
+    }
+};
+
 // One workgroup per (block, head): gather the block's 64 rows of K and of V
 // and write each as the exact image of its LDS tile (K rows in the MFMA row
 // order, V transposed to fp16 [d][64] with the head's prescale 2^e applied,
@@ -105,7 +146,7 @@ __global__ __launch_bounds__(512) void block_pool_kernel(SparseGeom g, const __b
 template <int HD>
 __global__ __launch_bounds__(256) void vt_blocks_kernel(SparseGeom g, const __bf16* __restrict__ k,
                                                         const __bf16* __restrict__ v, SparseWs w) {
-    using L = TileLayout<HD>;
+    using L = StreamTile<HD>;
     __shared__ _Float16 tile[kTileN][HD + 2];
     const int j = blockIdx.x, head = blockIdx.y;
     const float sc = __builtin_ldexpf(1.f, v_scale_exp(w.vmax, head));   // the head's V prescale
@@ -201,12 +242,16 @@ __global__ __launch_bounds__(256) void block_scores_kernel(SparseGeom g, double 
 
 constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup of one-wave rows
 // Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
-// Measured on the 24 x 64 x 112 grid (density 27.6 %): a group stages on
-// average 0.73 (pairs), 0.62 (triples), 0.50 (4 blocks) of the tiles its
-// blocks select; with workgroup barriers per tile, pairs (two workgroups per
-// CU) took 164 ms and groups of 4 (idle waves on tiles only some blocks
-// selected) 205 ms, while groups of 4 fed by producer waves take 132-134 ms.
-constexpr int kStreamGroup = 4;
+// Measured on the 24 x 64 x 112 grid (density 27.6 %), where a block selects
+// 742 key blocks on average: a group of G consecutive blocks stages the union
+// of their selections, 1488 tiles for G = 4 and 1951 for G = 7, so the
+// gathered K/V tiles per call fall from 786 GB to 589 GB and the copies alone
+// from 95 ms to 69 ms.  The consumers' compute bounds the kernel, and more
+// waves per SIMD keep more of them busy: the call went from 133.3 ms (G = 4,
+// whole-tile steps at 168 registers) to 129.4 ms (G = 7, half-tile steps at
+// 128).  With workgroup barriers per tile instead of producer waves, pairs
+// took 164 ms and groups of 4 205 ms.
+constexpr int kStreamGroup = 7;
 constexpr int kStreamRing = 4;
 
 // Wave-wide reductions.  The xor butterfly combines the same two partial
@@ -512,31 +557,76 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
     }
 }
 
+// One 32-key half KB of a staged 64-key tile for the wave's 32 queries:
+// S^T = K_KB Q^T (8 MFMAs), the online softmax against the reference maximum,
+// O^T += V_KB^T P^T (8 MFMAs).  The steps, key order and rounding points of
+// tile_step, on half its registers: with 16 waves per workgroup a wave has
+// 128.  lo is the lane's StreamTile offset.
+template <int HD, int KB>
+__device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, int lo, const bf16x8 (&qf)[HD / 16],
+                                               SoftmaxState<HD, 1>& st, float scale_log2) {
+    using L = StreamTile<HD>;
+    constexpr int NK = HD / 16;   // MFMA steps over d
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L::k_frag(tile, lo, ks, KB), qf[ks], s, 0, 0, 0);
+    float x = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
+    const float mx[1] = {pair_max(x) * scale_log2};
+    maybe_rescale<HD, 1>(st, mx);
+    const float mneg = -st.m_run[0];
+    // P in the B-operand order of the P V^T product: register r of the score
+    // block is key 16 (r / 8) + 8 hh + r % 8 of this half
+    f16x8 pf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, mneg));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+            st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(L::v_frag(tile, lo, db, 2 * KB + u), pf[u],
+                                                                 st.o[0][db], 0, 0, 0);
+    const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+    float ls = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const f16x2 pair = {pf[p >> 2][2 * (p & 3)], pf[p >> 2][2 * (p & 3) + 1]};
+        ls = __builtin_amdgcn_fdot2(pair, ones, ls, false);
+    }
+    st.l_run[0] += ls;
+}
+
 // Sparse attention with producer waves.  A workgroup serves G consecutive
-// query blocks of one head with 2 G consumer waves, two per block (which
-// waves own which block is chosen for the SIMD placement described at the
-// consumers), and two producer waves.  The producers stream the union of
+// query blocks of one head with 2 G consumer waves, two per block (32
+// queries each), and two producer waves.  The producers stream the union of
 // the G selections, in ascending block id, into a ring of R LDS tiles (the
-// block's K rows and fp16 V^T, each one contiguous image); producer p copies
-// the tiles t with t % 2 == p.  Consumers follow the same walk and compute
-// only the tiles their block selected.  There is no workgroup barrier in the
-// walk: a producer publishes each tile through its slot's LDS flag and reuses
-// a slot once every consumer has released the tile in it, so the consumers
-// run up to R - 1 tiles apart and none waits on another's compute except
-// through a full ring.  A producer publishes its previous tile as soon as its
-// copies have landed, before it waits for the slot of its next tile: when
+// block's K rows and fp16 V^T, one contiguous StreamTile image); producer p
+// copies the tiles t with t % 2 == p.  Consumers follow the same walk and
+// wait for, compute and release only the tiles their block selected.  There
+// is no workgroup barrier in the walk: a producer publishes each tile through
+// its slot's LDS flag and reuses a slot once the waves that use the tile in
+// it have released it, so a wave waits on another's compute only through a
+// full ring.  A producer publishes its previous tile as soon as its copies
+// have landed, before it waits for the slot of its next tile: when
 // publication waited behind that slot, a tile became visible only after the
 // consumers had released the tiles ahead of it, which shrank the consumers'
 // lead (4 % slower with one producer).  Two producers keep two tiles' copies
 // in flight (one more 1.3 % on the 24 x 64 x 112 grid; three or four gain no
 // more).  Larger groups share each staged tile among more blocks (a tile
-// costs the same 32 KB however many blocks use it), and the decoupled walk
-// keeps the waves of blocks that did not select a tile from idling on it.
+// costs the same 32 KB however many blocks use it); G = 7 fills the 16 waves
+// a workgroup can hold.
 //
 // Flags: ready[s] = t + 1 once tile t (slot s = t mod R) has landed (slots
-// are written in increasing t: tile t + R is issued only after every consumer
-// released tile t, which follows its publication); released[s] counts
-// consumer waves done with slot s over all its uses.
+// are written in increasing t: tile t + R is issued only after the users of
+// tile t released it, which follows its publication); released[s] counts the
+// releases of slot s over all its uses, and the producer owning the slot
+// (s % 2) counts the releases its tiles are due: two per block that selected
+// the tile.
 typedef __attribute__((address_space(3))) int lds_int;
 
 __device__ __forceinline__ int lds_load(lds_int* p) {
@@ -585,13 +675,13 @@ __device__ __forceinline__ void spin_ge(lds_int* p, int v, lds_int* broken, int 
 
 template <int HD, int G, int R>
 __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_kernel(
-        SparseGeom g, const __bf16* __restrict__ q, const __bf16* __restrict__ k, float scale_log2,
-        SparseWs w, float* __restrict__ o, float* __restrict__ lse, int spin_limit) {
-    using L = TileLayout<HD>;
+        SparseGeom g, const __bf16* __restrict__ q, float scale_log2, SparseWs w, float* __restrict__ o,
+        float* __restrict__ lse, int spin_limit) {
+    using L = StreamTile<HD>;
     constexpr int NC = 2 * G;                          // consumer waves; waves NC, NC + 1 produce
     constexpr int KS = HD / 16;
-    constexpr int KCP = kTileN * L::kKChunks / kWave;  // producer copies per tile: K
-    constexpr int VCP = HD * 8 / kWave;                //                          V^T
+    constexpr int KCP = L::kKBytes / (16 * kWave);     // producer copies per tile: K
+    constexpr int VCP = L::kVBytes / (16 * kWave);     //                          V^T
     static_assert(R >= 2 && (R & (R - 1)) == 0, "ring of a power-of-two number of tiles");
     static_assert(KCP + VCP < 64, "vmcnt immediate");
     __shared__ __attribute__((aligned(16))) char lds[R * L::kBytes];
@@ -662,12 +752,27 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
         // ---- producers: wave NC + p copies the tiles t with t % 2 == p ----
         const int pp = wv - NC;
         int t = 0, last = -1;
+        // releases of this producer's slots (sl % 2 == pp) that its tiles so
+        // far will collect: two per block that selected the tile
+        int due[R / 2];
+#pragma unroll
+        for (int i = 0; i < R / 2; ++i) due[i] = 0;
         for (int j = advance(); j >= 0; j = advance(), ++t) {
             if (t % 2 != pp) continue;
             const int sl = t & (R - 1);
             // publish this producer's previous tile once it has landed
             if (last >= 0) publish_after<0>(ready_at(last & (R - 1)), last + 1);
-            if (t >= R) spin_ge(released_at(sl), NC * (t / R), brk, spin_limit);   // tile t - R is done
+            int users = 0;
+#pragma unroll
+            for (int sd = 0; sd < G; ++sd) users += (msk[sd][j >> 5] >> (j & 31)) & 1u;
+            users = __builtin_amdgcn_readfirstlane(users);
+#pragma unroll
+            for (int i = 0; i < R / 2; ++i) {
+                if ((sl >> 1) != i) continue;
+                // every user of tile t - R in this slot is done with it
+                if (t >= R) spin_ge(released_at(sl), due[i], brk, spin_limit);
+                due[i] += 2 * users;
+            }
             char* lb = lds + sl * L::kBytes;
             const int64_t blk = (int64_t)head * g.nb + j;
             const char* kt = reinterpret_cast<const char*>(w.kimg + blk * (kTileN * HD)) + 16 * lane;
@@ -682,13 +787,8 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
         return;
     }
 
-    // ---- consumers ----
-    // Waves w and w + 4 share a SIMD.  Blocks of a group are a 2 x 2 (h, w)
-    // square of neighbours; the selections of edge neighbours correlate most,
-    // so each SIMD gets one wave of each block of a diagonal pair (blocks 0
-    // and 3 on SIMDs 0-1, 1 and 2 on SIMDs 2-3) and concurrent work on edge
-    // neighbours spreads over all four SIMDs.
-    const int side = G == 4 ? (wv < 4 ? (wv >> 1) : 3 - ((wv - 4) >> 1)) : (wv >> 1);
+    // ---- consumers: waves 2 b and 2 b + 1 hold the two halves of block b ----
+    const int side = wv >> 1;
     const int hh = lane >> 5;
     const int m = lane & 31;
     const int qb = min(b0 + side, g.nb - 1);
@@ -699,10 +799,7 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
     for (int ks = 0; ks < KS; ++ks)
         qf[0][ks] = load_bf16x8(q + qtok * rstride + head * HD + 16 * ks + 8 * hh, true);
 
-    FragAddr<HD> fa;
-    fa.init();
-    f32x16 sc[1][2], sd[1][2];
-    float mx[1];
+    const int lo = L::lane_offset();
     SoftmaxState<HD, 1> st;
     st.init();
     int t = 0;
@@ -714,19 +811,16 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
             own_word = j >> 5;
             own = __builtin_amdgcn_readfirstlane(msk[side][own_word]);
         }
-        // Wait for the tile even when this block skips it: released[] counts
-        // every use of a slot, so a wave may release tile t only once tile
-        // t has been published, i.e. once every wave released tile t - R.
-        // Otherwise a wave skipping ahead could release t and t + R before
-        // a slower wave is done with t, and the producer would overwrite it.
+        // Only the waves of blocks that selected a tile wait for it and
+        // release it; the producer reuses the slot once those releases are
+        // in.  A wave whose block skips a stretch of tiles therefore neither
+        // waits for them nor holds their slots.
+        if (!((own >> (j & 31)) & 1u)) continue;
         wait_published(t);
-        if ((own >> (j & 31)) & 1u) {
-            const char* cur = lds + sl * L::kBytes;
-            qk_tile<HD, 1>(cur, fa, qf, sc);
-            tile_max<false, 1>(sc, scale_log2, kTileN, mx);
-            maybe_rescale<HD, 1>(st, mx);
-            tile_step<HD, 1, false, false>(nullptr, cur + L::kKBytes, fa, qf, sc, sd, st, scale_log2, kTileN, mx);
-        }
+        const char* cur = lds + sl * L::kBytes;
+        half_tile_step<HD, 0>(cur, lo, qf[0], st, scale_log2);
+        __builtin_amdgcn_sched_barrier(0);
+        half_tile_step<HD, 1>(cur, lo, qf[0], st, scale_log2);
         // this wave's reads of the slot are done (LDS serves a wave in order)
         __asm__ volatile("" ::: "memory");
         if (lane == 0) __hip_atomic_fetch_add(released_at(sl), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -748,6 +842,7 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
         lse[(int64_t)head * ((int64_t)g.T * g.H * g.W) + qtok] =
             bad ? __builtin_nanf("") : (st.m_run[0] + log2f(l_tot)) * kLn2;
 }
+
 
 }  // namespace
 
@@ -804,14 +899,14 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, const __bf16* k, int hd,
+hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, int hd,
                               float scale_log2, const SparseWs& w, float* o, float* lse, int wait_limit,
                               hipStream_t s) {
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
     const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
-    hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g,
-                       q, k, scale_log2, w, o, lse, wait_limit);
+    hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g, q,
+                       scale_log2, w, o, lse, wait_limit);
     return hipGetLastError();
 }
 
