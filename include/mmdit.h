@@ -371,7 +371,7 @@ mmdit_status mmdit_token_norms(const float* x, int64_t n, int64_t width, float* 
  * int32 number of blocks; sel_mask [heads][nt][ceil(nt/32)] uint32, row i
  * (tile i) has bit j set iff tile j's block is selected by tile i's block;
  * sel_count [heads][nt] int32 selected blocks of tile i's block.  T, H, W must
- * be multiples of 8, nz <= 512, head_dim 128.  Workspace:
+ * be multiples of 8, nz <= 4096, head_dim 128.  Workspace:
  * mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE, T*H*W, 0, heads,
  * head_dim, MMDIT_BF16, NULL). */
 mmdit_status mmdit_block_sparse_attn_adaptive(const void* q, const void* k, const void* v, const float* a_norm,

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kStatPairs) void zone_stats_kernel(SparseGeom g, co
     }
 }
 
-// One workgroup of 1024 threads; zones <= kMaxZones (512).
+// One workgroup of 1024 threads; zones <= kMaxZones, up to four per thread.
 __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chunks, int channels,
                                                            AdaptiveWs w) {
 #pragma clang fp contract(off)
@@ -164,9 +164,10 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
     __shared__ uint8_t zcode[kMaxZones];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nz = g.nb / kZoneTiles;
-    const int m = tid;
-    double s2[3] = {0.0, 0.0, 0.0}, E = 0.0, am = 0.0;
-    if (m < nz) {
+    // per-axis variance sums of zone m (channel means), their total E and the
+    // zone's audio norm
+    auto zone_energy = [&](int m, double (&s2)[3], double& E, double& am) {
+        s2[0] = s2[1] = s2[2] = 0.0;
         for (int y = 0; y < chunks; ++y)
 #pragma unroll
             for (int d = 0; d < 3; ++d) s2[d] += w.part[((int64_t)m * chunks + y) * 3 + d];
@@ -174,8 +175,14 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
         for (int d = 0; d < 3; ++d) s2[d] /= (double)channels;
         E = (s2[0] + s2[1]) + s2[2];
         am = w.audio[m * 4];
+    };
+    double e = 0.0, x = 0.0;
+    for (int m = tid; m < nz; m += 1024) {
+        double s2[3], E, am;
+        zone_energy(m, s2, E, am);
+        e = fmax(e, E);
+        x = fmax(x, am);
     }
-    double e = E, x = am;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         e = fmax(e, __shfl_xor(e, o));
@@ -185,7 +192,9 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
     __syncthreads();
     double emax = 0.0, amax = 0.0;
     for (int i = 0; i < 16; ++i) emax = fmax(emax, emax_s[i]), amax = fmax(amax, amax_s[i]);
-    if (m < nz) {
+    for (int m = tid; m < nz; m += 1024) {
+        double s2[3], E, am;
+        zone_energy(m, s2, E, am);
         const double rho = emax > 0.0 ? E / emax : 0.0;
         const int lb = rho >= kTau128 ? 6 : rho >= kTau256 ? 7 : 8;   // log2 B
         const double abar = amax > 0.0 ? am / amax : 0.0;
@@ -204,13 +213,13 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
         int best = lb == 6 ? 0 : lb == 7 ? 7 : 13;
         double bd = __builtin_inf();
         for (int i = 0; i < 16; ++i) {
-            int e[3];
-            adaptive_candidate(i, e[0], e[1], e[2]);
-            if (e[0] + e[1] + e[2] != lb) continue;
+            int ed[3];
+            adaptive_candidate(i, ed[0], ed[1], ed[2]);
+            if (ed[0] + ed[1] + ed[2] != lb) continue;
             double dist = 0.0;
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
-                const double diff = (double)e[d] - (-0.5 * lg[d] + c3);
+                const double diff = (double)ed[d] - (-0.5 * lg[d] + c3);
                 dist += diff * diff;
             }
             if (dist < bd) bd = dist, best = i;

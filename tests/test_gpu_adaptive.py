@@ -155,9 +155,9 @@ def test_adaptive_full_size_sampled():
     assert err <= TOL_O
 
 
-def test_adaptive_maximum_zones():
-    """512 zones (4096 tiles per head), the most one shape pass serves: every
-    zone's code, the whole tile bitmask, o of sampled query blocks."""
+def test_adaptive_512_zones():
+    """512 zones (4096 tiles per head, the most one selection wave holds):
+    every zone's code, the whole tile bitmask, o of sampled query blocks."""
     w = shrink("adaptive2k", T=16, H=128, W=128, heads=1, fg_radius=30.0, audio_radius=15.0, seed=16)
     T, H, W = w["T"], w["H"], w["W"]
     x = adaptive_inputs(w, DEV)
@@ -179,6 +179,36 @@ def test_adaptive_maximum_zones():
     out = A.ragged_sparse_attention(q64, k64, v64, blocks, m_ref, query_blocks=sample)
     o64 = f64(r["o"])
     err = max(float(np.max(np.abs(o64[blocks[i], hi] - o))) for (hi, i), o in out.items())
+    assert err <= TOL_O
+
+
+def test_adaptive_zones_beyond_one_per_thread():
+    """1536 zones (12288 tiles per head, 786432 tokens): more zones than the
+    shape pass has threads and more tiles than one selection wave holds.
+    Every zone's code, the whole tile bitmask and counts, o of sampled query
+    blocks."""
+    w = shrink("adaptive2k", T=24, H=128, W=256, heads=1, fg_radius=40.0, audio_radius=20.0, seed=17)
+    T, H, W = w["T"], w["H"], w["W"]
+    x = adaptive_inputs(w, DEV)
+    r = run(x, T, H, W, 16, 0.8)
+    torch.cuda.synchronize()
+    q64, k64, v64 = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    codes, ind = A.zone_shapes(v64, f64(x["a"]), T, H, W)
+    assert len(codes) == 1536 and len(set(ind["volume"].tolist())) == 3
+    np.testing.assert_array_equal(r["zone_shape"].cpu().numpy().astype(np.int64), codes)
+    tb, nb = expected_tile_blocks(codes)
+    np.testing.assert_array_equal(r["tile_block"].cpu().numpy(), tb)
+    blocks, _ = A.adaptive_block_tokens(T, H, W, codes)
+    P = B.block_probs(A.ragged_means(q64, blocks), A.ragged_means(k64, blocks))
+    m_ref, c_ref, _ = B.select_blocks(P, 16, 0.8)
+    np.testing.assert_array_equal(unpack_rows(r["sel_mask"], len(tb)), m_ref[:, tb][:, :, tb])
+    np.testing.assert_array_equal(r["sel_count"].cpu().numpy(), c_ref[:, tb])
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, 4, replace=False)]))
+    out = A.ragged_sparse_attention(q64, k64, v64, blocks, m_ref, query_blocks=sample)
+    o64 = f64(r["o"])
+    err = max(float(np.max(np.abs(o64[blocks[i], hi] - o))) for (hi, i), o in out.items())
+    print("blocks %d, sampled o max-abs %.3e" % (nb, err), flush=True)
     assert err <= TOL_O
 
 
