@@ -437,18 +437,24 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
             c += __popcll(__ballot(P[r] == t));
         return R.count(c);
     };
-    auto count_in = [&](double lo, double hi) {
-        int c = 0;
-#pragma unroll
-        for (int r = 0; r < EM; ++r)
-            c += __popcll(__ballot(P[r] >= lo && P[r] < hi));
-        return R.count(c);
-    };
     auto sum_ge = [&](double t) {
         double x = 0.0;
 #pragma unroll
         for (int r = 0; r < EM; ++r)
             if (P[r] >= t) x += P[r];
+        return R.sum(x);
+    };
+    // sum and count of P >= t in one pass (the count from the compare masks)
+    auto sum_count_ge = [&](double t, int& cnt) {
+        double x = 0.0;
+        int c = 0;
+#pragma unroll
+        for (int r = 0; r < EM; ++r) {
+            const bool ge = P[r] >= t;
+            c += __popcll(__ballot(ge));
+            if (ge) x += P[r];
+        }
+        cnt = R.count(c);
         return R.sum(x);
     };
     // the one value left in [lo, hi) once the bisection stops
@@ -475,12 +481,16 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
             n_p = 1;
         } else {
             uint64_t lo = 0, hi = kInf;   // sum(P >= lo) >= p > sum(P >= hi)
-            while (hi - lo > 1 && count_in(key_value(lo), key_value(hi)) > 1) {
+            // count(P >= lo) and count(P >= hi): their difference is the
+            // number of elements left in [lo, hi)
+            int c_lo = nv, c_hi = 0;
+            while (hi - lo > 1 && c_lo - c_hi > 1) {
                 const uint64_t mid = lo + ((hi - lo) >> 1);
-                if (sum_ge(key_value(mid)) >= top_p)
-                    lo = mid;
+                int c;
+                if (sum_count_ge(key_value(mid), c) >= top_p)
+                    lo = mid, c_lo = c;
                 else
-                    hi = mid;
+                    hi = mid, c_hi = c;
             }
             vp = value_in(key_value(lo), key_value(hi));
             // within the run of elements equal to vp, in id order
@@ -504,12 +514,14 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
     int mk = 0;
     if (kk > 0 && kk < nv) {
         uint64_t lo = 0, hi = kInf;   // count(P >= lo) >= k > count(P >= hi)
-        while (hi - lo > 1 && count_in(key_value(lo), key_value(hi)) > 1) {
+        int c_lo = nv, c_hi = 0;
+        while (hi - lo > 1 && c_lo - c_hi > 1) {
             const uint64_t mid = lo + ((hi - lo) >> 1);
-            if (count_ge(key_value(mid)) >= kk)
-                lo = mid;
+            const int c = count_ge(key_value(mid));
+            if (c >= kk)
+                lo = mid, c_lo = c;
             else
-                hi = mid;
+                hi = mid, c_hi = c;
         }
         vk = value_in(key_value(lo), key_value(hi));
         mk = kk - count_ge(key_value(value_key(vk) + 1));
