@@ -582,9 +582,11 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
 
 // One 32-key half KB of a staged 64-key tile for the wave's 32 queries:
 // S^T = K_KB Q^T (8 MFMAs), the online softmax against the reference maximum,
-// O^T += V_KB^T P^T (8 MFMAs).  The steps, key order and rounding points of
-// tile_step, on half its registers: with 16 waves per workgroup a wave has
-// 128.  lo is the lane's StreamTile offset.
+// O^T += V_KB^T P^T (8 MFMAs).  The steps and key order of tile_step (exp2
+// against the reference maximum, P and its row sums in fp16, fp32
+// accumulation), with the lazy rescale checked per half, on half the
+// registers: with 16 waves per workgroup a wave has 128.  lo is the lane's
+// StreamTile offset.
 template <int HD, int KB>
 __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, int lo, const bf16x8 (&qf)[HD / 16],
                                                SoftmaxState<HD, 1>& st, float scale_log2) {
