@@ -389,10 +389,11 @@ mmdit_status mmdit_block_sparse_attn_adaptive(const void* q, const void* k, cons
  * q, k, v, T, H, W, heads, head_dim and softmax_scale as passed to the
  * forward; o and lse (required) are its outputs, zone_shape [T*H*W/512] and
  * sel_mask (tile level) likewise.  d_o [T*H*W][heads][head_dim] bf16; dq, dk,
- * dv fp32, written, 16-byte aligned, overlapping nothing.  The inputs are
- * permuted to the tile order of the forward's blocks, the uniform sparse
- * backward runs on them, and the gradients are permuted back (about 25 GB of
- * extra traffic at 172032 tokens x 24 x 128).  Deterministic.  Workspace:
+ * dv fp32, written, 16-byte aligned, overlapping nothing.  The uniform sparse
+ * backward's passes run over the forward's 64-token tiles, each tile's tokens
+ * found in place in the raster tensors from its first token and shape (a
+ * tile table built from zone_shape); nothing is permuted.  Deterministic.
+ * Workspace:
  * mmdit_workspace_bytes(MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, T*H*W, 0,
  * heads, head_dim, MMDIT_BF16, NULL). */
 mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,

@@ -542,10 +542,10 @@ SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) 
     return p;
 }
 
-// Adaptive-shape backward: the token map of the tile order, the inputs and
-// gradients permuted to it, then the uniform backward's workspace.
+// Adaptive-shape backward: the tile table (first token and log2 edges of
+// every 64-token tile), then the uniform backward's workspace over the tiles.
 struct AdaptiveBwdPlan {
-    size_t off_map, off_q, off_k, off_v, off_do, off_o, off_lse, off_dq, off_dk, off_dv, off_bwd, total;
+    size_t off_tbase, off_tdim, off_bwd, total;
     SparseBwdPlan bwd;
 };
 
@@ -557,30 +557,22 @@ AdaptiveBwdPlan plan_adaptive_bwd(int64_t n, int32_t heads, int32_t hd) {
         off += align256(bytes);
         return o;
     };
-    const size_t hb = (size_t)n * heads * hd * 2, fb = hb * 2;
-    p.off_map = take((size_t)n * 4);
-    p.off_q = take(hb);
-    p.off_k = take(hb);
-    p.off_v = take(hb);
-    p.off_do = take(hb);
-    p.off_o = take(fb);
-    p.off_lse = take((size_t)n * heads * 4);
-    p.off_dq = take(fb);
-    p.off_dk = take(fb);
-    p.off_dv = take(fb);
+    p.off_tbase = take((size_t)(n / kTileN) * 4);
+    p.off_tdim = take((size_t)(n / kTileN));
     p.bwd = plan_sparse_bwd(n, n / kTileN, heads, hd);
     p.off_bwd = take(p.bwd.total);
     p.total = off;
     return p;
 }
 
-// The kernels of a block-sparse backward over the plan's geometry.
-mmdit_status run_sparse_bwd(const SparsePlan& p, const SparseBwdPlan& bp, const void* q, const void* k,
+// The kernels of a block-sparse backward over geometry g: uniform blocks, or
+// (tbase, tdim set) the content-adaptive tiles of the grid.
+mmdit_status run_sparse_bwd(const SparseGeom& g, const SparseBwdPlan& bp, const void* q, const void* k,
                             const void* v, const float* o, const float* lse, const void* d_o,
-                            const uint32_t* sel_mask, float* dq, float* dk, float* dv, double softmax_scale, char* w,
-                            hipStream_t s, const char* who) {
-    const int64_t n = (int64_t)p.g.T * p.g.H * p.g.W;
-    const int heads = p.g.heads;
+                            const uint32_t* sel_mask, float* dq, float* dk, float* dv, double softmax_scale,
+                            const int32_t* tbase, const uint8_t* tdim, char* w, hipStream_t s, const char* who) {
+    const int64_t n = (int64_t)g.T * g.H * g.W;
+    const int heads = g.heads;
     const int head_dim = 128;
     SparseBwdArgs a{};
     a.q = (const __bf16*)q;
@@ -597,16 +589,18 @@ mmdit_status run_sparse_bwd(const SparsePlan& p, const SparseBwdPlan& bp, const 
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    a.tbase = tbase;
+    a.tdim = tdim;
     a.scale = (float)softmax_scale;
     a.scale_log2 = (float)(softmax_scale * 1.4426950408889634);
     hipError_t e;
     if ((e = launch_bwd_rowterm(o, d_o, MMDIT_BF16, lse, n, n, heads, head_dim, (float*)a.dd, (float*)a.ls2, s)) !=
             hipSuccess ||
-        (e = launch_block_timg(p.g, a.q, (__bf16*)a.qt_img, s)) != hipSuccess ||
-        (e = launch_block_timg(p.g, a.d_o, (__bf16*)a.dot_img, s)) != hipSuccess ||
-        (e = launch_block_timg(p.g, a.k, (__bf16*)a.kt_img, s)) != hipSuccess ||
-        (e = launch_mask_transpose(p.g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
-        (e = launch_sparse_bwd(p.g, a, s)) != hipSuccess)
+        (e = launch_block_timg(g, a.q, (__bf16*)a.qt_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_timg(g, a.d_o, (__bf16*)a.dot_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_timg(g, a.k, (__bf16*)a.kt_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_mask_transpose(g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
+        (e = launch_sparse_bwd(g, a, s)) != hipSuccess)
         return hip_fail(e, who);
     return MMDIT_OK;
 }
@@ -1106,8 +1100,8 @@ mmdit_status mmdit_block_sparse_attn_bwd(const void* q, const void* k, const voi
     }
     const SparseBwdPlan bp = plan_sparse_bwd(n, nb, heads, head_dim);
     if ((st = check_ws(ws, ws_bytes, bp.total, who)) != MMDIT_OK) return st;
-    return run_sparse_bwd(p, bp, q, k, v, o, lse, d_o, sel_mask, dq, dk, dv, softmax_scale, (char*)ws,
-                          (hipStream_t)stream, who);
+    return run_sparse_bwd(p.g, bp, q, k, v, o, lse, d_o, sel_mask, dq, dk, dv, softmax_scale, nullptr, nullptr,
+                          (char*)ws, (hipStream_t)stream, who);
 }
 
 mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, const void* v, int32_t T, int32_t H,
@@ -1160,39 +1154,20 @@ mmdit_status mmdit_block_sparse_attn_adaptive_bwd(const void* q, const void* k, 
     if ((st = check_ws(ws, ws_bytes, ap.total, who)) != MMDIT_OK) return st;
     char* w = (char*)ws;
     hipStream_t s = (hipStream_t)stream;
-    // tile order of the grid the forward chose, then the inputs in that order
+    // the grid and the tiles of the shapes the forward chose; the backward
+    // reads and writes the raster tensors in place
     SparseGeom grid{};
     grid.T = T, grid.H = H, grid.W = W;
     grid.nzh = H / kZoneEdge, grid.nzw = W / kZoneEdge;
     grid.nb = (int32_t)nb;
     grid.heads = heads;
-    int32_t* tokmap = (int32_t*)(w + ap.off_map);
-    char* qp = w + ap.off_q;
-    char* kp = w + ap.off_k;
-    char* vp = w + ap.off_v;
-    char* gp = w + ap.off_do;
-    char* op = w + ap.off_o;
-    float* lp = (float*)(w + ap.off_lse);
-    float* gq = (float*)(w + ap.off_dq);
-    float* gk = (float*)(w + ap.off_dk);
-    float* gv = (float*)(w + ap.off_dv);
-    const int64_t rbh = (int64_t)heads * head_dim * 2, rbf = rbh * 2;
+    int32_t* tbase = (int32_t*)(w + ap.off_tbase);
+    uint8_t* tdim = (uint8_t*)(w + ap.off_tdim);
     hipError_t e;
-    if ((e = launch_tile_token_map(grid, zone_shape, tokmap, s)) != hipSuccess ||
-        (e = launch_permute_rows(q, qp, tokmap, n, rbh, true, s)) != hipSuccess ||
-        (e = launch_permute_rows(k, kp, tokmap, n, rbh, true, s)) != hipSuccess ||
-        (e = launch_permute_rows(v, vp, tokmap, n, rbh, true, s)) != hipSuccess ||
-        (e = launch_permute_rows(d_o, gp, tokmap, n, rbh, true, s)) != hipSuccess ||
-        (e = launch_permute_rows(o, op, tokmap, n, rbf, true, s)) != hipSuccess ||
-        (e = launch_permute_cols(lse, lp, tokmap, n, heads, s)) != hipSuccess)
-        return hip_fail(e, who);
-    st = run_sparse_bwd(p, ap.bwd, qp, kp, vp, (const float*)op, lp, gp, sel_mask, gq, gk, gv, softmax_scale,
+    if ((e = launch_tile_table(grid, zone_shape, tbase, tdim, s)) != hipSuccess) return hip_fail(e, who);
+    st = run_sparse_bwd(grid, ap.bwd, q, k, v, o, lse, d_o, sel_mask, dq, dk, dv, softmax_scale, tbase, tdim,
                         w + ap.off_bwd, s, who);
     if (st != MMDIT_OK) return st;
-    if ((e = launch_permute_rows(gq, dq, tokmap, n, rbf, false, s)) != hipSuccess ||
-        (e = launch_permute_rows(gk, dk, tokmap, n, rbf, false, s)) != hipSuccess ||
-        (e = launch_permute_rows(gv, dv, tokmap, n, rbf, false, s)) != hipSuccess)
-        return hip_fail(e, who);
     return MMDIT_OK;
 }
 

@@ -245,42 +245,18 @@ __global__ __launch_bounds__(1024) void zone_shapes_kernel(SparseGeom g, int chu
     }
 }
 
-// Raster token of every position of the tile order: tokmap[64 s + r] is
-// local token r of tile s.  One workgroup of 64 threads per tile.  Codes
-// outside 0..15 are clamped (they come from a forward call of this library).
-__global__ __launch_bounds__(64) void tile_token_map_kernel(SparseGeom g, const uint8_t* __restrict__ codes,
-                                                            int32_t* __restrict__ tokmap) {
-    const int s = blockIdx.x, r = threadIdx.x;
-    const int code = min((int)codes[s / kZoneTiles], 15);
-    const TileGeom tg = tile_geom(g, s, code);
-    tokmap[(int64_t)s * kTileN + r] = (int32_t)(tg.base + tile_local(g, tg.dims, r));
+// First raster token and log2 edges of every tile: one thread per tile.
+// Codes outside 0..15 are clamped (they come from a forward call of this
+// library).
+__global__ __launch_bounds__(256) void tile_table_kernel(SparseGeom g, const uint8_t* __restrict__ codes,
+                                                         int32_t* __restrict__ tbase, uint8_t* __restrict__ tdim) {
+    const int s = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (s >= g.nb) return;
+    const TileGeom tg = tile_geom(g, s, min((int)codes[s / kZoneTiles], 15));
+    tbase[s] = (int32_t)tg.base;
+    tdim[s] = (uint8_t)tg.dims;
 }
 
-// Rows of row_bytes bytes (a multiple of 16): gather (dst[p] = src[tokmap[p]])
-// or scatter (dst[tokmap[p]] = src[p]).  One workgroup per 8 rows.
-__global__ __launch_bounds__(256) void permute_rows_kernel(const char* __restrict__ src, char* __restrict__ dst,
-                                                           const int32_t* __restrict__ tokmap, int64_t n,
-                                                           int64_t row_bytes, int gather) {
-    const int64_t chunks = row_bytes / 16;
-    for (int64_t i = threadIdx.x; i < 8 * chunks; i += 256) {
-        const int64_t p = (int64_t)blockIdx.x * 8 + i / chunks;
-        if (p >= n) break;
-        const int64_t c = i - (i / chunks) * chunks;
-        const int64_t t = tokmap[p];
-        const int64_t from = gather ? t : p, to = gather ? p : t;
-        *reinterpret_cast<uint4*>(dst + to * row_bytes + c * 16) =
-            *reinterpret_cast<const uint4*>(src + from * row_bytes + c * 16);
-    }
-}
-
-// dst[h][p] = src[h][tokmap[p]] for [heads][n] fp32.
-__global__ __launch_bounds__(256) void permute_cols_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                           const int32_t* __restrict__ tokmap, int64_t n) {
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (p >= n) return;
-    const int64_t h = blockIdx.y;
-    dst[h * n + p] = src[h * n + tokmap[p]];
-}
 
 // out[t] = sqrt(sum_c x[t][c]^2), one workgroup of 256 threads per token,
 // float4 loads, fp32 sums in a fixed tree order.
@@ -306,26 +282,6 @@ __global__ __launch_bounds__(256) void token_norms_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_tile_token_map(const SparseGeom& g, const uint8_t* codes, int32_t* tokmap, hipStream_t s) {
-    hipLaunchKernelGGL(tile_token_map_kernel, dim3(g.nb), dim3(kTileN), 0, s, g, codes, tokmap);
-    return hipGetLastError();
-}
-
-hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* tokmap, int64_t n, int64_t row_bytes,
-                               bool gather, hipStream_t s) {
-    if (row_bytes % 16) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(permute_rows_kernel, dim3((uint32_t)((n + 7) / 8)), dim3(256), 0, s, (const char*)src,
-                       (char*)dst, tokmap, n, row_bytes, gather ? 1 : 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_permute_cols(const float* src, float* dst, const int32_t* tokmap, int64_t n, int heads,
-                               hipStream_t s) {
-    hipLaunchKernelGGL(permute_cols_kernel, dim3((uint32_t)((n + 255) / 256), heads), dim3(256), 0, s, src, dst,
-                       tokmap, n);
-    return hipGetLastError();
-}
-
 hipError_t launch_token_norms(const float* x, int64_t n, int64_t width, float* out, hipStream_t s) {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(token_norms_kernel, dim3((uint32_t)n), dim3(256), 0, s, x, width, out);
@@ -333,6 +289,13 @@ hipError_t launch_token_norms(const float* x, int64_t n, int64_t width, float* o
 }
 
 int zone_stat_chunks(int heads, int hd) { return (heads * hd / 2 + kStatPairs - 1) / kStatPairs; }
+
+hipError_t launch_tile_table(const SparseGeom& g, const uint8_t* codes, int32_t* tbase, uint8_t* tdim,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(tile_table_kernel, dim3((unsigned)((g.nb + 255) / 256)), dim3(256), 0, s, g, codes, tbase,
+                       tdim);
+    return hipGetLastError();
+}
 
 hipError_t launch_zone_stats(const SparseGeom& g, const __bf16* v, const float* a, int hd, const AdaptiveWs& w,
                              hipStream_t s) {

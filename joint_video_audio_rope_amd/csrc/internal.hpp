@@ -369,15 +369,10 @@ hipError_t launch_zone_stats(const SparseGeom& g, const __bf16* v, const float* 
                              hipStream_t s);
 hipError_t launch_zone_shapes(const SparseGeom& g, int hd, const AdaptiveWs& w, hipStream_t s);
 int zone_stat_chunks(int heads, int hd);
-// Tile order of an adaptive grid (from the zone shape codes of a forward
-// call): tokmap[64 s + r] = raster token of local token r of tile s.
-hipError_t launch_tile_token_map(const SparseGeom& g, const uint8_t* codes, int32_t* tokmap, hipStream_t s);
-// Row permutation by tokmap: gather dst[p] = src[tokmap[p]], scatter dst[tokmap[p]] = src[p].
-hipError_t launch_permute_rows(const void* src, void* dst, const int32_t* tokmap, int64_t n, int64_t row_bytes,
-                               bool gather, hipStream_t s);
-// [heads][n] fp32: dst[h][p] = src[h][tokmap[p]].
-hipError_t launch_permute_cols(const float* src, float* dst, const int32_t* tokmap, int64_t n, int heads,
-                               hipStream_t s);
+// Per tile of the tiling the zone shape codes of a forward call define: its
+// first raster token and log2 edges.
+hipError_t launch_tile_table(const SparseGeom& g, const uint8_t* codes, int32_t* tbase, uint8_t* tdim,
+                             hipStream_t s);
 // out[t] = ||x[t][0 .. width)||_2 for t < n; width a multiple of 4.
 hipError_t launch_token_norms(const float* x, int64_t n, int64_t width, float* out, hipStream_t s);
 
@@ -397,11 +392,17 @@ struct SparseBwdArgs {
     float* dq;               // [n][heads][hd]
     float* dk;
     float* dv;
+    // Content-adaptive tiles (null for uniform blocks): "blocks" are then the
+    // 64-token tiles, tile j's local token r is raster token tbase[j] +
+    // tile_local(g, tdim[j], r), and g holds the grid (T, H, W, nb tiles).
+    const int32_t* tbase;
+    const uint8_t* tdim;
     float scale;
     float scale_log2;
 };
 
-hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, hipStream_t s);
+hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
+                             const uint8_t* tdim, hipStream_t s);
 hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint32_t* maskt, hipStream_t s);
 hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s);
 

@@ -26,7 +26,9 @@
 // layout by the copies: each lane's copy fetches the 16-byte chunk of the
 // token that belongs at its LDS position.  Walks are synchronous (one
 // workgroup barrier per tile, double-buffered copies); a wave whose block did
-// not select the tile skips its products.
+// not select the tile skips its products.  With content-adaptive tiles
+// (SparseBwdArgs::tdim set) the same passes run over the 64-token tiles, each
+// tile's tokens found from its first token and shape.
 #include "attn_core.hpp"
 
 namespace mmdit {
@@ -52,22 +54,28 @@ __device__ __forceinline__ int block_off(const SparseGeom& g, int r) {
     return (a * g.H + b) * g.W + c;
 }
 
+// Raster token of local token r of block (or adaptive tile) j.
+__device__ __forceinline__ int64_t bwd_token(const SparseGeom& g, const int32_t* tbase, const uint8_t* tdim, int j,
+                                             int r) {
+    return tdim ? (int64_t)tbase[j] + tile_local(g, tdim[j], r) : block_token(g, j, 0) + block_off(g, r);
+}
+
 // One workgroup per (block, head): the block's 64 tokens of src, transposed
 // to [HD][64] bf16 and laid out as the LDS image of a transposed tile (chunk
 // u of the image holds (d, c) = v_at(u): tokens 8c .. 8c + 7 of row d).  The
 // 16-bit values move as halves of 32-bit words.
 template <int HD>
 __global__ __launch_bounds__(256) void block_timg_kernel(SparseGeom g, const __bf16* __restrict__ src,
-                                                         __bf16* __restrict__ dst) {
+                                                         __bf16* __restrict__ dst, const int32_t* __restrict__ tbase,
+                                                         const uint8_t* __restrict__ tdim) {
     using L = TileLayout<HD>;
     __shared__ uint16_t tile[kTileN][HD + 2];
     const int j = blockIdx.x, head = blockIdx.y;
-    const int64_t base = block_token(g, j, 0);
     const int64_t rs = (int64_t)g.heads * HD;
     constexpr int CPR = HD / 8;
     for (int u = threadIdx.x; u < kTileN * CPR; u += 256) {
         const int r = u / CPR, c = u % CPR;
-        const int64_t tok = base + block_off(g, r);
+        const int64_t tok = bwd_token(g, tbase, tdim, j, r);
         const uint4 x = *reinterpret_cast<const uint4*>(src + tok * rs + head * HD + c * 8);
         const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -148,6 +156,16 @@ __device__ __forceinline__ void gather_rows(const char* g0, const uint32_t (&rof
     for (int i = 0; i < CK; ++i) dma16(g0 + roff[i], tile + (w * CK + i) * 1024);
 }
 
+// The same copies for an adaptive tile: this lane's copy i fetches chunk
+// rc[i] & 15 of the tile's local token rc[i] >> 4 (tile-order rows).
+template <int CK>
+__device__ __forceinline__ void gather_tile_rows(const SparseGeom& g, const char* g0, int64_t rb, uint32_t code,
+                                                 const int (&rc)[CK], char* tile, int w) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i)
+        dma16(g0 + tile_local(g, code, rc[i] >> 4) * rb + (rc[i] & 15) * 16, tile + (w * CK + i) * 1024);
+}
+
 template <int HD>
 __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, SparseBwdArgs a) {
     using L = TileLayout<HD>;
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
     const int64_t rb = rstride * 2;
     const bool own_ok = b0 + side < g.nb;
     const int qb = min(b0 + side, g.nb - 1);
-    const int64_t qtok = block_token(g, qb, 0) + block_off(g, (w & 1) * 32 + m);
+    const int64_t qtok = bwd_token(g, a.tbase, a.tdim, qb, (w & 1) * 32 + m);
     bf16x8 qr[KS], gr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -198,13 +216,16 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
     const float lq2 = a.ls2[(int64_t)head * n + qtok];
     const float dq_d = a.dd[(int64_t)head * n + qtok];
 
-    // this lane's row-tile copies: offset of the token (and chunk) it fetches
+    // this lane's row-tile copies: the tile row (local token) and chunk it
+    // fetches, and for uniform blocks their offset from the block's first row
+    int rc[CK];
     uint32_t roff[CK];
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
         int row, c;
         L::k_at((w * CK + i) * kWave + lane, row, c);
-        roff[i] = (uint32_t)(block_off(g, (row & ~31) | perm_row(row & 31)) * rb + c * 16);
+        rc[i] = ((row & ~31) | perm_row(row & 31)) << 4 | c;
+        roff[i] = a.tdim ? 0u : (uint32_t)(block_off(g, rc[i] >> 4) * rb + c * 16);
     }
     const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
     const char* vg = reinterpret_cast<const char*>(a.v + head * HD);
@@ -212,9 +233,16 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
 
     auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
     auto issue = [&](int j, char* b) {
-        const int64_t t0 = block_token(g, j, 0) * rb;
-        gather_rows<CK>(kg + t0, roff, b, w);
-        gather_rows<CK>(vg + t0, roff, b + L::kKBytes, w);
+        if (a.tdim) {
+            const int64_t t0 = (int64_t)a.tbase[j] * rb;
+            const uint32_t code = a.tdim[j];
+            gather_tile_rows<CK>(g, kg + t0, rb, code, rc, b, w);
+            gather_tile_rows<CK>(g, vg + t0, rb, code, rc, b + L::kKBytes, w);
+        } else {
+            const int64_t t0 = block_token(g, j, 0) * rb;
+            gather_rows<CK>(kg + t0, roff, b, w);
+            gather_rows<CK>(vg + t0, roff, b + L::kKBytes, w);
+        }
         const char* src = ktg + (int64_t)j * (HD * kTileN * 2);
 #pragma unroll
         for (int i = 0; i < CV; ++i)
@@ -332,7 +360,7 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
     const int64_t rb = rstride * 2;
     const bool own_ok = c0 + side < g.nb;
     const int kb_own = min(c0 + side, g.nb - 1);
-    const int64_t ktok = block_token(g, kb_own, 0) + block_off(g, (w & 1) * 32 + m);
+    const int64_t ktok = bwd_token(g, a.tbase, a.tdim, kb_own, (w & 1) * 32 + m);
     bf16x8 kr[KS], vr[DK ? KS : 1];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -340,14 +368,16 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
         if (DK) vr[ks] = load_bf16x8(a.v + ktok * rstride + head * HD + 16 * ks + 8 * hh, true);
     }
 
+    int rc[CK];
     uint32_t roff[CK];
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
         int row, c;
         L::k_at((w * CK + i) * kWave + lane, row, c);
-        roff[i] = (uint32_t)(block_off(g, (row & ~31) | perm_row(row & 31)) * rb + c * 16);
+        rc[i] = ((row & ~31) | perm_row(row & 31)) << 4 | c;
+        roff[i] = a.tdim ? 0u : (uint32_t)(block_off(g, rc[i] >> 4) * rb + c * 16);
     }
-    const int loff = block_off(g, lane);   // this lane's query of the lse / D copies
+    const int loff = a.tdim ? 0 : block_off(g, lane);   // this lane's query of the lse / D copies
     const char* qg = reinterpret_cast<const char*>(a.q + head * HD);
     const char* og = reinterpret_cast<const char*>(a.d_o + head * HD);
     const char* tg = reinterpret_cast<const char*>((DK ? a.qt_img : a.dot_img) + (int64_t)head * g.nb * (HD * kTileN)) +
@@ -357,14 +387,24 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
 
     auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
     auto issue = [&](int i, char* b) {
-        const int64_t tok0 = block_token(g, i, 0);
-        gather_rows<CK>(qg + tok0 * rb, roff, b, w);
-        if (DK) gather_rows<CK>(og + tok0 * rb, roff, b + L::kKBytes, w);
+        int64_t lt;   // raster token of this lane's query of the lse / D copies
+        if (a.tdim) {
+            const int64_t tok0 = a.tbase[i];
+            const uint32_t code = a.tdim[i];
+            gather_tile_rows<CK>(g, qg + tok0 * rb, rb, code, rc, b, w);
+            if (DK) gather_tile_rows<CK>(g, og + tok0 * rb, rb, code, rc, b + L::kKBytes, w);
+            lt = tok0 + tile_local(g, code, lane);
+        } else {
+            const int64_t tok0 = block_token(g, i, 0);
+            gather_rows<CK>(qg + tok0 * rb, roff, b, w);
+            if (DK) gather_rows<CK>(og + tok0 * rb, roff, b + L::kKBytes, w);
+            lt = tok0 + loff;
+        }
         const char* src = tg + (int64_t)i * (HD * kTileN * 2);
 #pragma unroll
         for (int c = 0; c < CV; ++c) dma16(src + (w * CV + c) * 1024, b + kOffT + (w * CV + c) * 1024);
-        if (w == 0) dma4(lsg + tok0 + loff, b + kOffL);
-        if (DK && w == 1) dma4(ddg + tok0 + loff, b + kOffL + kTileN * 4);
+        if (w == 0) dma4(lsg + lt, b + kOffL);
+        if (DK && w == 1) dma4(ddg + lt, b + kOffL + kTileN * 4);
     };
 
     FragAddr<HD> fa;
@@ -451,8 +491,9 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, hipStream_t s) {
-    hipLaunchKernelGGL(block_timg_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, src, dst);
+hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
+                             const uint8_t* tdim, hipStream_t s) {
+    hipLaunchKernelGGL(block_timg_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, src, dst, tbase, tdim);
     return hipGetLastError();
 }
 

@@ -386,9 +386,12 @@ def test_adaptive_bwd_workspace_plan():
     hb = n * h * 128 * 2
     uniform_bwd = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, 128, J.MMDIT_BF16,
                                           J.sparse_desc())
-    want = a256(n * 4) + 4 * a256(hb) + a256(2 * hb) + a256(n * h * 4) + 3 * a256(2 * hb) + a256(uniform_bwd)
+    # the tile table (first token int32, log2 edges uint8 per 64-token tile)
+    # and the uniform backward's workspace over the tiles: no permuted copies
+    want = a256(nb * 4) + a256(nb) + a256(uniform_bwd)
     need = J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_ADAPTIVE_BWD, n, 0, h, 128, J.MMDIT_BF16, None)
     assert need == want
+    assert need < uniform_bwd + hb
     assert _adaptive_bwd_call(ws_bytes=need - 1) == L.MMDIT_ERR_WORKSPACE
 
 
