@@ -587,17 +587,41 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
 // accumulation), with the lazy rescale checked per half, on half the
 // registers: with 16 waves per workgroup a wave has 128.  lo is the lane's
 // StreamTile offset.
+//
+// Each LDS fragment is read two MFMAs ahead of its use, in two alternating
+// registers.  Left to itself the scheduler issued every K fragment read just
+// before its MFMA and waited for it (lgkmcnt(0)), so a wave paid the LDS
+// latency once per product; with few of a SIMD's waves selecting a tile,
+// nothing hid it.  The QK phase's order is therefore pinned with
+// sched_group_barrier: on the 24 x 64 x 112 grid the call went from 131.5 to
+// 125.6 ms (results bitwise identical).  Three ahead no longer fits: the
+// register allocator then spills Q fragments inside the walk.
 template <int HD, int KB>
 __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, int lo, const bf16x8 (&qf)[HD / 16],
                                                SoftmaxState<HD, 1>& st, float scale_log2) {
     using L = StreamTile<HD>;
     constexpr int NK = HD / 16;   // MFMA steps over d
+    constexpr int PD = 2;         // fragments read ahead
+    constexpr int kMfma = 0x008, kDsRead = 0x100;   // sched_group_barrier instruction classes
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    bf16x8 kf[PD];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(L::k_frag(tile, lo, ks, KB), qf[ks], s, 0, 0, 0);
+    for (int j = 0; j < PD; ++j) kf[j] = L::k_frag(tile, lo, j, KB);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % PD], qf[ks], s, 0, 0, 0);
+        if (ks + PD < NK) kf[ks % PD] = L::k_frag(tile, lo, ks + PD, KB);
+    }
+    // order: PD reads, then (one MFMA, the next read) ..., then the last PD MFMAs
+    __builtin_amdgcn_sched_group_barrier(kDsRead, PD, 0);
+#pragma unroll
+    for (int i = 0; i < NK - PD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, PD, 0);
     float x = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
@@ -610,12 +634,19 @@ __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, in
 #pragma unroll
     for (int r = 0; r < 16; ++r)
         pf[r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, mneg));
+    // P V^T: products i = (key group u, row block db), V^T fragments PD ahead
+    // (the scheduler keeps this order by itself and issues the first reads
+    // during the exponentials)
+    constexpr int NV = 2 * (HD / 32);
+    f16x8 vf[PD];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int j = 0; j < PD; ++j) vf[j] = L::v_frag(tile, lo, j % (HD / 32), 2 * KB + j / (HD / 32));
 #pragma unroll
-        for (int db = 0; db < HD / 32; ++db)
-            st.o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(L::v_frag(tile, lo, db, 2 * KB + u), pf[u],
-                                                                 st.o[0][db], 0, 0, 0);
+    for (int i = 0; i < NV; ++i) {
+        st.o[0][i % (HD / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i % PD], pf[i / (HD / 32)],
+                                                                        st.o[0][i % (HD / 32)], 0, 0, 0);
+        if (i + PD < NV) vf[i % PD] = L::v_frag(tile, lo, (i + PD) % (HD / 32), 2 * KB + (i + PD) / (HD / 32));
+    }
     const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
     float ls = 0.f;
 #pragma unroll
