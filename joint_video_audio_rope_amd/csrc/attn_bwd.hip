@@ -232,16 +232,33 @@ void bwd_key_kernel(BwdArgs a) {
         const char* lt = lq + kOffT;
         const float* lls = reinterpret_cast<const float*>(lq + kOffL);
         const float* ldd = lls + kTileN;
+        // One stream of LDS fragments over both query halves, read two
+        // products ahead: per half the S (and dP) operands, ks-major, then
+        // the transposed-tile operands of dV^T / dK^T.
+        constexpr int PD = 2;
+        constexpr int NA = (DK ? 2 : 1) * KS, NQ = NA + 2 * DB, NT = 2 * NQ;
+        auto frag = [&](int i) -> bf16x8 {
+            const int qb = i / NQ, u = i % NQ;
+            if (u < NA) return k_frag<HD>((DK && (u & 1)) ? lo : lq, fa, 2 * (DK ? u >> 1 : u) + qb);
+            const int c = u - NA;   // product (db, g) = (c / 2, c % 2)
+            return t_frag<HD>(lt, fa, 4 * (c >> 1) + 2 * qb + (c & 1));
+        };
+        bf16x8 fr[PD];
+#pragma unroll
+        for (int j = 0; j < PD; ++j) fr[j] = frag(j);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             f32x16 s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lq, fa, 2 * ks + qb), kr[ks], s, 0, 0, 0);
-                if (DK)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lo, fa, 2 * ks + qb), vr[ks], dp, 0, 0, 0);
+            for (int u = 0; u < NA; ++u) {
+                const int i = qb * NQ + u, ks = DK ? u >> 1 : u;
+                if (DK && (u & 1))
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], vr[ks], dp, 0, 0, 0);
+                else
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], kr[ks], s, 0, 0, 0);
+                fr[i % PD] = frag(i + PD);
             }
             // register r holds query 32 qb + 16 (r / 8) + 8 hh + r % 8 of the tile
             bf16x8 xb[2];
@@ -265,12 +282,14 @@ void bwd_key_kernel(BwdArgs a) {
                     }
                 }
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag<HD>(lt, fa, 4 * db + 2 * qb + g), xb[g],
-                                                                      acc[db], 0, 0, 0);
+            for (int c = 0; c < 2 * DB; ++c) {
+                const int i = qb * NQ + NA + c;
+                acc[c >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], xb[c & 1], acc[c >> 1], 0, 0, 0);
+                if (i + PD < NT) fr[i % PD] = frag(i + PD);
+            }
         }
+        // the half's lse (and D) reads join the stream before its dV^T / dK^T products
+        order_fragment_stream<PD, NT, NQ, NA - 1, DK ? 8 : 4>();
         wait_dma();
         __syncthreads();
     }
@@ -383,17 +402,31 @@ __global__ __launch_bounds__(kBwdDqWaves * kWave) void bwd_dq_kernel(BwdArgs a) 
         const char* lk = buf(t);
         const char* lv = lk + L::kKBytes;
         const char* lkt = lk + 2 * L::kKBytes;
+        // One stream of LDS fragments read two products ahead: the S^T and
+        // dP^T operands (i = 2 KS kb + 2 ks + {0: K, 1: V}), then the K^T
+        // operands of dQ^T (i = NA + 4 db + g).
+        constexpr int PD = 2;
+        constexpr int NA = 4 * KS, NT = NA + 4 * DB;
+        auto frag = [&](int i) -> bf16x8 {
+            if (i < NA) return k_frag<HD>((i & 1) ? lv : lk, fa, 2 * ((i >> 1) % KS) + i / (2 * KS));
+            return t_frag<HD>(lkt, fa, i - NA);
+        };
+        bf16x8 fr[PD];
+#pragma unroll
+        for (int j = 0; j < PD; ++j) fr[j] = frag(j);
         f32x16 s[2], dp[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lk, fa, 2 * ks + kb), qr[ks], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag<HD>(lv, fa, 2 * ks + kb), gr[ks], dp[kb], 0, 0,
-                                                                 0);
-            }
+        for (int i = 0; i < NA; ++i) {
+            const int kb = i / (2 * KS), ks = (i >> 1) % KS;
+            if (i & 1)
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], gr[ks], dp[kb], 0, 0, 0);
+            else
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], qr[ks], s[kb], 0, 0, 0);
+            fr[i % PD] = frag(i + PD);
         }
         const int valid = (int)min<int64_t>(kTileN, a.n_kv - (int64_t)t * kTileN);
         bf16x8 sb[4];
@@ -406,11 +439,12 @@ __global__ __launch_bounds__(kBwdDqWaves * kWave) void bwd_dq_kernel(BwdArgs a) 
                 sb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dp[kb][r] - dq_d));
             }
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t_frag<HD>(lkt, fa, 4 * db + g), sb[g], dqt[db], 0,
-                                                                  0, 0);
+        for (int c = 0; c < 4 * DB; ++c) {
+            const int i = NA + c;
+            dqt[c >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % PD], sb[c & 3], dqt[c >> 2], 0, 0, 0);
+            if (i + PD < NT) fr[i % PD] = frag(i + PD);
+        }
+        order_fragment_stream<PD, NT>();
         wait_dma();
         __syncthreads();
     }

@@ -137,6 +137,27 @@ __device__ __forceinline__ f16x8 v_frag(const char* lv, const FragAddr<HD>& fa, 
     return *reinterpret_cast<const f16x8*>(lv + fa.v[i & 3] + (i >> 2) * 32 * TileLayout<HD>::kVRowBytes);
 }
 
+// Instruction order for a chain of N MFMAs whose LDS fragments are read PD
+// products ahead into PD alternating registers: PD reads, then (one MFMA,
+// the next read) N - PD times, then the last PD MFMAs.  Left alone, the
+// scheduler tends to issue each read right before its product and wait for
+// it (lgkmcnt(0)), so the wave pays the LDS latency once per MFMA.  EXTRA
+// further LDS reads of the region (say row statistics) join after pair i
+// whenever i % PERIOD == AT.  Call once, after the code of the region it
+// orders (a basic block; the groups are matched against its instructions).
+template <int PD, int N, int PERIOD = 1, int AT = 0, int EXTRA = 0>
+__device__ __forceinline__ void order_fragment_stream() {
+    constexpr int kMfma = 0x008, kDsRead = 0x100;   // sched_group_barrier instruction classes
+    __builtin_amdgcn_sched_group_barrier(kDsRead, PD, 0);
+#pragma unroll
+    for (int i = 0; i < N - PD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        if (EXTRA > 0 && i % PERIOD == AT) __builtin_amdgcn_sched_group_barrier(kDsRead, EXTRA, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, PD, 0);
+}
+
 // Scores S^T = K Q^T of one tile (not overlapped; the first tile of a walk).
 // Each K fragment read from LDS feeds the QB query blocks.
 template <int HD, int QB>

@@ -602,7 +602,6 @@ __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, in
     using L = StreamTile<HD>;
     constexpr int NK = HD / 16;   // MFMA steps over d
     constexpr int PD = 2;         // fragments read ahead
-    constexpr int kMfma = 0x008, kDsRead = 0x100;   // sched_group_barrier instruction classes
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -614,14 +613,7 @@ __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, in
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % PD], qf[ks], s, 0, 0, 0);
         if (ks + PD < NK) kf[ks % PD] = L::k_frag(tile, lo, ks + PD, KB);
     }
-    // order: PD reads, then (one MFMA, the next read) ..., then the last PD MFMAs
-    __builtin_amdgcn_sched_group_barrier(kDsRead, PD, 0);
-#pragma unroll
-    for (int i = 0; i < NK - PD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kMfma, PD, 0);
+    order_fragment_stream<PD, NK>();
     float x = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
