@@ -129,6 +129,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
     constexpr int KS = HD / 16;
     constexpr int KCH = kTileN * L::kKChunks / (kWave * NW);   // K copies per wave per tile
     constexpr int VCH = HD * 8 / (kWave * NW);                 // V^T copies per wave per tile
+    constexpr bool kPin = QB == 1 && NW == 8;                   // fragment stream order pinned
     __shared__ __attribute__((aligned(16))) char lds[2 * L::kBytes];
 
     const int total = a.q_tiles * a.heads * a.splits;
@@ -273,13 +274,13 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
     int t = tile0;
     for (; t + 1 < main_end; t += 2) {
         top(t, 0);
-        tile_step<HD, QB, true, false>(kbuf(1), vbuf(0), fa, qf, sa, sb, st, a.scale_log2, kTileN, mx);
+        tile_step<HD, QB, true, false, kPin>(kbuf(1), vbuf(0), fa, qf, sa, sb, st, a.scale_log2, kTileN, mx);
         top(t + 1, 1);
-        tile_step<HD, QB, true, false>(kbuf(0), vbuf(1), fa, qf, sb, sa, st, a.scale_log2, kTileN, mx);
+        tile_step<HD, QB, true, false, kPin>(kbuf(0), vbuf(1), fa, qf, sb, sa, st, a.scale_log2, kTileN, mx);
     }
     if (t < main_end) {
         top(t, (t - tile0) & 1);
-        tile_step<HD, QB, true, false>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+        tile_step<HD, QB, true, false, kPin>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
                                        st, a.scale_log2, kTileN, mx);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -289,7 +290,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
     }
     if (t + 1 < tile1) {   // the next tile is the partial last one
         top(t, (t - tile0) & 1);
-        tile_step<HD, QB, true, true>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
+        tile_step<HD, QB, true, true, kPin>(kbuf((t + 1 - tile0) & 1), vbuf((t - tile0) & 1), fa, qf, sa, sb,
                                       st, a.scale_log2, last_valid, mx);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -298,7 +299,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a, const RopeFuse
         ++t;
     }
     top(t, (t - tile0) & 1);
-    tile_step<HD, QB, false, false>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN,
+    tile_step<HD, QB, false, false, kPin>(nullptr, vbuf((t - tile0) & 1), fa, qf, sa, sb, st, a.scale_log2, kTileN,
                                     mx);
 
 #pragma unroll

@@ -240,11 +240,14 @@ __device__ __forceinline__ void maybe_rescale(SoftmaxState<HD, QB>& st, const fl
 //            of P(t) (fp16 pairs through v_dot2, i.e. exactly the values the
 //            MFMA consumes) and, when NEXT, the maximum of S(t+1).
 // Every fragment read from LDS feeds QB MFMAs.  Writes the scaled maximum of
-// S(t+1) per query block to mx (untouched when !NEXT).  The interleave is left
-// to the instruction scheduler: pinning it with sched_group_barrier (reads PD
-// fragments ahead, each MFMA slot with its share of the softmax) measured
-// 2.4 % slower on the 35050-token joint attention.
-template <int HD, int QB, bool NEXT, bool MASK_NEXT>
+// S(t+1) per query block to mx (untouched when !NEXT).  The vector work is
+// left to the instruction scheduler (pinning each MFMA slot with its share of
+// the softmax measured 2.4 % slower on the 35050-token joint attention).
+// With PIN (QB = 1) the LDS reads and MFMAs of both phases keep the order of
+// one fragment stream read PD ahead: 13.34 -> 13.08 ms on that attention
+// (bitwise identical); 2, 3, 5 and 6 ahead were slower.  The 4-wave kernels
+// leave it unpinned: there it spills.
+template <int HD, int QB, bool NEXT, bool MASK_NEXT, bool PIN = false>
 __device__ __forceinline__ void tile_step(const char* __restrict__ lk_next,
                                           const char* __restrict__ lv_cur, const FragAddr<HD>& fa,
                                           const bf16x8 (&qf)[QB][HD / 16], const f32x16 (&s_cur)[QB][2],
@@ -316,6 +319,10 @@ __device__ __forceinline__ void tile_step(const char* __restrict__ lk_next,
             }
         }
         if (i + PD < NF) vf[i % PD] = v_frag<HD>(lv_cur, fa, i + PD);
+    }
+    if constexpr (PIN) {
+        static_assert(QB == 1, "one MFMA per fragment");
+        order_fragment_stream<PD, NEXT ? 2 * NF : NF>();
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += ls[qb];
