@@ -299,7 +299,8 @@ mmdit_status plan_rope(const mmdit_rope_desc* d, int dtype, RopePlan* out) {
 struct SparsePlan {
     SparseGeom g{};
     int32_t chunk_rows;   // query blocks whose logits are computed and selected at once
-    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, off_vmax, total;
+    size_t off_qbar, off_kbar, off_scores, off_mask, off_count, off_base, off_vt, off_kimg, off_vmax, off_order,
+        total;
 };
 
 // Query blocks per chunk of block logits: whole 128-row tiles of the score
@@ -314,7 +315,7 @@ int32_t score_chunk_rows(int64_t nb, int32_t heads) {
 // Workspace layout of a block-sparse call (shared by the plan and the size
 // query): fp64 block means, fp64 scores, selection bitmask and counts, block
 // first tokens, per-block fp16 V^T and per-block K tile images, the partial
-// maxima of V (its prescale exponents).
+// maxima of V (its prescale exponents), the attention kernel's group order.
 void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -332,6 +333,7 @@ void sparse_layout(int64_t nb, int32_t heads, int32_t hd, SparsePlan* p) {
     p->off_vt = take((size_t)heads * nb * hd * kTileN * 2);
     p->off_kimg = take((size_t)heads * nb * hd * kTileN * 2);
     p->off_vmax = take((size_t)heads * kVmaxParts * 4);
+    p->off_order = take((size_t)heads * stream_groups(nb) * 4);
     p->total = off;
 }
 
@@ -477,6 +479,7 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
     sw.vt = (_Float16*)(w + p.off_vt);
     sw.kimg = (__bf16*)(w + p.off_kimg);
     sw.vmax = (uint32_t*)(w + p.off_vmax);
+    sw.order = (int32_t*)(w + p.off_order);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (ad) {
@@ -510,6 +513,8 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
             hipSuccess)
             return hip_fail(e, "block_sparse select");
     }
+    if ((e = launch_group_order(p.g, kStreamGroup, sw.mask, sw.order, s)) != hipSuccess)
+        return hip_fail(e, "block_sparse group order");
     if ((e = launch_sparse_attn(p.g, (const __bf16*)q, head_dim,
                                 (float)(softmax_scale * 1.4426950408889634), sw, o, lse,
                                 sp->wait_limit ? sp->wait_limit : kSpinLimit, s)) != hipSuccess)
@@ -518,10 +523,11 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
 }
 
 // Workspace of a block-sparse backward: D and lse2 [heads][n] fp32, the
-// transposed block images Q^T, dO^T, K^T [heads][nb][hd * 64] bf16, and the
-// transposed selection bitmask [heads][nb][ceil(nb/32)].
+// transposed block images Q^T, dO^T, K^T [heads][nb][hd * 64] bf16, the
+// transposed selection bitmask [heads][nb][ceil(nb/32)], and the dispatch
+// orders of the query-block and key-block groups [heads][groups] i32.
 struct SparseBwdPlan {
-    size_t off_dd, off_ls2, off_qt, off_dot, off_kt, off_maskt, total;
+    size_t off_dd, off_ls2, off_qt, off_dot, off_kt, off_maskt, off_order_q, off_order_k, total;
 };
 
 SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) {
@@ -538,6 +544,8 @@ SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) 
     p.off_dot = take((size_t)heads * nb * hd * kTileN * 2);
     p.off_kt = take((size_t)heads * nb * hd * kTileN * 2);
     p.off_maskt = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
+    p.off_order_q = take((size_t)heads * ((nb + kBwdGroup - 1) / kBwdGroup) * 4);
+    p.off_order_k = take((size_t)heads * ((nb + kBwdGroup - 1) / kBwdGroup) * 4);
     p.total = off;
     return p;
 }
@@ -591,6 +599,8 @@ mmdit_status run_sparse_bwd(const SparseGeom& g, const SparseBwdPlan& bp, const 
     a.dv = dv;
     a.tbase = tbase;
     a.tdim = tdim;
+    a.order_q = (const int32_t*)(w + bp.off_order_q);
+    a.order_k = (const int32_t*)(w + bp.off_order_k);
     a.scale = (float)softmax_scale;
     a.scale_log2 = (float)(softmax_scale * 1.4426950408889634);
     hipError_t e;
@@ -600,6 +610,8 @@ mmdit_status run_sparse_bwd(const SparseGeom& g, const SparseBwdPlan& bp, const 
         (e = launch_block_timg(g, a.d_o, (__bf16*)a.dot_img, tbase, tdim, s)) != hipSuccess ||
         (e = launch_block_timg(g, a.k, (__bf16*)a.kt_img, tbase, tdim, s)) != hipSuccess ||
         (e = launch_mask_transpose(g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
+        (e = launch_group_order(g, kBwdGroup, sel_mask, (int32_t*)a.order_q, s)) != hipSuccess ||
+        (e = launch_group_order(g, kBwdGroup, a.maskt, (int32_t*)a.order_k, s)) != hipSuccess ||
         (e = launch_sparse_bwd(g, a, s)) != hipSuccess)
         return hip_fail(e, who);
     return MMDIT_OK;

@@ -247,6 +247,19 @@ struct SparseGeom {
     int32_t heads;
 };
 
+// Query blocks per workgroup of the block-sparse attention kernel.  Measured
+// on the 24 x 64 x 112 grid (density 27.6 %), where a block selects 742 key
+// blocks on average: a group of G consecutive blocks stages the union of
+// their selections, 1488 tiles for G = 4 and 1951 for G = 7, so the gathered
+// K/V tiles per call fall from 786 GB to 589 GB and the copies alone from
+// 95 ms to 69 ms.  The consumers' compute bounds the kernel, and more waves
+// per SIMD keep more of them busy: the call went from 133.3 ms (G = 4,
+// whole-tile steps at 168 registers) to 129.4 ms (G = 7, half-tile steps at
+// 128).  With workgroup barriers per tile instead of producer waves, pairs
+// took 164 ms and groups of 4 205 ms.
+constexpr int kStreamGroup = 7;
+__host__ __device__ constexpr int64_t stream_groups(int64_t nb) { return (nb + kStreamGroup - 1) / kStreamGroup; }
+
 struct SparseWs {
     double* qbar;       // [heads][nb][hd]
     double* kbar;       // [heads][nb][hd]
@@ -257,6 +270,7 @@ struct SparseWs {
     _Float16* vt;       // [heads][nb][hd * 64]: each key block's V^T (prescaled) in LDS tile order
     __bf16* kimg;       // [heads][nb][64 * hd]: each key block's K rows in LDS tile order
     uint32_t* vmax;     // [heads][kVmaxParts] partial maxima of V (the prescale exponents)
+    int32_t* order;     // [heads][stream_groups(nb)] group ids in the attention kernel's dispatch order
     // Content-adaptive blocks (null for uniform blocks).  "Blocks" above are
     // then 64-token tiles; a block of 128 or 256 tokens is 2 or 4 consecutive
     // tiles, and base[] is filled by the shape pass.
@@ -275,6 +289,36 @@ hipError_t launch_block_scores(const SparseGeom& g, int hd, double scale, const 
                                hipStream_t s);
 hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, const SparseWs& w, int row0, int rows,
                                uint32_t* sel_mask, int32_t* sel_count, hipStream_t s);
+// Blocks per workgroup of the block-sparse backward passes (a 2 x 2 square).
+constexpr int kBwdGroup = 4;
+
+// Per head, the groups of `group` consecutive blocks (kStreamGroup or
+// kBwdGroup) ranked by an estimate of their walk's time from the bitmask rows
+// [heads][nb][ceil(nb/32)], costliest first, into order [heads][groups].
+hipError_t launch_group_order(const SparseGeom& g, int group, const uint32_t* mask, int32_t* order, hipStream_t s);
+
+// Workgroups of a walk kernel over `groups` groups per head: 8 per rank slot
+// of every head (one per XCD), head-major.
+__host__ __device__ constexpr int64_t group_workgroups(int64_t groups, int64_t heads) {
+    return 8 * ((groups + 7) / 8) * heads;
+}
+
+// The (head, group) of this workgroup: head-major, so the tiles in flight
+// stay those of one head; within a head, rank 8 j + x of the order table to
+// XCD x (blockIdx % 8) for even j and to XCD 7 - x for odd j.  False for the
+// padding workgroups past the last rank.
+__device__ __forceinline__ bool group_of_workgroup(int groups, int heads, const int32_t* order, int& head,
+                                                   int& grp) {
+    const int per = (groups + 7) >> 3;
+    const int xcd = (int)(blockIdx.x & 7);
+    const int slot = (int)(blockIdx.x >> 3);
+    head = slot / per;
+    const int j = slot - head * per;
+    const int rank = 8 * j + ((j & 1) ? 7 - xcd : xcd);
+    if (head >= heads || rank >= groups) return false;
+    grp = order[(int64_t)head * groups + rank];
+    return true;
+}
 // wait_limit: bound of each of the kernel's internal waits, in sleeps of
 // about 64 cycles (1 .. kSpinLimit).  A wait that reaches it gives up and the
 // workgroup writes NaN to its o rows and lse entries.
@@ -397,6 +441,8 @@ struct SparseBwdArgs {
     // tile_local(g, tdim[j], r), and g holds the grid (T, H, W, nb tiles).
     const int32_t* tbase;
     const uint8_t* tdim;
+    const int32_t* order_q;  // [heads][groups] dispatch order of the dQ pass's groups of query blocks
+    const int32_t* order_k;  // [heads][groups] dispatch order of the key passes' groups of key blocks
     float scale;
     float scale_log2;
 };

@@ -252,17 +252,8 @@ __global__ __launch_bounds__(256, 2) void block_scores_kernel(SparseGeom g, doub
 }
 
 constexpr int kSelWaves = 4;   // rows (one per wave) per selection workgroup of one-wave rows
-// Sparse attention: query blocks per workgroup and LDS ring depth (tiles).
-// Measured on the 24 x 64 x 112 grid (density 27.6 %), where a block selects
-// 742 key blocks on average: a group of G consecutive blocks stages the union
-// of their selections, 1488 tiles for G = 4 and 1951 for G = 7, so the
-// gathered K/V tiles per call fall from 786 GB to 589 GB and the copies alone
-// from 95 ms to 69 ms.  The consumers' compute bounds the kernel, and more
-// waves per SIMD keep more of them busy: the call went from 133.3 ms (G = 4,
-// whole-tile steps at 168 registers) to 129.4 ms (G = 7, half-tile steps at
-// 128).  With workgroup barriers per tile instead of producer waves, pairs
-// took 164 ms and groups of 4 205 ms.
-constexpr int kStreamGroup = 7;
+// Sparse attention: LDS ring depth (tiles).  The query blocks per workgroup,
+// kStreamGroup, are measured where they are declared.
 constexpr int kStreamRing = 4;
 
 // Wave-wide reductions.  The xor butterfly combines the same two partial
@@ -649,6 +640,80 @@ __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, in
     st.l_run[0] += ls;
 }
 
+// Dispatch order of the groups of a block-sparse walk kernel: G consecutive
+// blocks of one head per workgroup (the forward's kStreamGroup query
+// blocks, the backward's query or key blocks).  Workgroups go to the 8 XCDs
+// round robin in blockIdx order and each XCD runs its share in that order.
+// A fixed split of a head's groups over the XCDs leaves some XCDs more work
+// than others (by the estimate below, on the 24 x 64 x 112 grid the XCD
+// totals of the forward spread over 0.955-1.026 of their mean), and a costly
+// group dispatched last ends the kernel late.  So per head this pass ranks
+// the groups by an estimate of their time, costliest first (ties by group
+// id), and the walk kernels deal the ranks to the XCDs in a snake
+// (group_of_workgroup): rank 8 j + x to XCD x for even j, to XCD 7 - x for
+// odd j.  On that grid the forward call went from 120.4 to 117.8 ms.  The
+// estimate is 3 x (bits set in the group's rows of the bitmask) + 2 x (bits
+// in their union): a selected pair costs the products of one wave pair, a
+// union tile its copies and a step of every wave's walk.  Only the order of
+// the workgroups changes, never what any of them computes.  One workgroup
+// per head; the ranks are sorted in LDS (bitonic sort of 64-bit keys
+// ~cost << 32 | group).
+constexpr int kOrderMax = 8192;   // >= groups per head for G >= 4 and kSelMax blocks, a power of two
+static_assert(kOrderMax >= (kSelMax + 3) / 4, "order table");
+
+template <int G>
+__global__ __launch_bounds__(1024) void group_order_kernel(SparseGeom g, const uint32_t* __restrict__ mask,
+                                                           int32_t* __restrict__ order) {
+    __shared__ uint64_t key[kOrderMax];
+    const int head = blockIdx.x;
+    const int groups = (g.nb + G - 1) / G;
+    const int nw = (g.nb + 31) >> 5;
+    int n2 = 1;
+    while (n2 < groups) n2 <<= 1;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int gr = wv; gr < n2; gr += 16) {
+        uint64_t k = ~0ull;   // padding sorts last
+        if (gr < groups) {
+            const int b0 = gr * G, nbk = min(G, g.nb - b0);
+            const uint32_t* rows = mask + ((int64_t)head * g.nb + b0) * nw;
+            int uni = 0, sel = 0;
+            for (int wd = lane; wd < nw; wd += 64) {
+                uint32_t u = 0u;
+                for (int sd = 0; sd < nbk; ++sd) {
+                    const uint32_t x = rows[(int64_t)sd * nw + wd];
+                    u |= x;
+                    sel += __popc(x);
+                }
+                uni += __popc(u);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                uni += __shfl_xor(uni, o);
+                sel += __shfl_xor(sel, o);
+            }
+            const uint32_t cost = 3u * (uint32_t)sel + 2u * (uint32_t)uni;
+            k = ((uint64_t)(~cost) << 32) | (uint32_t)gr;
+        }
+        if (lane == 0) key[gr] = k;
+    }
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (n2 >> 1); i += 1024) {
+                const int lo = 2 * i - (i & (stride - 1));   // bit `stride` clear
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;             // ascending run
+                const uint64_t a = key[lo], b = key[hi];
+                if ((a > b) == up) {
+                    key[lo] = b;
+                    key[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    for (int r = threadIdx.x; r < groups; r += 1024) order[(int64_t)head * groups + r] = (int32_t)(uint32_t)key[r];
+}
+
 // Sparse attention with producer waves.  A workgroup serves G consecutive
 // query blocks of one head with 2 G consumer waves, two per block (32
 // queries each), and two producer waves.  The producers stream the union of
@@ -736,12 +801,10 @@ __global__ __launch_bounds__((2 * G + 2) * kWave, 1) void sparse_attn_stream_ker
     __shared__ uint32_t msk[G][kSelMax / 32];
     __shared__ int ready[R], released[R], broken;
 
-    const int groups = (g.nb + G - 1) / G;
-    const int per = (groups + 7) >> 3;
-    const int slot = (int)(blockIdx.x >> 3);
-    const int head = slot / per;
-    const int grp = (int)(blockIdx.x & 7) * per + (slot - head * per);
-    if (head >= g.heads || grp >= groups) return;
+    static_assert(G == kStreamGroup, "group order table");
+    const int groups = (int)stream_groups(g.nb);
+    int head, grp;
+    if (!group_of_workgroup(groups, g.heads, w.order, head, grp)) return;
     const int nw = (g.nb + 31) >> 5;
     const int b0 = G * grp;
 
@@ -947,12 +1010,22 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
     return hipGetLastError();
 }
 
+hipError_t launch_group_order(const SparseGeom& g, int group, const uint32_t* mask, int32_t* order, hipStream_t s) {
+    if (group == kStreamGroup)
+        hipLaunchKernelGGL(group_order_kernel<kStreamGroup>, dim3(g.heads), dim3(1024), 0, s, g, mask, order);
+    else if (group == kBwdGroup)
+        hipLaunchKernelGGL(group_order_kernel<kBwdGroup>, dim3(g.heads), dim3(1024), 0, s, g, mask, order);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const SparseGeom& g, const __bf16* q, int hd,
                               float scale_log2, const SparseWs& w, float* o, float* lse, int wait_limit,
                               hipStream_t s) {
     (void)hd;
     constexpr int G = kStreamGroup, R = kStreamRing;
-    const unsigned blocks = (unsigned)(8 * ((((g.nb + G - 1) / G) + 7) / 8) * g.heads);
+    const unsigned blocks = (unsigned)group_workgroups(stream_groups(g.nb), g.heads);
     hipLaunchKernelGGL((sparse_attn_stream_kernel<128, G, R>), dim3(blocks), dim3((2 * G + 2) * kWave), 0, s, g, q,
                        scale_log2, w, o, lse, wait_limit);
     return hipGetLastError();

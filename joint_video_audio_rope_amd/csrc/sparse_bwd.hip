@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void mask_transpose_kernel(const uint32_t* __r
     maskt[id] = word;
 }
 
-constexpr int kSG = 4;   // blocks per workgroup (2 waves of 32 tokens each)
+constexpr int kSG = kBwdGroup;   // blocks per workgroup (2 waves of 32 tokens each)
 
 // Cursor over the union of kSG bitmask rows staged in LDS (the same walk in
 // every wave; values are wave-uniform).
@@ -180,12 +180,8 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
     __shared__ uint32_t msk[kSG][kSelMax / 32];
 
     const int groups = (g.nb + kSG - 1) / kSG;
-    const int total = groups * g.heads;
-    const int per_xcd = (total + 7) >> 3;
-    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (logical >= total) return;
-    const int grp = logical % groups;
-    const int head = logical / groups;
+    int head, grp;
+    if (!group_of_workgroup(groups, g.heads, a.order_q, head, grp)) return;
     const int b0 = kSG * grp;
     const int nw = (g.nb + 31) >> 5;
     const int64_t n = (int64_t)g.T * g.H * g.W;
@@ -348,12 +344,8 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
     __shared__ uint32_t msk[kSG][kSelMax / 32];
 
     const int groups = (g.nb + kSG - 1) / kSG;
-    const int total = groups * g.heads;
-    const int per_xcd = (total + 7) >> 3;
-    const int logical = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (logical >= total) return;
-    const int grp = logical % groups;
-    const int head = logical / groups;
+    int head, grp;
+    if (!group_of_workgroup(groups, g.heads, a.order_k, head, grp)) return;
     const int c0 = kSG * grp;
     const int nw = (g.nb + 31) >> 5;
     const int64_t n = (int64_t)g.T * g.H * g.W;
@@ -536,8 +528,7 @@ hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint
 }
 
 hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s) {
-    const int groups = (g.nb + kSG - 1) / kSG;
-    const unsigned blocks = (unsigned)((groups * g.heads + 7) / 8 * 8);
+    const unsigned blocks = (unsigned)group_workgroups((g.nb + kSG - 1) / kSG, g.heads);
     const dim3 block(8 * kWave);
     hipLaunchKernelGGL(sparse_bwd_dq_kernel<128>, dim3(blocks), block, 0, s, g, a);
     hipLaunchKernelGGL((sparse_bwd_key_kernel<128, false>), dim3(blocks), block, 0, s, g, a);
