@@ -524,10 +524,12 @@ mmdit_status run_sparse(const void* q, const void* k, const void* v, int32_t T, 
 
 // Workspace of a block-sparse backward: D and lse2 [heads][n] fp32, the
 // transposed block images Q^T, dO^T, K^T [heads][nb][hd * 64] bf16, the
-// transposed selection bitmask [heads][nb][ceil(nb/32)], and the dispatch
-// orders of the query-block and key-block groups [heads][groups] i32.
+// transposed selection bitmask [heads][nb][ceil(nb/32)], the dispatch
+// orders of the query-block and key-block groups [heads][groups] i32, and
+// the block row images Q, dO, K, V [heads][nb][64 * hd] bf16.
 struct SparseBwdPlan {
-    size_t off_dd, off_ls2, off_qt, off_dot, off_kt, off_maskt, off_order_q, off_order_k, total;
+    size_t off_dd, off_ls2, off_qt, off_dot, off_kt, off_maskt, off_order_q, off_order_k, off_qi, off_doi, off_ki,
+        off_vi, total;
 };
 
 SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) {
@@ -546,6 +548,10 @@ SparseBwdPlan plan_sparse_bwd(int64_t n, int64_t nb, int32_t heads, int32_t hd) 
     p.off_maskt = take((size_t)heads * nb * ((nb + 31) / 32) * 4);
     p.off_order_q = take((size_t)heads * ((nb + kBwdGroup - 1) / kBwdGroup) * 4);
     p.off_order_k = take((size_t)heads * ((nb + kBwdGroup - 1) / kBwdGroup) * 4);
+    p.off_qi = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_doi = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_ki = take((size_t)heads * nb * hd * kTileN * 2);
+    p.off_vi = take((size_t)heads * nb * hd * kTileN * 2);
     p.total = off;
     return p;
 }
@@ -590,6 +596,10 @@ mmdit_status run_sparse_bwd(const SparseGeom& g, const SparseBwdPlan& bp, const 
     a.qt_img = (const __bf16*)(w + bp.off_qt);
     a.dot_img = (const __bf16*)(w + bp.off_dot);
     a.kt_img = (const __bf16*)(w + bp.off_kt);
+    a.q_img = (const __bf16*)(w + bp.off_qi);
+    a.do_img = (const __bf16*)(w + bp.off_doi);
+    a.k_img = (const __bf16*)(w + bp.off_ki);
+    a.v_img = (const __bf16*)(w + bp.off_vi);
     a.mask = sel_mask;
     a.maskt = (const uint32_t*)(w + bp.off_maskt);
     a.ls2 = (const float*)(w + bp.off_ls2);
@@ -609,6 +619,10 @@ mmdit_status run_sparse_bwd(const SparseGeom& g, const SparseBwdPlan& bp, const 
         (e = launch_block_timg(g, a.q, (__bf16*)a.qt_img, tbase, tdim, s)) != hipSuccess ||
         (e = launch_block_timg(g, a.d_o, (__bf16*)a.dot_img, tbase, tdim, s)) != hipSuccess ||
         (e = launch_block_timg(g, a.k, (__bf16*)a.kt_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_rimg(g, a.q, (__bf16*)a.q_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_rimg(g, a.d_o, (__bf16*)a.do_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_rimg(g, a.k, (__bf16*)a.k_img, tbase, tdim, s)) != hipSuccess ||
+        (e = launch_block_rimg(g, a.v, (__bf16*)a.v_img, tbase, tdim, s)) != hipSuccess ||
         (e = launch_mask_transpose(g, sel_mask, (uint32_t*)a.maskt, s)) != hipSuccess ||
         (e = launch_group_order(g, kBwdGroup, sel_mask, (int32_t*)a.order_q, s)) != hipSuccess ||
         (e = launch_group_order(g, kBwdGroup, a.maskt, (int32_t*)a.order_k, s)) != hipSuccess ||

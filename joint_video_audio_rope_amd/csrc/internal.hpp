@@ -429,6 +429,10 @@ struct SparseBwdArgs {
     const __bf16* qt_img;    // [heads][nb][hd * 64] transposed block images
     const __bf16* dot_img;
     const __bf16* kt_img;
+    const __bf16* q_img;     // [heads][nb][64 * hd] block row images (row-major tile order)
+    const __bf16* do_img;
+    const __bf16* k_img;
+    const __bf16* v_img;
     const uint32_t* mask;    // [heads][nb][ceil(nb/32)] query block -> selected key blocks
     const uint32_t* maskt;   // [heads][nb][ceil(nb/32)] key block -> query blocks that selected it
     const float* ls2;        // [heads][n] lse * log2(e)
@@ -448,6 +452,8 @@ struct SparseBwdArgs {
 };
 
 hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
+                             const uint8_t* tdim, hipStream_t s);
+hipError_t launch_block_rimg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
                              const uint8_t* tdim, hipStream_t s);
 hipError_t launch_mask_transpose(const SparseGeom& g, const uint32_t* mask, uint32_t* maskt, hipStream_t s);
 hipError_t launch_sparse_bwd(const SparseGeom& g, const SparseBwdArgs& a, hipStream_t s);

@@ -13,6 +13,8 @@
 //                in the LDS order of a transposed tile (the operands that
 //                contract over tokens; a block's 64 tokens are not contiguous
 //                in the raster layout, so these are staged once);
+//   block_rimg   per-block row images Q, dO, K, V [heads][nb][64 x hd] in the
+//                LDS order of a row-major tile;
 //   mask_transpose  the selection bitmask transposed: for each key block, the
 //                query blocks that selected it;
 //   dq           a workgroup owns 4 query blocks (8 waves of 32 queries) and
@@ -22,9 +24,8 @@
 //                the union of the query blocks that selected them: S = Q K^T
 //                -> P -> dV^T += dO^T P, and S, dP = dO V^T -> dS -> dK^T +=
 //                Q^T dS.
-// Row-major tiles (Q, dO, K, V rows) are gathered straight from the raster
-// layout by the copies: each lane's copy fetches the 16-byte chunk of the
-// token that belongs at its LDS position.  Walks are synchronous (one
+// Every tile is staged by contiguous 1 KB copies of these images.  Walks are
+// synchronous (one
 // workgroup barrier per tile, double-buffered copies); a wave whose block did
 // not select the tile skips its products.  With content-adaptive tiles
 // (SparseBwdArgs::tdim set) the same passes run over the 64-token tiles, each
@@ -91,6 +92,28 @@ __global__ __launch_bounds__(256) void block_timg_kernel(SparseGeom g, const __b
     }
 }
 
+// One workgroup per (block, head): the block's 64 rows of src laid out as
+// the LDS image of a row-major tile (chunk u of the image holds chunk c of
+// tile row r, (r, c) = k_at(u), and tile row r holds block-local token
+// (r & ~31) | perm_row(r & 31), the order the products take).  The walks
+// then stage a tile with contiguous 1 KB copies: gathering the 64 scattered
+// 256-byte rows per tile in the walk itself cost ~14 % of the backward.
+template <int HD>
+__global__ __launch_bounds__(256) void block_rimg_kernel(SparseGeom g, const __bf16* __restrict__ src,
+                                                         __bf16* __restrict__ dst, const int32_t* __restrict__ tbase,
+                                                         const uint8_t* __restrict__ tdim) {
+    using L = TileLayout<HD>;
+    const int j = blockIdx.x, head = blockIdx.y;
+    const int64_t rs = (int64_t)g.heads * HD;
+    __bf16* out = dst + ((int64_t)head * g.nb + j) * (HD * kTileN);
+    for (int u = threadIdx.x; u < kTileN * L::kKChunks; u += 256) {
+        int row, c;
+        L::k_at(u, row, c);
+        const int64_t tok = bwd_token(g, tbase, tdim, j, (row & ~31) | perm_row(row & 31));
+        *reinterpret_cast<uint4*>(out + u * 8) = *reinterpret_cast<const uint4*>(src + tok * rs + head * HD + c * 8);
+    }
+}
+
 // maskT[head][j][w] bit b = mask[head][32 w + b][j / 32] bit j % 32 (0 past nb).
 __global__ __launch_bounds__(256) void mask_transpose_kernel(const uint32_t* __restrict__ mask, int nb, int heads,
                                                              uint32_t* __restrict__ maskt) {
@@ -146,25 +169,6 @@ __device__ __forceinline__ void dma4(const void* gp, char* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(gp, MMDIT_LDS(lds_wave_base), 4, 0, 0);
 }
 
-// Copy one block's 64 rows of a [tokens][heads][HD] bf16 tensor into a
-// row-major tile (MFMA row m of each 32-row half holds block-local token
-// perm(m)); roff holds this lane's per-copy offsets from the block's first
-// token row.
-template <int CK>
-__device__ __forceinline__ void gather_rows(const char* g0, const uint32_t (&roff)[CK], char* tile, int w) {
-#pragma unroll
-    for (int i = 0; i < CK; ++i) dma16(g0 + roff[i], tile + (w * CK + i) * 1024);
-}
-
-// The same copies for an adaptive tile: this lane's copy i fetches chunk
-// rc[i] & 15 of the tile's local token rc[i] >> 4 (tile-order rows).
-template <int CK>
-__device__ __forceinline__ void gather_tile_rows(const SparseGeom& g, const char* g0, int64_t rb, uint32_t code,
-                                                 const int (&rc)[CK], char* tile, int w) {
-#pragma unroll
-    for (int i = 0; i < CK; ++i)
-        dma16(g0 + tile_local(g, code, rc[i] >> 4) * rb + (rc[i] & 15) * 16, tile + (w * CK + i) * 1024);
-}
 
 template <int HD>
 __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, SparseBwdArgs a) {
@@ -199,7 +203,6 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
     const int m = lane & 31;
     const int side = simd_pair_side(w);
     const int64_t rstride = (int64_t)g.heads * HD;
-    const int64_t rb = rstride * 2;
     const bool own_ok = b0 + side < g.nb;
     const int qb = min(b0 + side, g.nb - 1);
     const int64_t qtok = bwd_token(g, a.tbase, a.tdim, qb, (w & 1) * 32 + m);
@@ -212,34 +215,21 @@ __global__ __launch_bounds__(8 * kWave) void sparse_bwd_dq_kernel(SparseGeom g, 
     const float lq2 = a.ls2[(int64_t)head * n + qtok];
     const float dq_d = a.dd[(int64_t)head * n + qtok];
 
-    // this lane's row-tile copies: the tile row (local token) and chunk it
-    // fetches, and for uniform blocks their offset from the block's first row
-    int rc[CK];
-    uint32_t roff[CK];
-#pragma unroll
-    for (int i = 0; i < CK; ++i) {
-        int row, c;
-        L::k_at((w * CK + i) * kWave + lane, row, c);
-        rc[i] = ((row & ~31) | perm_row(row & 31)) << 4 | c;
-        roff[i] = a.tdim ? 0u : (uint32_t)(block_off(g, rc[i] >> 4) * rb + c * 16);
-    }
-    const char* kg = reinterpret_cast<const char*>(a.k + head * HD);
-    const char* vg = reinterpret_cast<const char*>(a.v + head * HD);
-    const char* ktg = reinterpret_cast<const char*>(a.kt_img + (int64_t)head * g.nb * (HD * kTileN)) + 16 * lane;
+    // this lane's 16 bytes of each 1 KB copy of the per-block images
+    const int64_t img = (int64_t)head * g.nb * (HD * kTileN);
+    const char* kig = reinterpret_cast<const char*>(a.k_img + img) + 16 * lane;
+    const char* vig = reinterpret_cast<const char*>(a.v_img + img) + 16 * lane;
+    const char* ktg = reinterpret_cast<const char*>(a.kt_img + img) + 16 * lane;
 
     auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
     auto issue = [&](int j, char* b) {
-        if (a.tdim) {
-            const int64_t t0 = (int64_t)a.tbase[j] * rb;
-            const uint32_t code = a.tdim[j];
-            gather_tile_rows<CK>(g, kg + t0, rb, code, rc, b, w);
-            gather_tile_rows<CK>(g, vg + t0, rb, code, rc, b + L::kKBytes, w);
-        } else {
-            const int64_t t0 = block_token(g, j, 0) * rb;
-            gather_rows<CK>(kg + t0, roff, b, w);
-            gather_rows<CK>(vg + t0, roff, b + L::kKBytes, w);
+        const int64_t jb = (int64_t)j * (HD * kTileN * 2);
+#pragma unroll
+        for (int i = 0; i < CK; ++i) {
+            dma16(kig + jb + (w * CK + i) * 1024, b + (w * CK + i) * 1024);
+            dma16(vig + jb + (w * CK + i) * 1024, b + L::kKBytes + (w * CK + i) * 1024);
         }
-        const char* src = ktg + (int64_t)j * (HD * kTileN * 2);
+        const char* src = ktg + jb;
 #pragma unroll
         for (int i = 0; i < CV; ++i)
             dma16(src + (w * CV + i) * 1024, b + 2 * L::kKBytes + (w * CV + i) * 1024);
@@ -363,7 +353,6 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
     const int m = lane & 31;
     const int side = simd_pair_side(w);
     const int64_t rstride = (int64_t)g.heads * HD;
-    const int64_t rb = rstride * 2;
     const bool own_ok = c0 + side < g.nb;
     const int kb_own = min(c0 + side, g.nb - 1);
     const int64_t ktok = bwd_token(g, a.tbase, a.tdim, kb_own, (w & 1) * 32 + m);
@@ -374,39 +363,26 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
         if (DK) vr[ks] = load_bf16x8(a.v + ktok * rstride + head * HD + 16 * ks + 8 * hh, true);
     }
 
-    int rc[CK];
-    uint32_t roff[CK];
-#pragma unroll
-    for (int i = 0; i < CK; ++i) {
-        int row, c;
-        L::k_at((w * CK + i) * kWave + lane, row, c);
-        rc[i] = ((row & ~31) | perm_row(row & 31)) << 4 | c;
-        roff[i] = a.tdim ? 0u : (uint32_t)(block_off(g, rc[i] >> 4) * rb + c * 16);
-    }
     const int loff = a.tdim ? 0 : block_off(g, lane);   // this lane's query of the lse / D copies
-    const char* qg = reinterpret_cast<const char*>(a.q + head * HD);
-    const char* og = reinterpret_cast<const char*>(a.d_o + head * HD);
-    const char* tg = reinterpret_cast<const char*>((DK ? a.qt_img : a.dot_img) + (int64_t)head * g.nb * (HD * kTileN)) +
-                     16 * lane;
+    // this lane's 16 bytes of each 1 KB copy of the per-block images
+    const int64_t img = (int64_t)head * g.nb * (HD * kTileN);
+    const char* qig = reinterpret_cast<const char*>(a.q_img + img) + 16 * lane;
+    const char* oig = reinterpret_cast<const char*>(a.do_img + img) + 16 * lane;
+    const char* tg = reinterpret_cast<const char*>((DK ? a.qt_img : a.dot_img) + img) + 16 * lane;
     const float* lsg = a.ls2 + (int64_t)head * n;
     const float* ddg = a.dd + (int64_t)head * n;
 
     auto buf = [&](int t) { return lds + (t & 1) * kBuf; };
     auto issue = [&](int i, char* b) {
-        int64_t lt;   // raster token of this lane's query of the lse / D copies
-        if (a.tdim) {
-            const int64_t tok0 = a.tbase[i];
-            const uint32_t code = a.tdim[i];
-            gather_tile_rows<CK>(g, qg + tok0 * rb, rb, code, rc, b, w);
-            if (DK) gather_tile_rows<CK>(g, og + tok0 * rb, rb, code, rc, b + L::kKBytes, w);
-            lt = tok0 + tile_local(g, code, lane);
-        } else {
-            const int64_t tok0 = block_token(g, i, 0);
-            gather_rows<CK>(qg + tok0 * rb, roff, b, w);
-            if (DK) gather_rows<CK>(og + tok0 * rb, roff, b + L::kKBytes, w);
-            lt = tok0 + loff;
+        // raster token of this lane's query of the lse / D copies
+        const int64_t lt = a.tdim ? (int64_t)a.tbase[i] + tile_local(g, a.tdim[i], lane) : block_token(g, i, 0) + loff;
+        const int64_t ib = (int64_t)i * (HD * kTileN * 2);
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+            dma16(qig + ib + (w * CK + c) * 1024, b + (w * CK + c) * 1024);
+            if (DK) dma16(oig + ib + (w * CK + c) * 1024, b + L::kKBytes + (w * CK + c) * 1024);
         }
-        const char* src = tg + (int64_t)i * (HD * kTileN * 2);
+        const char* src = tg + ib;
 #pragma unroll
         for (int c = 0; c < CV; ++c) dma16(src + (w * CV + c) * 1024, b + kOffT + (w * CV + c) * 1024);
         if (w == 0) dma4(lsg + lt, b + kOffL);
@@ -517,6 +493,12 @@ void sparse_bwd_key_kernel(SparseGeom g, SparseBwdArgs a) {
 hipError_t launch_block_timg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
                              const uint8_t* tdim, hipStream_t s) {
     hipLaunchKernelGGL(block_timg_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, src, dst, tbase, tdim);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_rimg(const SparseGeom& g, const __bf16* src, __bf16* dst, const int32_t* tbase,
+                             const uint8_t* tdim, hipStream_t s) {
+    hipLaunchKernelGGL(block_rimg_kernel<128>, dim3(g.nb, g.heads), dim3(256), 0, s, g, src, dst, tbase, tdim);
     return hipGetLastError();
 }
 

@@ -269,8 +269,9 @@ def test_sparse_bwd_workspace_plan():
     a256 = lambda x: (x + 255) // 256 * 256
     n, nb, h = 172032, 2688, 24
     # D, lse2; Q^T, dO^T, K^T block images; transposed bitmask; dispatch orders of the
-    # 672 groups of 4 query blocks and of 4 key blocks per head
-    want = 2 * a256(h * n * 4) + 3 * a256(h * nb * 128 * 64 * 2) + a256(h * nb * 84 * 4) + 2 * a256(h * 672 * 4)
+    # 672 groups of 4 query blocks and of 4 key blocks per head; Q, dO, K, V row images
+    want = (2 * a256(h * n * 4) + 7 * a256(h * nb * 128 * 64 * 2) + a256(h * nb * 84 * 4)
+            + 2 * a256(h * 672 * 4))
     sd = J.sparse_desc()
     assert J.mmdit_workspace_bytes(J.MMDIT_OP_BLOCK_SPARSE_ATTN_BWD, n, n, h, 128, J.MMDIT_BF16, sd) == want
 
