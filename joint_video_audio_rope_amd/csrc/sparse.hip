@@ -7,15 +7,18 @@
 //                  block's first raster token.
 //   vt_blocks      each block's K rows (bf16) and V^T (fp16 [d][64]), each
 //                  laid out as the image of its LDS tile (HBM-bound).
-//   block_scores   fp64 logits Qbar Kbar^T * scale per head (fp64 FMA GEMM).
+//   block_scores   fp64 logits Qbar Kbar^T * scale per head, on the fp64
+//                  matrix cores, in chunks of query-block rows.
 //   block_select   per (head, query block): fp64 softmax, then the top-p and
 //                  top-k cuts found by bisection over the probabilities' bit
 //                  patterns (ties to the lower block id), keeping the longer
 //                  prefix; emits the bitmask and the count.
+//   group_order    per head, the groups of query blocks ranked by estimated
+//                  cost: the next kernel's dispatch order.
 //   sparse_attn    attention of groups of query blocks over the union of
 //                  their selected key blocks, fed through an LDS ring by
-//                  producer waves, with the dense kernel's online-softmax
-//                  tile step.
+//                  producer waves, in half-tile steps of the dense kernel's
+//                  online softmax.
 // Selection runs in fp64 throughout: on smooth-field inputs the probability
 // gaps and running-sum margins at the cut get down to ~1e-8, where fp32 flips
 // rows.
