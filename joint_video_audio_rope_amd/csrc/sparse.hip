@@ -502,11 +502,13 @@ __global__ __launch_bounds__(64 * (W == 1 ? kSelWaves : W)) void block_select_ke
         }
     }
 
-    // top-k prefix
+    // top-k prefix, needed only when it is the longer one (the selection
+    // below takes the top-p prefix whenever n_p >= k; every wave of a row
+    // holds the same n_p, so all of them skip or run the search together)
     const int kk = top_k < nv ? top_k : nv;
     double vk = -1.0;
     int mk = 0;
-    if (kk > 0 && kk < nv) {
+    if (kk > 0 && kk < nv && kk > n_p) {
         uint64_t lo = 0, hi = kInf;   // count(P >= lo) >= k > count(P >= hi)
         int c_lo = nv, c_hi = 0;
         while (hi - lo > 1 && c_lo - c_hi > 1) {
