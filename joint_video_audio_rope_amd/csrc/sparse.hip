@@ -666,9 +666,12 @@ __device__ __forceinline__ void half_tile_step(const char* __restrict__ tile, in
 constexpr int kOrderMax = 8192;   // >= groups per head for G >= 4 and kSelMax blocks, a power of two
 static_assert(kOrderMax >= (kSelMax + 3) / 4, "order table");
 
+constexpr int kOrderThreads = 1024;   // one workgroup per head
+
 template <int G>
-__global__ __launch_bounds__(1024) void group_order_kernel(SparseGeom g, const uint32_t* __restrict__ mask,
-                                                           int32_t* __restrict__ order) {
+__global__ __launch_bounds__(kOrderThreads) void group_order_kernel(SparseGeom g, const uint32_t* __restrict__ mask,
+                                                                    int32_t* __restrict__ order) {
+    constexpr int kWaves = kOrderThreads / kWave;
     __shared__ uint64_t key[kOrderMax];
     const int head = blockIdx.x;
     const int groups = (g.nb + G - 1) / G;
@@ -676,7 +679,7 @@ __global__ __launch_bounds__(1024) void group_order_kernel(SparseGeom g, const u
     int n2 = 1;
     while (n2 < groups) n2 <<= 1;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int gr = wv; gr < n2; gr += 16) {
+    for (int gr = wv; gr < n2; gr += kWaves) {
         uint64_t k = ~0ull;   // padding sorts last
         if (gr < groups) {
             const int b0 = gr * G, nbk = min(G, g.nb - b0);
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(1024) void group_order_kernel(SparseGeom g, const u
     __syncthreads();
     for (int size = 2; size <= n2; size <<= 1)
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n2 >> 1); i += 1024) {
+            for (int i = threadIdx.x; i < (n2 >> 1); i += kOrderThreads) {
                 const int lo = 2 * i - (i & (stride - 1));   // bit `stride` clear
                 const int hi = lo + stride;
                 const bool up = (lo & size) == 0;             // ascending run
@@ -716,7 +719,8 @@ __global__ __launch_bounds__(1024) void group_order_kernel(SparseGeom g, const u
             }
             __syncthreads();
         }
-    for (int r = threadIdx.x; r < groups; r += 1024) order[(int64_t)head * groups + r] = (int32_t)(uint32_t)key[r];
+    for (int r = threadIdx.x; r < groups; r += kOrderThreads)
+        order[(int64_t)head * groups + r] = (int32_t)(uint32_t)key[r];
 }
 
 // Sparse attention with producer waves.  A workgroup serves G consecutive
@@ -1017,9 +1021,10 @@ hipError_t launch_block_select(const SparseGeom& g, int top_k, double top_p, con
 
 hipError_t launch_group_order(const SparseGeom& g, int group, const uint32_t* mask, int32_t* order, hipStream_t s) {
     if (group == kStreamGroup)
-        hipLaunchKernelGGL(group_order_kernel<kStreamGroup>, dim3(g.heads), dim3(1024), 0, s, g, mask, order);
+        hipLaunchKernelGGL(group_order_kernel<kStreamGroup>, dim3(g.heads), dim3(kOrderThreads), 0, s, g, mask,
+                           order);
     else if (group == kBwdGroup)
-        hipLaunchKernelGGL(group_order_kernel<kBwdGroup>, dim3(g.heads), dim3(1024), 0, s, g, mask, order);
+        hipLaunchKernelGGL(group_order_kernel<kBwdGroup>, dim3(g.heads), dim3(kOrderThreads), 0, s, g, mask, order);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
